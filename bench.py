@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE FFN forward on one MI355X.
+
+Workload (default): the Zipf-skewed layer, T=16384 tokens, H=4096, I=2048, E=128
+experts, top-8, bf16, router logits N(0,1) plus a per-expert bias ln(rank^-1.2)
+(seed 0).  A step is one moe_forward call: route, permutation tables, row gather,
+GEMM1 + SwiGLU, GEMM2, combine, with every input already resident in HBM.
+
+Timing: W untimed warm-up steps, then K steps bracketed by device
+synchronisation; each timed step is the moe_forward_timed entry point (same
+kernels, plus a HIP event at every stage boundary on the library's stream), so the
+per-stage durations below are measured live over the timed region.
+
+Prints one JSON line.  The CPU baseline is the fp64 oracle (test infrastructure)
+timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/s + TFLOP/s (% MFMA peak), permute/combine % HBM, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_file, kernel, launches_bytes_key="bytes_per_launch"):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(kernel)
+    if not rec or rec.get("source_sha") != source_hash([kernel_file]):
+        return None
+    return rec.get(launches_bytes_key)
+
+
+def cpu_baseline(inp, budget_s):
+    import oracle
+    cfg = inp["cfg"]
+    cores = oracle.max_threads()
+    probe = np.linspace(0, cfg.T - 1, 2 * cores).astype(np.int32)  # two tokens per thread
+    t0 = time.perf_counter()
+    oracle.moe_forward(inp, probe)
+    per_tok = (time.perf_counter() - t0) / probe.size
+    n = int(max(4, min(cfg.T, budget_s / max(per_tok, 1e-9))))
+    tokens = np.linspace(0, cfg.T - 1, n).astype(np.int32)
+    log(f"cpu baseline: oracle on {n} tokens with {cores} threads (~{n * per_tok:.0f} s)")
+    t0 = time.perf_counter()
+    oracle.moe_forward(inp, tokens)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} evenly spaced tokens of the {cfg.name} workload (all k slots each), fp64, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="skewed")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import token_permute_grouped_amd as tpg
+    from moe_synth import CONFIGS, generate
+
+    cfg = CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    inp = generate(cfg, seed=args.seed)
+    log(f"generated {cfg.name} (seed {args.seed}) in {time.perf_counter() - t0:.1f} s")
+
+    dev = torch.device("cuda:0")
+
+    def dt(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    w4 = cfg.prec == "w4a8"
+    p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.MOE_PREC_W4A8 if w4 else tpg.MOE_PREC_BF16,
+                        cfg.glu_interleave, cfg.swiglu_clamp)
+    d = {k: dt(inp.get(k)) for k in ("logits", "slot_drop", "x", "x_scale", "w1", "w1_bscale", "w1_gscale", "w2",
+                                      "w2_bscale", "w2_gscale")}
+    wts = tpg.make_weights(d["w1"], d["w2"], d["w1_bscale"], d["w1_gscale"], d["w2_bscale"], d["w2_gscale"])
+    ws = torch.empty(tpg.moe_workspace_bytes(p, tpg.MOE_WS_FORWARD), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws.numel() / 2**30:.2f} GiB")
+
+    def step(events=None):
+        if events is None:
+            tpg.moe_forward(d["logits"], d["slot_drop"], d["x"], d["x_scale"], wts, p, out, ws)
+        else:
+            tpg.moe_forward_timed(d["logits"], d["slot_drop"], d["x"], d["x_scale"], wts, p, out, ws, events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+
+    hip = HipEvents()
+    evs = [[hip.create() for _ in range(tpg.MOE_N_STAGE_EVENTS)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    stage_ms = {}
+    for s, name in enumerate(tpg.STAGES):
+        stage_ms[name] = float(np.mean([hip.ms(evs[i][s], evs[i][s + 1]) for i in range(args.steps)]))
+    step_ms = float(np.mean([hip.ms(evs[i][0], evs[i][-1]) for i in range(args.steps)]))
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), {wall_ms:.3f} ms/step (wall)")
+
+    T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
+    R = T * k - (int(inp["slot_drop"].sum()) if inp.get("slot_drop") is not None else 0)
+    act_b = 1 if w4 else 2
+    gemm1_flops = 4.0 * R * H * I
+    gemm2_flops = 2.0 * R * H * I
+    gather_bytes = T * H * act_b + R * H * act_b + 4 * T * k
+    combine_bytes = R * H * 2 + T * H * 2 + 8 * T * k
+    s = 1e-3
+    gemm_ms = stage_ms["gemm1_swiglu"] + stage_ms["gemm2"]
+    tflops = lambda f, ms: f / (ms * s) / 1e12  # noqa: E731
+    gbs = lambda b, ms: b / (ms * s) / 1e9  # noqa: E731
+
+    g1 = tflops(gemm1_flops, stage_ms["gemm1_swiglu"])
+    roofline = {
+        "kernel": "grouped_gemm_bf16_kernel<true> (GEMM1 + SwiGLU)",
+        "bound": "mfma", "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(g1 / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu"),
+        "algorithmic_per_launch": f"4*R*H*I = {gemm1_flops:.4g} flop (R={R} rows)",
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(T / (step_ms * s), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8xfp4" if w4 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} H={H} I={I} E={cfg.E} top-{k}"
+                               + (f", Zipf s={cfg.zipf_s} expert bias" if cfg.zipf_s else "")
+                               + (f", interleave {cfg.glu_interleave}" if cfg.glu_interleave else "")
+                               + (f", {cfg.drop_p:.0%} slots dropped" if cfg.drop_p else ""),
+                   "T": T, "H": H, "I": I, "E": cfg.E, "k": k, "rows": R, "seed": args.seed},
+        "tflops_forward": round(tflops(gemm1_flops + gemm2_flops, step_ms), 2),
+        "tflops_gemms": round(tflops(gemm1_flops + gemm2_flops, gemm_ms), 2),
+        "mfma_frac_gemms": round(tflops(gemm1_flops + gemm2_flops, gemm_ms) / PEAK_BF16_TFLOPS, 4),
+        "gemm2_tflops": round(tflops(gemm2_flops, stage_ms["gemm2"]), 2),
+        "gather_gbs": round(gbs(gather_bytes, stage_ms["gather"]), 1),
+        "gather_hbm_frac": round(gbs(gather_bytes, stage_ms["gather"]) / PEAK_HBM_GBS, 4),
+        "combine_gbs": round(gbs(combine_bytes, stage_ms["combine"]), 1),
+        "combine_hbm_frac": round(gbs(combine_bytes, stage_ms["combine"]) / PEAK_HBM_GBS, 4),
+        "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts FFN forward.
+ *
+ * The forward of one MoE FFN layer on one GPU, in five steps:
+ *   route      per token, softmax over E router logits, top-k, renormalise;
+ *   permute    stable counting sort of the T*k (token, slot) pairs by expert and
+ *              a row gather into expert-contiguous order;
+ *   GEMM1      per expert, [gate | up] = x W1^T, h = silu(gate) * up (SwiGLU);
+ *   GEMM2      per expert, y = h W2^T;
+ *   combine    per token, out = sum over its k slots of w_j * y_j.
+ * The steps follow the fused MoE kernels described on the FlashInfer pull request
+ * "[SM90] Add W4A8 MegaMoE support" (dispatch, two expert GEMMs, clamped SwiGLU,
+ * top-k reduction), the GEMM + SwiGLU fused MLP of Megatron-LM "Support GEMM +
+ * Swiglu fused MLP", and the permute / unpermute fused into dispatch / combine of
+ * Megatron-LM "add permute fusion into hybrid ep".
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers unless a parameter says otherwise; the problem
+ *    and weight descriptors themselves are host structs.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call enqueues its
+ *    kernels on that stream and returns; none synchronises, allocates device
+ *    memory, or keeps a pointer after it returns.  Buffers must stay alive until
+ *    the stream has executed the work.  Weights are borrowed, never copied.
+ *  - All arrays are row-major with the last index contiguous.  bf16 is passed as
+ *    raw 16-bit patterns, fp8 as OCP E4M3FN bytes, fp4 as OCP E2M1 nibbles.
+ *  - Argument checks run on the host before anything is enqueued and read no
+ *    device memory; a failed check enqueues nothing.  T == 0 is valid and
+ *    enqueues nothing.  Device-side preconditions (not checked): logits finite;
+ *    tables consistent with one another.  Expert ids outside [0, E) are treated
+ *    as -1 (dropped) by every kernel that reads them.
+ *  - Return value: a moe_status; MOE_ERR_HIP means a launch failed, and
+ *    moe_last_hip_error() gives its hipError_t code.
+ *  - The library is stateless; calls on different streams may run concurrently
+ *    when they use disjoint buffers and workspaces.
+ */
+#ifndef TPG_MOE_H
+#define TPG_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,       /* a size is out of range (see moe_problem) */
+    MOE_ERR_UNSUPPORTED = 3, /* an option value this library does not implement */
+    MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = 5          /* a kernel launch failed */
+} moe_status;
+
+/* Arithmetic of the expert GEMMs. */
+enum {
+    /* x bf16 [T][H]; W1 bf16 [E][2I][H]; W2 bf16 [E][H][I]; fp32 accumulation;
+     * h and y rounded to bf16 (round to nearest even); out bf16 [T][H]. */
+    MOE_PREC_BF16 = 0,
+    /* FlashInfer "[SM90] Add W4A8 MegaMoE support", Usage section: FP8 E4M3
+     * activations with one fp32 scale per 128 channels; NVFP4 weights = E2M1 codes
+     * packed two per byte (low nibble = even K index, follow-up #6517 point 4), one
+     * E4M3 scale per 16 values along K, and one fp32 global scale per expert and
+     * matrix.  Each weight is dequantised in-kernel to FP8 (e2m1 * scale rounded to
+     * E4M3) and multiplied on FP8 matrix cores; h is re-quantised to FP8 per
+     * (row, 128 columns) with s = amax/448 (the split family's note that the
+     * second GEMM's activation scales are per 128 like the first's).  out bf16. */
+    MOE_PREC_W4A8 = 1
+};
+
+/* Selects which call moe_workspace_bytes() sizes the workspace for. */
+enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
+
+typedef struct moe_problem {
+    int32_t T;              /* tokens, >= 0 */
+    int32_t H;              /* hidden size, multiple of 128, 128..65536 */
+    int32_t I;              /* per-expert intermediate size, multiple of 128, 128..65536 */
+    int32_t E;              /* experts, 1..256 */
+    int32_t k;              /* experts per token, 1..min(E, 32); T*k < 2^31 */
+    int32_t prec;           /* MOE_PREC_BF16 or MOE_PREC_W4A8 */
+    /* Megatron-LM "Support GEMM + Swiglu fused MLP", option
+     * moe_mlp_glu_interleave_size: 0 = W1 rows are [gate (I rows) | up (I rows)]
+     * (the fused fc1 layout in Megatron-LM PR #5984's log); 32 = stored row
+     * 64q + r is gate row 32q + r for r < 32 and up row 32q + r - 32 otherwise. */
+    int32_t glu_interleave;
+    /* 0 = plain SwiGLU; c > 0 = clamp both gate and up to [-c, c] before the
+     * activation ("ClampedSwiGLU" in Megatron-LM PR #5984's log; the clamped
+     * SwiGLU of the FlashInfer fused kernel). */
+    float swiglu_clamp;
+} moe_problem;
+
+/* Expert weights (device pointers, borrowed).  bf16: only w1 and w2 are used.
+ * w4a8: w1 uint8 [E][2I][H/2], w1_bscale uint8 [E][2I][H/16], w1_gscale fp32 [E];
+ *       w2 uint8 [E][H][I/2],  w2_bscale uint8 [E][H][I/16],  w2_gscale fp32 [E]. */
+typedef struct moe_weights {
+    const void *w1;
+    const void *w1_bscale;
+    const float *w1_gscale;
+    const void *w2;
+    const void *w2_bscale;
+    const float *w2_gscale;
+} moe_weights;
+
+/* Host only.  Bytes of device workspace the given call needs for this problem
+ * (MOE_WS_*); 0 if the problem is invalid.  The size depends only on the problem,
+ * never on the routing, so one allocation made before graph capture serves every
+ * call of that shape.  Workspace contents need not be initialised and are not
+ * preserved between calls. */
+size_t moe_workspace_bytes(const moe_problem *p, int which);
+
+/* Host only.  Static English text for a moe_status value. */
+const char *moe_status_str(int status);
+
+/* Host only.  The hipError_t code behind the calling thread's most recent
+ * MOE_ERR_HIP (0 if there was none). */
+int moe_last_hip_error(void);
+
+/* Route.  logits fp32 [T][E]; slot_drop uint8 [T][k] or NULL (nonzero = the
+ * slot is routed to no local expert, as the FlashInfer Usage section's "-1 masks
+ * a route").  Writes topk_idx int32 [T][k] (expert ids by descending logit, ties
+ * to the lower id; -1 where dropped) and topk_w fp32 [T][k] (softmax over all E,
+ * restricted to the k chosen and renormalised to sum to 1; a dropped slot keeps
+ * its weight and is skipped by the combine). */
+int moe_route_topk(const float *logits, const uint8_t *slot_drop, const moe_problem *p, int32_t *topk_idx,
+                   float *topk_w, void *stream);
+
+/* Permute.  From topk_idx int32 [T][k] builds the tables
+ *   offsets int32 [E+1]  exclusive prefix of the expert counts (offsets[E] = R,
+ *                        the number of non-dropped slots);
+ *   row_src int32 [T*k]  row r < R holds slot s = t*k + j; rows are grouped by
+ *                        expert and ascending in s within an expert; -1 for r >= R;
+ *   slot_row int32 [T*k] inverse: row of slot s, or -1 if the slot is dropped;
+ * and gathers x_perm[r] = x[row_src[r] / k] for r < R (bf16 [T*k][H], or for
+ * W4A8 fp8 [T*k][H] plus x_perm_scale fp32 [T*k][H/128] from x_scale
+ * [T][H/128]).  Rows r >= R of x_perm are not written.  The tables are a pure
+ * function of topk_idx (bit-exact, deterministic). */
+int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
+                int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, void *ws,
+                size_t ws_bytes, void *stream);
+
+/* Grouped expert FFN.  For every expert e and row r in [offsets[e], offsets[e+1]):
+ * y_perm[r] = (silu(g) * u) W2_e^T with [g | u] = x_perm[r] W1_e^T (clamped if
+ * swiglu_clamp > 0).  x_perm as produced by moe_permute; y_perm bf16 [T*k][H];
+ * rows >= offsets[E] are not written.  Needs ws of at least
+ * moe_workspace_bytes(p, MOE_WS_GROUPED_FFN) bytes (holds h and the tile list). */
+int moe_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t *offsets, const moe_weights *w,
+                    const moe_problem *p, void *y_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Unpermute and combine: out[t] = bf16( sum_{j=0..k-1, slot_row[t*k+j] >= 0}
+ * topk_w[t][j] * y_perm[slot_row[t*k+j]] ), accumulated in fp32 in ascending j
+ * with no atomics (deterministic).  A token whose slots are all dropped gets 0. */
+int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const float *topk_w, const moe_problem *p,
+                          void *out, void *stream);
+
+/* The whole forward: route, permute, grouped FFN, combine, on one stream, with
+ * every intermediate in ws (at least moe_workspace_bytes(p, MOE_WS_FORWARD)). */
+int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
+                const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_forward with timing marks: identical work, plus hipEventRecord of
+ * stage_events[i] (MOE_N_STAGE_EVENTS hipEvent_t handles, created by the caller)
+ * on `stream` at each stage boundary:
+ *   [0] route [1] permutation tables [2] row gather [3] GEMM tile list [4]
+ *   GEMM1 + SwiGLU [5] GEMM2 [6] combine [7]
+ * (for W4A8 the two GEMMs run between marks 4 and 5 and mark 6 follows at once).
+ * For measurement; the marks add no work to the kernels. */
+#define MOE_N_STAGE_EVENTS 8
+int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
+                      const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
+                      void *const *stage_events);
+
+/* Diagnostic: writes the W4A8 dequant of every (e2m1 code c, e4m3 scale s) pair,
+ * as E4M3 codes, to out8 uint8 [16][256] (device), using the same device
+ * conversion the W4A8 GEMMs use. */
+int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPG_MOE_H */

@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP translation units of libtpg_moe.so.
+// Every kernel is written for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace tpg {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- workspace layout
+// One layout for every entry point, computed on the host from the problem only
+// (never from the routing), so a workspace allocated once serves every call of that
+// shape.  Offsets are 256-byte aligned.
+struct WsLayout {
+    size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
+    size_t tiles;         // int32 [max_tiles]      grouped GEMMs: (expert << 20 | m_tile) list
+    size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count
+    size_t h;             // bf16 [S][I]  or fp8 [S][I] + fp32 [S][I/128]
+    size_t h_scale;
+    size_t topk_idx;      // forward only: int32 [T][k]
+    size_t topk_w;        // forward only: fp32 [T][k]
+    size_t offsets;       // forward only: int32 [E+1]
+    size_t row_src;       // forward only: int32 [S]
+    size_t slot_row;      // forward only: int32 [S]
+    size_t x_perm;        // forward only: bf16/fp8 [S][H]
+    size_t x_perm_scale;  // forward only: fp32 [S][H/128]
+    size_t y_perm;        // forward only: bf16 [S][H]
+    size_t permute_end, ffn_end, forward_end;
+};
+
+// rows of the permutation processed by one workgroup of the table kernels
+constexpr int kChunk = 1024;
+// M tile of the grouped GEMMs (rows of one expert per workgroup)
+constexpr int kGemmBM = 128;
+
+inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
+inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
+inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + kGemmBM - 1) / kGemmBM + p.E; }
+
+WsLayout ws_layout(const moe_problem &p);
+
+// ---------------------------------------------------------------- launchers (enqueue only)
+hipError_t launch_route_topk(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int32_t *topk_idx,
+                             float *topk_w, hipStream_t s);
+
+hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *chunk_counts, int32_t *offsets,
+                         int32_t *row_src, int32_t *slot_row, hipStream_t s);
+
+hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *slot_row, int T, int k, int H,
+                          int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);
+
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
+
+hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
+                                    const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
+                                    int glu_interleave, float clamp, uint16_t *h, hipStream_t s);
+
+hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
+                             const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
+                             hipStream_t s);
+
+hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *offsets,
+                                   const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles,
+                                   const moe_weights &w, const moe_problem &p, uint8_t *h, float *h_scale,
+                                   uint16_t *y_perm, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,
+                          uint16_t *out, hipStream_t s);
+
+hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace tpg

@@ -1,0 +1,179 @@
+// Permutation tables: a stable counting sort of the T*k (token, slot) pairs by
+// expert id, giving expert-contiguous rows (Megatron-LM "add permute fusion into
+// hybrid ep": tokens are permuted into expert order before the experts and
+// unpermuted in the combine).  Rows of one expert keep ascending slot id
+// s = t*k + j, so the result is a pure function of topk_idx and bit-exact.
+//
+// Three launches, no atomics outside LDS and nothing order-dependent:
+//   1. chunk_hist  one workgroup per chunk of kChunk slots: LDS histogram -> chunk_counts[c][e]
+//   2. scan        one workgroup: per expert an exclusive prefix over chunks (in place),
+//                  then an exclusive prefix over experts -> offsets[E+1]
+//   3. rank        one workgroup per chunk, one wave per quarter chunk: per-wave LDS bases,
+//                  then 64 slots at a time, a slot's rank among equal ids of lower lanes
+//                  comes from 9 ballots (one per bit of id+1) and a popcount.
+// The GEMM tile list (expert, m-tile) is built from offsets by build_tiles.
+#include "moe_internal.h"
+
+namespace tpg {
+
+namespace {
+constexpr int kWavesPerChunk = 4;
+constexpr int kSub = kChunk / kWavesPerChunk;  // slots per wave in the rank kernel
+
+__device__ __forceinline__ int valid_id(int32_t x, int E) { return ((unsigned)x < (unsigned)E) ? x : -1; }
+}  // namespace
+
+__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t *__restrict__ idx, int64_t S, int E,
+                                                         int32_t *__restrict__ chunk_counts) {
+    __shared__ int h[256];
+    for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kChunk;
+    for (int i = threadIdx.x; i < kChunk; i += 256) {
+        const int64_t s = base + i;
+        if (s < S) {
+            const int x = valid_id(idx[s], E);
+            if (x >= 0) atomicAdd(&h[x], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ chunk_counts, int64_t nch, int E,
+                                                   int32_t *__restrict__ offsets) {
+    __shared__ int tot[256];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        int32_t *col = chunk_counts + e;
+        int64_t c = 0;
+        for (; c + 4 <= nch; c += 4) {  // four independent loads in flight
+            const int v0 = col[(c + 0) * E], v1 = col[(c + 1) * E], v2 = col[(c + 2) * E], v3 = col[(c + 3) * E];
+            col[(c + 0) * E] = run;
+            col[(c + 1) * E] = run + v0;
+            col[(c + 2) * E] = run + v0 + v1;
+            col[(c + 3) * E] = run + v0 + v1 + v2;
+            run += v0 + v1 + v2 + v3;
+        }
+        for (; c < nch; ++c) {
+            const int v = col[c * E];
+            col[c * E] = run;
+            run += v;
+        }
+    }
+    tot[e] = e < E ? run : 0;
+    __syncthreads();
+    // inclusive Hillis-Steele scan over the 256 expert totals
+    for (int d = 1; d < 256; d <<= 1) {
+        const int add = e >= d ? tot[e - d] : 0;
+        __syncthreads();
+        tot[e] += add;
+        __syncthreads();
+    }
+    if (e < E) offsets[e] = tot[e] - run;
+    if (e == E - 1) offsets[E] = tot[e];
+}
+
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ idx, int64_t S, int E,
+                                                   const int32_t *__restrict__ chunk_prefix,
+                                                   const int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ row_src, int32_t *__restrict__ slot_row) {
+    __shared__ int cnt[kWavesPerChunk][256];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t c = blockIdx.x;
+    for (int i = threadIdx.x; i < kWavesPerChunk * 256; i += 256) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+
+    const int64_t sub = c * kChunk + (int64_t)w * kSub;
+    for (int it = 0; it < kSub / 64; ++it) {
+        const int64_t s = sub + it * 64 + lane;
+        const int x = s < S ? valid_id(idx[s], E) : -1;
+        if (x >= 0) atomicAdd(&cnt[w][x], 1);
+    }
+    __syncthreads();
+    // per-wave base of every expert = offsets[e] + rows of e in earlier chunks + earlier waves
+    for (int e = threadIdx.x; e < E; e += 256) {
+        int b = offsets[e] + chunk_prefix[c * E + e];
+        for (int ww = 0; ww < kWavesPerChunk; ++ww) {
+            const int v = cnt[ww][e];
+            cnt[ww][e] = b;
+            b += v;
+        }
+    }
+    __syncthreads();
+
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int it = 0; it < kSub / 64; ++it) {
+        const int64_t s = sub + it * 64 + lane;
+        const int x = s < S ? valid_id(idx[s], E) : -1;
+        const unsigned key = (unsigned)(x + 1);  // 0 .. 256
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            const bool bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & lt);
+        int r = -1;
+        if (x >= 0) r = cnt[w][x] + rank;
+        // every lane has read its base; the lowest lane of each group advances it
+        __builtin_amdgcn_wave_barrier();
+        if (x >= 0 && rank == 0) cnt[w][x] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+        if (s < S) {
+            slot_row[s] = r;
+            if (r >= 0) row_src[r] = (int32_t)s;
+        }
+    }
+    // rows past the live count R hold -1 (this chunk's share of [R, S))
+    const int64_t R = offsets[E];
+    for (int i = threadIdx.x; i < kChunk; i += 256) {
+        const int64_t s = c * kChunk + i;
+        if (s < S && s >= R) row_src[s] = -1;
+    }
+}
+
+// tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert; n_tiles[0] = count.
+// One thread per expert; tiles are listed expert by expert.
+__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E,
+                                                          int32_t *__restrict__ tiles,
+                                                          int32_t *__restrict__ n_tiles) {
+    __shared__ int nt[256];
+    const int e = threadIdx.x;
+    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int mine = (cnt + kGemmBM - 1) / kGemmBM;
+    nt[e] = mine;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int add = e >= d ? nt[e - d] : 0;
+        __syncthreads();
+        nt[e] += add;
+        __syncthreads();
+    }
+    const int start = nt[e] - mine;
+    for (int m = 0; m < mine; ++m) {
+        tiles[2 * (start + m)] = e;
+        tiles[2 * (start + m) + 1] = m * kGemmBM;
+    }
+    if (e == 255) n_tiles[0] = nt[255];
+}
+
+hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *chunk_counts, int32_t *offsets,
+                         int32_t *row_src, int32_t *slot_row, hipStream_t s) {
+    const int64_t S = (int64_t)T * k;
+    const int64_t nch = (S + kChunk - 1) / kChunk;
+    hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(256), 0, s, topk_idx, S, E, chunk_counts);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, offsets);
+    hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(256), 0, s, topk_idx, S, E, chunk_counts, offsets, row_src,
+                       slot_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, tiles, n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace tpg
