@@ -7,26 +7,48 @@
 // Rows r of expert e are [offsets[e], offsets[e+1]): one ragged group per expert,
 // with no padding of the groups (Megatron-LM's "skip routed expert padding").
 //
-// Tiling.  A workgroup (4 waves) owns one (m-tile, n-tile) pair of one expert:
-// kBM token rows x kBN weight rows, K stepped by kBK = 64.  Both operands are
-// K-contiguous in HBM, so each 64-wide K slab of a row is eight 16-byte chunks; a
-// slab is staged global -> registers -> LDS (double buffered, one barrier per K
-// step) with chunk kc of row r stored at position kc ^ (r & 7), which makes the
-// 16-byte fragment reads of the MFMA loop conflict-free.  Each wave computes a
-// 64 x 64 sub-tile as 2 x 2 blocks of 32 x 32, issuing the weight fragment as the
-// MFMA's first operand so that a lane's 16 accumulators are 4 runs of 4
-// consecutive output columns of one token row (8-byte bf16 stores).
+// Tiling.  One workgroup of 4 waves (one per SIMD) owns a 256 x 256 output tile:
+// kBM token rows of one expert x kBN weight rows; each wave computes 128 x 128 as
+// 4 x 4 blocks of 32 x 32 (16 independent MFMAs per 16-wide K step, accumulators
+// in AGPRs).  Both operands are K-contiguous in HBM; K advances kBK = 64 per stage.
 //
-// SwiGLU fusion.  For GEMM1 the n-tile holds weight rows for 64 output columns
-// c0..c0+63 ordered [gate 32 | up 32 | gate 32 | up 32], so a wave's two 32-row
-// blocks are the gate and up values of the same 32 columns, in the same lanes,
-// and silu(g) * u is formed in registers.  With the interleave-32 layout these
-// 128 rows are one contiguous slice of W1; with [gate | up] they are two 64-row
-// slices I rows apart.
+// Pipeline.  LDS holds two stages (128 KB).  Global loads go to registers first:
+// while the MFMAs of stage k run, the wave writes stage k+1 from its register set
+// into the free LDS buffer and refills the set with the loads of stage k+2, so a
+// load has about one stage of MFMAs to land.  Per stage there is one
+// barrier, taken before the last 16-wide K step so that the next stage's first
+// fragments load under that step's MFMAs and the MFMA issue does not drain.
+// Fragment reads of step s+1 are interleaved with the MFMAs of step s.
 //
-// Ragged tails.  A tile with fewer than kBM live rows loads its last live row in
-// place of the missing ones (no out-of-range read) and stores only live rows.
-// Workgroups past the device-side tile count exit before any barrier.
+// LDS layout.  A stage row is 64 bf16 = eight 16-byte chunks; chunk kc of row r sits
+// at slot kc ^ ((r & 7) ^ ((r >> 3) & 1)).  A fragment read (32 rows, one chunk)
+// then hits distinct banks within every 8 rows (32-bank view) and every 16 rows
+// (64-bank view), and a thread's writes (rows r, r+32, ...) share one slot.
+//
+// Operand order.  The weight fragment is the MFMA's first operand, so a lane's 16
+// accumulators of a block are 4 runs of 4 consecutive output columns of one token
+// row (8-byte bf16 stores).
+//
+// SwiGLU fusion.  For GEMM1 an n-tile holds the weight rows of 128 output columns
+// c0..c0+127 ordered [gate 32 | up 32] x 4, so gate and up of a column are in the
+// same lane of two blocks and silu(g) * u is formed in registers.  With the
+// interleave-32 layout these 256 rows are one contiguous slice of W1; with
+// [gate | up] they are two 128-row slices I rows apart.
+//
+// Ragged tails.  Raw buffer resources bound every load: activation rows past the
+// tile's live rows, and weight rows past N (GEMM2 with H % 256 == 128), read as
+// zero.  A wave skips the MFMAs of 32-row blocks that hold no live row (the K loop
+// is instantiated per live-block count, so it stays branch-free) and only live
+// rows are stored.
+//
+// Scheduling.  The device-side tile list gives the m-tiles (expert, first row);
+// workgroup b runs on XCD b % 8, so it is mapped to position (b % 8) * per_xcd +
+// b / 8 of the (m-tile, n-tile) order: each XCD walks its own contiguous range, and
+// the 32 tiles an XCD runs at once share weight and activation rows in its L2.
+// Within the order, groups of kGroupM m-tiles are swept n-tile by n-tile.
+// Workgroups past the tile count exit before any barrier.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace tpg {
@@ -38,39 +60,75 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = kGemmBM;  // token rows per tile
-constexpr int kBN = 128;      // weight rows per tile
-constexpr int kBK = 64;       // K per LDS stage
+constexpr int kBM = kGemmBM;  // token rows per tile (256)
+constexpr int kBN = 256;      // weight rows per tile
+constexpr int kBK = 64;       // K per stage
 constexpr int kThreads = 256;
-constexpr int kChunksA = kBM * kBK / 8;  // 16-byte chunks per A stage
-constexpr int kChunksB = kBN * kBK / 8;
-constexpr int kLoadsA = kChunksA / kThreads;
-constexpr int kLoadsB = kChunksB / kThreads;
+constexpr int kGroupM = 4;    // m-tiles swept together along N
+constexpr int kRowBytes = kBK * 2;                    // 128: one row of one stage
+constexpr int kAStage = kBM * kRowBytes;               // 32 KB: activation rows of one stage
+constexpr int kBStage = kBN * kRowBytes;               // 32 KB: weight rows of one stage
+constexpr int kBStages = 3;                            // weight ring depth (DMA two stages ahead)
+constexpr int kBBase = 2 * kAStage;                    // weights follow the two activation stages
+constexpr int kLoads = kBM * kRowBytes / 16 / kThreads;  // 16-byte activation loads per thread (8)
+constexpr int kOpsB = kBStage / 1024 / 4;              // 1 KB weight DMAs per wave per stage (8)
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * 8 + (kc ^ (row & 7)); }
+__device__ __forceinline__ int slot(int r, int kc) { return kc ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
 __device__ __forceinline__ float silu_mul(float g, float u, float clamp) {
     if (clamp > 0.f) {
         g = fminf(fmaxf(g, -clamp), clamp);
         u = fminf(fmaxf(u, -clamp), clamp);
     }
-    return g / (1.0f + expf(-g)) * u;
+    // hardware exp2 / reciprocal (about 1 ulp each): far below the bf16 rounding of h
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-// stored W1 row of gate (up=false) or up (up=true) column c
-__device__ __forceinline__ int64_t w1_row(int c, bool up, int I, int il) {
-    if (il == 0) return up ? (int64_t)I + c : c;
-    return (int64_t)(c / il) * 2 * il + (up ? il : 0) + c % il;
+// one 16-byte-per-lane DMA from a raw buffer straight into LDS (1 KB per wave, lane-linear)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, void *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS barrier without a global-memory fence: register loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// scheduling pattern: NR fragment reads (DS) spread evenly over M MFMAs
+template <int NR, int M, int I = 0>
+__device__ __forceinline__ void interleave_ds_mfma() {
+    if constexpr (I < NR) {
+        constexpr int m = (M * (I + 1)) / NR - (M * I) / NR;
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       // DS read
+        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);  // MFMA
+        interleave_ds_mfma<NR, M, I + 1>();
+    }
+}
+
+// pattern with extra work: per group, X instructions of class `cls`, one DS read, MFMAs
+template <int cls, int X, int NR, int M, int I = 0>
+__device__ __forceinline__ void interleave_x_ds_mfma() {
+    if constexpr (I < NR) {
+        constexpr int m = (M * (I + 1)) / NR - (M * I) / NR;
+        constexpr int x = (X * (I + 1)) / NR - (X * I) / NR;
+        if constexpr (x > 0) __builtin_amdgcn_sched_group_barrier(cls, x, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+        interleave_x_ds_mfma<cls, X, NR, M, I + 1>();
+    }
 }
 
 }  // namespace
 
 template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const uint16_t *__restrict__ A,        // [S][K] activations in expert-contiguous row order
     const uint16_t *__restrict__ W,        // [E][N][K] expert weights
     const int32_t *__restrict__ offsets,   // [E+1]
@@ -78,127 +136,240 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_kernel(
     const int32_t *__restrict__ n_tiles,   // [1]
     int K, int N, int I, int il, float clamp,
     uint16_t *__restrict__ C, int ldc) {   // [S][ldc]
-    __shared__ u32x4 lds_a[2][kChunksA];
-    __shared__ u32x4 lds_b[2][kChunksB];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kBBase + kBStages * kBStage];  // 160 KB
 
-    const int nb_n = N / kBN;
-    const int mt = blockIdx.x / nb_n;
-    const int nt = blockIdx.x % nb_n;
-    if (mt >= n_tiles[0]) return;
+    // ---- tile of this workgroup (XCD-contiguous order, groups of kGroupM m-tiles)
+    const int nb_n = (N + kBN - 1) / kBN;
+    const int total = n_tiles[0] * nb_n;
+    const int per_xcd = (total + 7) / 8;
+    const int j = blockIdx.x >> 3;
+    if (j >= per_xcd) return;
+    const int t = (blockIdx.x & 7) * per_xcd + j;
+    if (t >= total) return;
+    const int n_mt = n_tiles[0];
+    const int group = t / (kGroupM * nb_n);
+    const int first_m = group * kGroupM;
+    const int gsize = min(kGroupM, n_mt - first_m);
+    const int in_group = t - group * kGroupM * nb_n;
+    const int mt = first_m + in_group % gsize;
+    const int nt = in_group / gsize;
+
     const int e = tiles[2 * mt];
     const int row_begin = offsets[e] + tiles[2 * mt + 1];
     const int rows = min(kBM, offsets[e + 1] - row_begin);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    // per-thread source rows of its 16-byte chunks (fixed over K)
-    const u32x4 *src_a[kLoadsA];
-    const u32x4 *src_b[kLoadsB];
-    int dst_a[kLoadsA], dst_b[kLoadsB];
-    const uint16_t *We = W + (int64_t)e * N * K;
+    // ---- activations: global -> registers -> LDS.  Thread loads chunk (tid & 7) of tile rows
+    //      (tid >> 3) + 32 i.  Weights: DMA straight into LDS, wave w filling rows w*64 .. w*64+63,
+    //      8 rows per 1 KB op (row lane/8, slot lane%8).  Raw buffer resources bound every read:
+    //      rows past the tile's live rows, and weight rows past N, read as zero.
+    const int lrow = tid >> 3, lkc = tid & 7;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A + (int64_t)row_begin * K), (short)0, rows * K * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(W + (int64_t)e * N * K), (short)0, N * K * 2, 0x00020000);
+    uint32_t offA[kLoads], offB[kOpsB];
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-        const int q = tid + i * kThreads, r = q >> 3, kc = q & 7;
-        const int rr = min(r, rows - 1);
-        src_a[i] = (const u32x4 *)(A + (int64_t)(row_begin + rr) * K) + kc;
-        dst_a[i] = swz(r, kc);
-    }
+    for (int i = 0; i < kLoads; ++i) offA[i] = (uint32_t)((lrow + 32 * i) * K + lkc * 8) * 2u;
 #pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) {
-        const int q = tid + i * kThreads, r = q >> 3, kc = q & 7;
-        int64_t wr;
+    for (int i = 0; i < kOpsB; ++i) {
+        const int r = wave * 64 + i * 8 + (lane >> 3);  // tile weight row
+        int wr;
         if (kSwiGLU) {
-            const int g = r >> 6, qq = r & 63;
-            const int c = nt * (kBN / 2) + g * 32 + (qq & 31);
-            wr = w1_row(c, qq >= 32, I, il);
+            // tile row r: wave column r >> 7, gate/up block (r >> 5) & 3 -> [g | u | g | u]
+            const int a = (r >> 5) & 3;
+            const int c = nt * (kBN / 2) + (r >> 7) * 64 + (a >> 1) * 32 + (r & 31);
+            const bool up = a & 1;
+            wr = il == 0 ? (up ? I + c : c) : (c / il) * 2 * il + (up ? il : 0) + c % il;
         } else {
-            wr = (int64_t)nt * kBN + r;
+            wr = nt * kBN + r;  // rows >= N read as zero
         }
-        src_b[i] = (const u32x4 *)(We + wr * K) + kc;
-        dst_b[i] = swz(r, kc);
+        const int kc = slot(r, lane & 7);  // the logical chunk LDS slot (lane & 7) holds
+        offB[i] = (uint32_t)(wr * K + kc * 8) * 2u;
     }
+    // LDS byte offset of this thread's activation writes (same slot for rows lrow + 32 i)
+    const int wofs = lrow * kRowBytes + slot(lrow, lkc) * 16;
 
-    f32x16 acc[2][2];
+    u32x4 RA0[kLoads], RA1[kLoads];
+    auto gloadA = [&](u32x4 *R, int kt) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int i = 0; i < kLoads; ++i) R[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[i], kt * kRowBytes, 0);
+    };
+    auto lwriteA = [&](const u32x4 *R, int astage) {
+        unsigned char *base = lds + astage * kAStage + wofs;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int i = 0; i < kLoads; ++i) *(u32x4 *)(base + i * 32 * kRowBytes) = R[i];
+    };
+    auto dmaB = [&](int kt, int bstage) {
+        unsigned char *dst = lds + kBBase + bstage * kBStage + wave * 64 * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kOpsB; ++i) dma16(rsB, offB[i], kt * kRowBytes, dst + i * 1024);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-    u32x4 ra[kLoadsA], rb[kLoadsB];
-    const int nk = K / kBK;
-#pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) ra[i] = src_a[i][0];
-#pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) rb[i] = src_b[i][0];
-#pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) lds_a[0][dst_a[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) lds_b[0][dst_b[i]] = rb[i];
-    __syncthreads();
+    // 32-row token blocks of this wave that hold a live row
+    const int nb_live = max(0, min(4, (rows - wm * 128 + 31) >> 5));
+    const int fr = lane & 31, fk = lane >> 5;
+    const int nk = K / kBK;  // even: K is a multiple of 128
 
-    const int frag_row = lane & 31, frag_kc = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const int off = (kt + 1) * (kBK / 8);  // in 16-byte chunks
+    auto mainloop = [&](auto nb_tag) {
+        constexpr int NB = decltype(nb_tag)::value;
+        constexpr int NR = 4 + NB;  // fragment reads per K step
+        constexpr int NM = 4 * NB;  // MFMAs per K step
+        bf16x8 fw[2][4], fx[2][NB > 0 ? NB : 1];
+        auto load = [&](int buf, int astage, int bstage, int ks) {
+            if constexpr (NB > 0) {
+                const u32x4 *sa = (const u32x4 *)(lds + astage * kAStage);
+                const u32x4 *sb = (const u32x4 *)(lds + kBBase + bstage * kBStage);
+                const int kc = ks * 2 + fk;
 #pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) ra[i] = src_a[i][off];
+                for (int a = 0; a < 4; ++a) {
+                    const int r = wn * 128 + a * 32 + fr;
+                    fw[buf][a] = __builtin_bit_cast(bf16x8, sb[r * 8 + slot(r, kc)]);
+                }
 #pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) rb[i] = src_b[i][off];
+                for (int b = 0; b < NB; ++b) {
+                    const int r = wm * 128 + b * 32 + fr;
+                    fx[buf][b] = __builtin_bit_cast(bf16x8, sa[r * 8 + slot(r, kc)]);
+                }
+            }
+        };
+        auto mfmas = [&](int buf) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][a], fx[buf][b], acc[a][b], 0, 0, 0);
+        };
+
+        // One stage kt: activations in LDS buffer kt & 1 (P), weights in ring slot bs = kt % 3;
+        // its step-0 fragments are already in fw/fx[0].  Issue order per stage (all VMEM, in
+        // order): weight DMA of kt+2 at the top, activation loads of kt+3 at step 2.  The weights
+        // of kt+1 (DMA issued one stage earlier) must have landed before the barrier; 24 younger
+        // VMEM ops (activations kt+2, weights kt+2, activations kt+3) may still be in flight.
+        // kIssue: stages kt+2 (weights) and kt+3 (activations) exist; kNext: stage kt+1 exists.
+        auto step = [&](auto p_tag, auto next_tag, auto issue_tag, int kt, int bs) {
+            constexpr int P = decltype(p_tag)::value;
+            constexpr bool kNext = decltype(next_tag)::value;
+            constexpr bool kIssue = decltype(issue_tag)::value;
+            u32x4 *Rn = P == 0 ? RA1 : RA0;  // holds the activations of stage kt+1
+            const int bs1 = bs + 1 == kBStages ? 0 : bs + 1;
+            const int bs2 = bs1 + 1 == kBStages ? 0 : bs1 + 1;
+            if constexpr (kIssue) {
+                dmaB(kt + 2, bs2);
+                __builtin_amdgcn_sched_group_barrier(0x020, kOpsB, 0);
+            }
+            // K step 0: fragments of step 1 under the MFMAs of step 0
+            load(1, P, bs, 1);
+            mfmas(0);
+            if constexpr (NB > 0) interleave_ds_mfma<NR, NM>();
+            // K step 1: activations of stage kt+1 into the free LDS buffer
+            if constexpr (kNext) lwriteA(Rn, P ^ 1);
+            load(0, P, bs, 2);
+            mfmas(1);
+            if constexpr (NB > 0) {
+                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads, NR, NM>();
+                else interleave_ds_mfma<NR, NM>();
+            }
+            // K step 2: refill the register set with the activations of stage kt+3
+            if constexpr (kIssue) {
+                if (kt + 3 < nk) gloadA(Rn, kt + 3);
+            }
+            load(1, P, bs, 3);
+            mfmas(0);
+            if constexpr (NB > 0) interleave_ds_mfma<NR, NM>();
+            // K step 3: publish stage kt+1 and load its first fragments under the last MFMAs
+            if constexpr (kNext) {
+                if constexpr (kIssue) {
+                    if (kt + 3 < nk) wait_vmcnt<2 * kLoads + kOpsB>();  // activations kt+2, kt+3; weights kt+2
+                    else wait_vmcnt<kLoads + kOpsB>();                 // no activations kt+3 were issued
+                } else {
+                    wait_vmcnt<0>();
+                }
+                lds_barrier();
+                load(0, P ^ 1, bs1, 0);
+            }
+            mfmas(1);
+            if constexpr (NB > 0 && kNext) interleave_ds_mfma<NR, NM>();
+        };
+        using T0 = std::integral_constant<int, 0>;
+        using T1 = std::integral_constant<int, 1>;
+        using Y = std::true_type;
+        using F = std::false_type;
+
+        // prologue: weights of stages 0 and 1 in flight, activations of 0 and 1 in flight,
+        // activations of 0 written, activations of 2 in flight
+        dmaB(0, 0);
+        dmaB(1, 1);
+        gloadA(RA0, 0);
+        gloadA(RA1, 1);
+        lwriteA(RA0, 0);
+        if (nk > 2) gloadA(RA0, 2);
+        wait_vmcnt<0>();
+        lds_barrier();
+        load(0, 0, 0, 0);
+        int bs = 0;
+        int kt = 0;
+        for (; kt + 2 < nk; kt += 2) {  // both stages of the pair issue (weights kt+2, kt+3 exist)
+            step(T0{}, Y{}, Y{}, kt, bs);
+            bs = bs + 1 == kBStages ? 0 : bs + 1;
+            step(T1{}, Y{}, Y{}, kt + 1, bs);
+            bs = bs + 1 == kBStages ? 0 : bs + 1;
         }
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            bf16x8 fw[2], fx[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-                fw[a] = __builtin_bit_cast(bf16x8, lds_b[cur][swz(wn * 64 + a * 32 + frag_row, ks * 2 + frag_kc)]);
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                fx[b] = __builtin_bit_cast(bf16x8, lds_a[cur][swz(wm * 64 + b * 32 + frag_row, ks * 2 + frag_kc)]);
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[a], fx[b], acc[a][b], 0, 0, 0);
-        }
-        if (kt + 1 < nk) {
-#pragma unroll
-            for (int i = 0; i < kLoadsA; ++i) lds_a[cur ^ 1][dst_a[i]] = ra[i];
-#pragma unroll
-            for (int i = 0; i < kLoadsB; ++i) lds_b[cur ^ 1][dst_b[i]] = rb[i];
-        }
-        __syncthreads();
+        // last pair: stage nk-2 has a next stage but nothing to issue; nk-1 is the last
+        step(T0{}, Y{}, F{}, nk - 2, bs);
+        bs = bs + 1 == kBStages ? 0 : bs + 1;
+        step(T1{}, F{}, F{}, nk - 1, bs);
+    };
+    switch (nb_live) {
+        case 4: mainloop(std::integral_constant<int, 4>{}); break;
+        case 3: mainloop(std::integral_constant<int, 3>{}); break;
+        case 2: mainloop(std::integral_constant<int, 2>{}); break;
+        case 1: mainloop(std::integral_constant<int, 1>{}); break;
+        default: mainloop(std::integral_constant<int, 0>{}); break;
     }
 
-    // epilogue: lane holds token row (lane & 31) of block b, weight rows m = 8*(v>>2) + 4*(lane>>5) + (v&3)
+    // ---- epilogue: lane holds token row (lane & 31) of block b and weight rows
+    //      m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) of block a
     const int half = lane >> 5;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int tr = wm * 64 + b * 32 + (lane & 31);
+    for (int b = 0; b < 4; ++b) {
+        const int tr = wm * 128 + b * 32 + (lane & 31);
         if (tr >= rows) continue;
         uint16_t *crow = C + (int64_t)(row_begin + tr) * ldc;
         if (kSwiGLU) {
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c0 = nt * (kBN / 2) + wn * 32 + g4 * 8 + half * 4;
-                float hv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) hv[j] = silu_mul(acc[0][b][g4 * 4 + j], acc[1][b][g4 * 4 + j], clamp);
-                u32x2 o;
-                o.x = pack2(hv[0], hv[1]);
-                o.y = pack2(hv[2], hv[3]);
-                *(u32x2 *)(crow + c0) = o;
-            }
-        } else {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int pr = 0; pr < 2; ++pr)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = nt * kBN + wn * 64 + a * 32 + g4 * 8 + half * 4;
+                    const int c0 = nt * (kBN / 2) + wn * 64 + pr * 32 + g4 * 8 + half * 4;
+                    float hv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        hv[q] = silu_mul(acc[2 * pr][b][g4 * 4 + q], acc[2 * pr + 1][b][g4 * 4 + q], clamp);
+                    u32x2 o;
+                    o.x = pack2(hv[0], hv[1]);
+                    o.y = pack2(hv[2], hv[3]);
+                    *(u32x2 *)(crow + c0) = o;
+                }
+        } else {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c0 = nt * kBN + wn * 128 + a * 32 + g4 * 8 + half * 4;
+                    if (c0 >= N) continue;
                     u32x2 o;
                     o.x = pack2(acc[a][b][g4 * 4 + 0], acc[a][b][g4 * 4 + 1]);
                     o.y = pack2(acc[a][b][g4 * 4 + 2], acc[a][b][g4 * 4 + 3]);
@@ -208,23 +379,30 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_bf16_kernel(
     }
 }
 
+namespace {
+template <bool kSwiGLU>
+hipError_t launch(const uint16_t *A, const uint16_t *W, const int32_t *offsets, const int32_t *tiles,
+                  const int32_t *n_tiles, int64_t max_tiles, int K, int N, int I, int il, float clamp, uint16_t *C,
+                  int ldc, hipStream_t s) {
+    const int nb_n = (N + kBN - 1) / kBN;
+    const int64_t total = max_tiles * nb_n;
+    const int64_t blocks = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kSwiGLU>, dim3(blocks), dim3(kThreads), 0, s, A, W, offsets, tiles,
+                       n_tiles, K, N, I, il, clamp, C, ldc);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
                                     int glu_interleave, float clamp, uint16_t *h, hipStream_t s) {
-    const int N = 2 * I;
-    const int64_t blocks = max_tiles * (N / kBN);
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, x_perm, w1, offsets,
-                       tiles, n_tiles, H, N, I, glu_interleave, clamp, h, I);
-    return hipGetLastError();
+    return launch<true>(x_perm, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave, clamp, h, I, s);
 }
 
 hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
                              hipStream_t s) {
-    const int64_t blocks = max_tiles * (H / kBN);
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, h, w2, offsets, tiles,
-                       n_tiles, I, H, I, 0, 0.0f, y_perm, H);
-    return hipGetLastError();
+    return launch<false>(h, w2, offsets, tiles, n_tiles, max_tiles, I, H, I, 0, 0.0f, y_perm, H, s);
 }
 
 }  // namespace tpg

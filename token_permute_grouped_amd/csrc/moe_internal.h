@@ -36,7 +36,7 @@ struct WsLayout {
 // rows of the permutation processed by one workgroup of the table kernels
 constexpr int kChunk = 1024;
 // M tile of the grouped GEMMs (rows of one expert per workgroup)
-constexpr int kGemmBM = 128;
+constexpr int kGemmBM = 256;
 
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
