@@ -68,6 +68,11 @@ def test_e4m3_encode_matches_torch_cast_on_every_midpoint():
     assert bad.size == 0, [(probes[i], got[i], want[i]) for i in bad[:10]]
 
 
+def test_e4m3_encode_nan_is_the_nan_code():
+    want = int(torch.tensor([float("nan")]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+    assert oracle.e4m3_encode(float("nan")) == want == 0x7F
+
+
 def test_e4m3_encode_saturates():
     # torch's cast overflows to NaN beyond 464; the reading used here (and on the GPU) saturates.
     for v in [448.0, 449.0, 464.0, 465.0, 1e6, 1e30]:
@@ -80,7 +85,8 @@ def test_fp4_to_fp8_dequant_table_matches_torch():
     for c in range(16):
         for s in range(256):
             sv = _torch_e4m3(s)
-            if np.isnan(sv):
+            if np.isnan(sv):    # outside the defined domain: NaN in, the NaN code out (torch's NaN cast)
+                assert tab[c, s] == int(torch.tensor([float("nan")]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
                 continue
             prod = np.float32(E2M1_VALUES[c & 7] * (-1 if c & 8 else 1) * sv)  # exact: <= 5 significant bits
             want = torch.tensor([np.clip(prod, -448, 448)], dtype=torch.float32).to(torch.float8_e4m3fn)
