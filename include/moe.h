@@ -73,8 +73,9 @@ enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
 
 typedef struct moe_problem {
     int32_t T;              /* tokens, >= 0 */
-    int32_t H;              /* hidden size, multiple of 128, 128..65536 */
-    int32_t I;              /* per-expert intermediate size, multiple of 128, 128..65536 */
+    int32_t H;              /* hidden size, multiple of 128 (W4A8: of 256), 128..65536 */
+    int32_t I;              /* per-expert intermediate size, multiple of 128 (W4A8: of 256);
+                               one expert matrix (2*I*H bf16) must be below 2 GB */
     int32_t E;              /* experts, 1..256 */
     int32_t k;              /* experts per token, 1..min(E, 32); T*k < 2^31 */
     int32_t prec;           /* MOE_PREC_BF16 or MOE_PREC_W4A8 */
@@ -169,9 +170,12 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
                       const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
                       void *const *stage_events);
 
-/* Diagnostic: writes the W4A8 dequant of every (e2m1 code c, e4m3 scale s) pair,
- * as E4M3 codes, to out8 uint8 [16][256] (device), using the same device
- * conversion the W4A8 GEMMs use. */
+/* Diagnostic: writes the W4A8 dequant of every (e2m1 code c, e4m3 block scale s)
+ * pair, as E4M3 codes, to out8 uint8 [2][16][256] (device): out8[0][c][s] with the
+ * code in the even-K (low) nibble of its byte, out8[1][c][s] in the odd-K (high)
+ * nibble.  Uses the same device routine as the W4A8 GEMMs (FlashInfer #6343: NVFP4
+ * -> FP8 dequant; e2m1 value times scale, rounded to nearest even, saturating; a
+ * NaN block scale, outside the defined domain, gives the NaN code 0x7F). */
 int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
 
 #ifdef __cplusplus

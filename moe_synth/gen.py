@@ -147,18 +147,24 @@ def _e4m3_decode(c: np.ndarray) -> np.ndarray:
     return t.to(torch.float32).numpy()
 
 
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], dtype=np.float32)
+
+
 def _e2m1_codes(v: np.ndarray) -> np.ndarray:
-    """float -> e2m1 codes (sign bit 3), round to nearest even, saturating at +-6."""
-    a = np.abs(v).astype(np.float64)
-    mids = (E2M1_VALUES[1:] + E2M1_VALUES[:-1]) / 2.0
-    idx = np.searchsorted(mids, a, side="left")          # a <= mid -> lower value
-    at_mid = np.zeros(a.shape, dtype=bool)
-    inb = idx < mids.size
-    at_mid[inb] = a[inb] == mids[idx[inb]]
-    # a exactly on a midpoint: searchsorted(left) chose the lower code; ties go to the even code
-    idx = np.where(at_mid & (idx % 2 == 1), idx + 1, idx)
+    """float32 -> e2m1 codes (sign bit 3), round to nearest even, saturating at +-6.
+
+    The magnitude code is the number of midpoints between neighbouring e2m1 values
+    that lie strictly below |v|; a value exactly on a midpoint goes to the even code.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v)
+    idx = np.zeros(v.shape, dtype=np.uint8)
+    for j, m in enumerate(_E2M1_MIDS):
+        idx += a > m
+        if j % 2 == 1:          # a tie at an odd midpoint rounds up to the even code j + 1
+            idx += a == m
     sign = (np.signbit(v) & (idx > 0)).astype(np.uint8)
-    return (idx.astype(np.uint8) | (sign << 3)).astype(np.uint8)
+    return idx | (sign << np.uint8(3))
 
 
 def _quantise_act_rows(xf: np.ndarray):
@@ -183,16 +189,19 @@ def _quantise_nvfp4(w: np.ndarray):
     gs = np.float32(np.abs(w).max() / 448.0)
     if gs == 0:
         gs = np.float32(1.0)
-    blk = w.reshape(N, K // 16, 16)
-    amax16 = np.abs(blk).max(axis=2).astype(np.float32)
-    bs_code = _e4m3_codes((amax16 / (np.float32(6.0) * gs)).astype(np.float32))
-    bs_val = _e4m3_decode(bs_code).astype(np.float32)
-    denom = (bs_val * gs)[:, :, None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        ratio = np.where(denom > 0, blk / np.where(denom > 0, denom, 1), 0).astype(np.float32)
-    codes = _e2m1_codes(ratio).reshape(N, K)
-    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return packed, bs_code.reshape(N, K // 16), gs
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    bs_code = np.empty((N, K // 16), dtype=np.uint8)
+    for r0 in range(0, N, 256):  # row blocks keep the temporaries small
+        blk = w[r0:r0 + 256].reshape(-1, K // 16, 16)
+        amax16 = np.abs(blk).max(axis=2).astype(np.float32)
+        bc = _e4m3_codes((amax16 / (np.float32(6.0) * gs)).astype(np.float32))
+        denom = (_e4m3_decode(bc).astype(np.float32) * gs)[:, :, None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(denom > 0, blk / np.where(denom > 0, denom, 1), 0).astype(np.float32)
+        codes = _e2m1_codes(ratio).reshape(-1, K)
+        packed[r0:r0 + 256] = codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))
+        bs_code[r0:r0 + 256] = bc
+    return packed, bs_code, gs
 
 
 # ----------------------------------------------------------------------------

@@ -48,6 +48,8 @@ def _p(**kw):
     (dict(T=2 ** 28, k=8), tpg.MOE_ERR_SHAPE), (dict(prec=7), tpg.MOE_ERR_UNSUPPORTED),
     (dict(glu_interleave=16), tpg.MOE_ERR_UNSUPPORTED), (dict(swiglu_clamp=-1.0), tpg.MOE_ERR_UNSUPPORTED),
     (dict(swiglu_clamp=float("nan")), tpg.MOE_ERR_UNSUPPORTED),
+    (dict(prec=1, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=1, I=384), tpg.MOE_ERR_SHAPE),
+    (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE),
 ])
 def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     lib = tpg.load()
@@ -76,7 +78,7 @@ def test_null_pointers_are_rejected():
     assert lib.moe_forward(FAKE, None, None, None, w, p, FAKE, FAKE, 1 << 40, None) == NULL
     assert lib.moe_w4a8_dequant_table(None, None) == NULL
     # W4A8 needs the scale arrays too
-    p4 = ctypes.byref(_p(prec=tpg.MOE_PREC_W4A8))
+    p4 = ctypes.byref(_p(prec=tpg.MOE_PREC_W4A8, H=256))
     assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p4, FAKE, FAKE, 1 << 40, None) == NULL
     assert lib.moe_forward(FAKE, None, FAKE, None, ctypes.byref(tpg.Weights(*[FAKE] * 6)), p4, FAKE, FAKE,
                            1 << 40, None) == NULL

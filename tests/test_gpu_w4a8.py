@@ -1,0 +1,160 @@
+"""GPU parity of the W4A8 path (FP8 E4M3 activations x NVFP4 weights dequantised
+to FP8 in-kernel) against the CPU oracle.
+
+Bars: the NVFP4 -> FP8 dequant of every (code, block scale) pair bit-exact in both
+nibble positions; routing, tables and permuted rows (fp8 codes and their fp32
+scales) bit-exact; expert outputs and the forward max|err| / max|ref| <= 3e-2
+against the fp64 oracle (the kernel accumulates in fp32 and re-quantises the
+SwiGLU output from fp32 values, so a few fp8 codes of h may land one step away
+from the oracle's).
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_permute_grouped_amd as tpg
+from moe_synth import CONFIGS, MoeConfig, generate
+from moe_synth.gen import w4a8_sweep_tokens
+from tests._gpu import DEV, DeviceProblem, bf16_f64, bf16_host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+W4A8_BAR = 3e-2
+SMALL = {
+    "w4_tiny": MoeConfig("w4_tiny", T=64, H=256, I=256, E=8, k=2, prec="w4a8", swiglu_clamp=10.0),
+    "w4_one_token": MoeConfig("w4_one_token", T=1, H=256, I=256, E=4, k=4, prec="w4a8", swiglu_clamp=10.0),
+    "w4_interleaved_drop": MoeConfig("w4_interleaved_drop", T=100, H=512, I=512, E=6, k=3, prec="w4a8",
+                                     glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    "w4_ragged_no_clamp": MoeConfig("w4_ragged_no_clamp", T=300, H=768, I=768, E=5, k=2, prec="w4a8"),
+    "w4_tight_clamp": MoeConfig("w4_tight_clamp", T=90, H=512, I=256, E=4, k=2, prec="w4a8", swiglu_clamp=0.5),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def small(name):
+    cfg = SMALL[name]
+    print(f"[gpu w4a8] generating {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    inp = generate(cfg, seed=0)
+    return inp, DeviceProblem(inp)
+
+
+@functools.lru_cache(maxsize=1)
+def full_weights():
+    print("[gpu w4a8] generating the W4A8 layer (H=7168 I=2048 E=32 top-8, T=256)", flush=True)
+    return generate(CONFIGS["w4a8"], seed=0)
+
+
+def sweep_case(T: int):
+    """the first T tokens of the T=256 draw (the generator's x and logits rows do not depend on T)"""
+    base = full_weights()
+    inp = dict(base, cfg=CONFIGS["w4a8"].with_tokens(T), logits=base["logits"][:T], x=base["x"][:T],
+               x_scale=base["x_scale"][:T])
+    return inp, DeviceProblem(inp)
+
+
+def test_dequant_table_both_nibbles_bit_exact():
+    out = torch.full((2, 16, 256), 0x55, dtype=torch.uint8, device=DEV)
+    tpg.moe_w4a8_dequant_table(out)
+    got = out.cpu().numpy()
+    ref = oracle.fp4_to_fp8_table()
+    bad = np.argwhere(got[0] != ref)
+    assert bad.size == 0, f"low nibble: first mismatches (code, scale) {bad[:8].tolist()}"
+    bad = np.argwhere(got[1] != ref)
+    assert bad.size == 0, f"high nibble: first mismatches (code, scale) {bad[:8].tolist()}"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permute_fp8_rows_and_scales_bit_exact(name):
+    inp, d = small(name)
+    cfg = inp["cfg"]
+    idx, _ = d.route()
+    offsets, row_src, slot_row, x_perm, x_perm_scale = d.permute(idx)
+    torch.cuda.synchronize()
+    ref_idx, _ = oracle.route(inp["logits"], cfg.k, inp.get("slot_drop"))
+    assert (idx.cpu().numpy() == ref_idx).all()
+    _, ref_off, ref_rs, ref_sr = oracle.tables(ref_idx, cfg.E)
+    assert (offsets.cpu().numpy() == ref_off).all()
+    assert (slot_row.cpu().numpy() == ref_sr).all()
+    R = int(ref_off[-1])
+    tok = ref_rs[:R] // cfg.k
+    assert (x_perm.cpu().numpy()[:R] == inp["x"][tok]).all()
+    xs = x_perm_scale.cpu().numpy()
+    assert (xs[:R].view(np.uint32) == inp["x_scale"][tok].view(np.uint32)).all()
+    assert (x_perm.cpu().numpy()[R:] == 0x7F).all()      # canary rows past R untouched
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_grouped_ffn_rows(name):
+    inp, d = small(name)
+    cfg = inp["cfg"]
+    idx, _ = d.route()
+    offsets, row_src, _, x_perm, x_perm_scale = d.permute(idx)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    R = int(off[-1])
+    rows = np.arange(R)
+    expert = np.searchsorted(off, rows, side="right") - 1
+    ref = oracle.ffn_rows(inp, row_src.cpu().numpy()[rows] // cfg.k, expert)
+    got_bits = bf16_host(y)
+    err = rel_err(bf16_f64(got_bits[rows]), ref)
+    print(f"[gpu w4a8] {name}: grouped FFN on {R} rows, max|err|/max|ref| = {err:.3e}")
+    assert err <= W4A8_BAR
+    assert (got_bits[R:] == 0xFFFF).all()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    inp, d = small(name)
+    out = bf16_host(d.forward())
+    ref = oracle.moe_forward(inp)
+    err = rel_err(bf16_f64(out), ref)
+    print(f"[gpu w4a8] {name}: forward, max|err|/max|ref| = {err:.3e}")
+    assert err <= W4A8_BAR
+
+
+@pytest.mark.parametrize("T", w4a8_sweep_tokens())
+def test_forward_token_sweep(T):
+    inp, d = sweep_case(T)
+    out = bf16_host(d.forward())
+    tokens = np.arange(T) if T <= 16 else np.unique(
+        np.concatenate([np.random.default_rng(T).integers(0, T, 6), [0, T - 1]]))
+    ref = oracle.moe_forward(inp, tokens)
+    err = rel_err(bf16_f64(out[tokens]), ref)
+    print(f"[gpu w4a8] sweep T={T}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}")
+    assert err <= W4A8_BAR
+
+
+def test_grouped_ffn_full_layer_sampled_rows():
+    inp, d = sweep_case(256)
+    cfg = inp["cfg"]
+    idx, _ = d.route()
+    offsets, row_src, _, x_perm, x_perm_scale = d.permute(idx)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    torch.cuda.synchronize()
+    off = offsets.cpu().numpy()
+    rows = []
+    for e in range(cfg.E):
+        if off[e + 1] > off[e]:
+            rows += [off[e], off[e + 1] - 1]
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    expert = np.searchsorted(off, rows, side="right") - 1
+    ref = oracle.ffn_rows(inp, row_src.cpu().numpy()[rows] // cfg.k, expert)
+    err = rel_err(bf16_f64(bf16_host(y)[rows]), ref)
+    print(f"[gpu w4a8] full layer: grouped FFN on {rows.size} rows, max|err|/max|ref| = {err:.3e}")
+    assert err <= W4A8_BAR
+
+
+def test_forward_deterministic_and_workspace_reuse():
+    _, d = sweep_case(128)
+    ws = d.workspace(tpg.MOE_WS_FORWARD, fill=0x00)
+    a = bf16_host(d.forward(ws))
+    b = bf16_host(d.forward(ws))
+    c = bf16_host(d.forward())
+    assert (a == b).all() and (a == c).all()
+

@@ -19,7 +19,11 @@ int check_problem(const moe_problem *p) {
     if (p->H < 128 || p->H > 65536 || p->H % 128 != 0) return MOE_ERR_SHAPE;
     if (p->I < 128 || p->I > 65536 || p->I % 128 != 0) return MOE_ERR_SHAPE;
     if ((int64_t)p->T * p->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+    // one expert matrix must stay below 2 GB (32-bit byte offsets inside a matrix)
+    if ((int64_t)p->H * p->I * 4 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     if (p->prec != MOE_PREC_BF16 && p->prec != MOE_PREC_W4A8) return MOE_ERR_UNSUPPORTED;
+    // W4A8 stages K 256 at a time: H and I multiples of 256
+    if (p->prec == MOE_PREC_W4A8 && (p->H % 256 != 0 || p->I % 256 != 0)) return MOE_ERR_SHAPE;
     if (p->glu_interleave != 0 && p->glu_interleave != 32) return MOE_ERR_UNSUPPORTED;
     if (!(p->swiglu_clamp >= 0.0f) || p->swiglu_clamp > 3.0e38f) return MOE_ERR_UNSUPPORTED;  // also rejects NaN
     return MOE_OK;
@@ -57,6 +61,8 @@ WsLayout ws_layout(const moe_problem &p) {
     o = align256(o + S * (size_t)p.I * act);
     L.h_scale = o;
     if (is_w4a8(&p)) o = align256(o + S * (size_t)(p.I / 128) * 4);
+    L.h32 = o;
+    if (is_w4a8(&p)) o = align256(o + S * (size_t)p.I * 4);
     L.ffn_end = o;
     L.topk_idx = o;
     o = align256(o + S * 4);
@@ -96,12 +102,12 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
     int32_t *tiles = (int32_t *)(ws + L.tiles);
     int32_t *n_tiles = (int32_t *)(ws + L.n_tiles);
     const int64_t max_tiles = max_m_tiles(p);
-    int st = hip_status(launch_build_tiles(offsets, p.E, tiles, n_tiles, s));
+    int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), tiles, n_tiles, s));
     if (st) return st;
     if (is_w4a8(&p))
         return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,
-                                                  max_tiles, w, p, (uint8_t *)(ws + L.h), (float *)(ws + L.h_scale),
-                                                  (uint16_t *)y_perm, s));
+                                                  max_tiles, w, p, (float *)(ws + L.h32), (uint8_t *)(ws + L.h),
+                                                  (float *)(ws + L.h_scale), (uint16_t *)y_perm, s));
     uint16_t *h = (uint16_t *)(ws + L.h);
     st = hip_status(launch_gemm1_swiglu_bf16((const uint16_t *)x_perm, (const uint16_t *)w.w1, offsets, tiles,
                                              n_tiles, max_tiles, p.H, p.I, p.glu_interleave, p.swiglu_clamp, h, s));
@@ -149,11 +155,11 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
                                         x_perm_scale, s))))
         return st;
     if ((st = mark(3))) return st;
-    if ((st = hip_status(launch_build_tiles(offsets, p->E, tiles, n_tiles, s)))) return st;
+    if ((st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), tiles, n_tiles, s)))) return st;
     if ((st = mark(4))) return st;
     if (w4) {
         if ((st = hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,
-                                                     max_tiles, *w, *p, (uint8_t *)(b + L.h),
+                                                     max_tiles, *w, *p, (float *)(b + L.h32), (uint8_t *)(b + L.h),
                                                      (float *)(b + L.h_scale), (uint16_t *)y_perm, s))))
             return st;
         if ((st = mark(5))) return st;

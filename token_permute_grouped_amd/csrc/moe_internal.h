@@ -18,10 +18,11 @@ constexpr int kWave = 64;
 // shape.  Offsets are 256-byte aligned.
 struct WsLayout {
     size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
-    size_t tiles;         // int32 [max_tiles]      grouped GEMMs: (expert << 20 | m_tile) list
+    size_t tiles;         // int32 [2 * max_tiles]  grouped GEMMs: (expert, first row) per m-tile
     size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count
-    size_t h;             // bf16 [S][I]  or fp8 [S][I] + fp32 [S][I/128]
-    size_t h_scale;
+    size_t h;             // bf16 [S][I]  or (W4A8) fp8 [S][I]
+    size_t h_scale;       // W4A8: fp32 [S][I/128]
+    size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation)
     size_t topk_idx;      // forward only: int32 [T][k]
     size_t topk_w;        // forward only: fp32 [T][k]
     size_t offsets;       // forward only: int32 [E+1]
@@ -35,12 +36,15 @@ struct WsLayout {
 
 // rows of the permutation processed by one workgroup of the table kernels
 constexpr int kChunk = 1024;
-// M tile of the grouped GEMMs (rows of one expert per workgroup)
+// M tile (rows of one expert per workgroup) of the bf16 and of the W4A8 grouped GEMMs
 constexpr int kGemmBM = 256;
+constexpr int kGemmBMW4A8 = 128;
 
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
-inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + kGemmBM - 1) / kGemmBM + p.E; }
+inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_W4A8 ? kGemmBMW4A8 : kGemmBM; }
+// upper bound of sum_e ceil(count_e / bm) over any routing
+inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + gemm_bm(p) - 1) / gemm_bm(p) + p.E; }
 
 WsLayout ws_layout(const moe_problem &p);
 
@@ -54,7 +58,7 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
 hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *slot_row, int T, int k, int H,
                           int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);
 
-hipError_t launch_build_tiles(const int32_t *offsets, int E, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
 
 hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
@@ -66,7 +70,7 @@ hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_
 
 hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *offsets,
                                    const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles,
-                                   const moe_weights &w, const moe_problem &p, uint8_t *h, float *h_scale,
+                                   const moe_weights &w, const moe_problem &p, float *h32, uint8_t *h8, float *hs,
                                    uint16_t *y_perm, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,

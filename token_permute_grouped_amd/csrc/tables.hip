@@ -135,15 +135,16 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ i
     }
 }
 
-// tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert; n_tiles[0] = count.
+// tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert (tiles of bm rows);
+// n_tiles[0] = count.
 // One thread per expert; tiles are listed expert by expert.
-__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E,
+__global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E, int bm,
                                                           int32_t *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles) {
     __shared__ int nt[256];
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int mine = (cnt + kGemmBM - 1) / kGemmBM;
+    const int mine = (cnt + bm - 1) / bm;
     nt[e] = mine;
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
     const int start = nt[e] - mine;
     for (int m = 0; m < mine; ++m) {
         tiles[2 * (start + m)] = e;
-        tiles[2 * (start + m) + 1] = m * kGemmBM;
+        tiles[2 * (start + m) + 1] = m * bm;
     }
     if (e == 255) n_tiles[0] = nt[255];
 }
@@ -171,8 +172,8 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
     return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(const int32_t *offsets, int E, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, tiles, n_tiles);
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, bm, tiles, n_tiles);
     return hipGetLastError();
 }
 
