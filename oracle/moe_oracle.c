@@ -96,8 +96,8 @@ double orc_e2m1_value(uint8_t c)
     return s ? -v : v;
 }
 
-/* Nearest E4M3FN code to v, ties to the even code, saturating at +-448; NaN gives
- * the NaN code 0x7F.  The 127 non-negative finite codes 0x00..0x7E have increasing magnitude, so
+/* Nearest E4M3FN code to v, ties to the even code, saturating at +-448; a NaN
+ * gives the NaN code with its sign (0x7F or 0xFF).  The 127 non-negative finite codes 0x00..0x7E have increasing magnitude, so
  * the nearest one is found by a binary search over their values. */
 static double e4m3_mag[127]; /* magnitudes of the non-negative finite codes 0x00..0x7E */
 
@@ -114,7 +114,7 @@ uint8_t orc_e4m3_encode(double v)
     double a = fabs(v);
     int lo, hi, c;
     if (isnan(v))
-        return 0x7F;
+        return (signbit(v) ? 0x80 : 0) | 0x7F;
     if (a >= mag[126])
         return sign | 126;
     lo = 0;
@@ -137,9 +137,12 @@ uint8_t orc_e4m3_encode(double v)
 
 /* NVFP4 -> FP8 dequant of one weight: e2m1(code) * e4m3(block scale), rounded to
  * E4M3 [FI6343, nvfp4_dequant: NVFP4 -> FP8].  The product is exact in fp64.  The
- * pages define finite block scales only; a NaN scale (0x7F, 0xFF) gives 0x7F. */
+ * pages define finite block scales only; a NaN scale (0x7F, 0xFF) gives the NaN
+ * code whose sign is that of the product: sign(code) xor sign(scale). */
 uint8_t orc_fp4_to_fp8(uint8_t code4, uint8_t scale8)
 {
+    if ((scale8 & 0x7F) == 0x7F)
+        return (uint8_t)(0x7F | ((((code4 >> 3) ^ (scale8 >> 7)) & 1) << 7));
     return orc_e4m3_encode(orc_e2m1_value(code4 & 15) * orc_e4m3_value(scale8));
 }
 

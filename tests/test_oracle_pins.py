@@ -68,9 +68,10 @@ def test_e4m3_encode_matches_torch_cast_on_every_midpoint():
     assert bad.size == 0, [(probes[i], got[i], want[i]) for i in bad[:10]]
 
 
-def test_e4m3_encode_nan_is_the_nan_code():
-    want = int(torch.tensor([float("nan")]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
-    assert oracle.e4m3_encode(float("nan")) == want == 0x7F
+def test_e4m3_encode_nan_is_the_nan_code_with_its_sign():
+    for v, code in [(float("nan"), 0x7F), (-float("nan"), 0xFF)]:
+        want = int(torch.tensor([v]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+        assert oracle.e4m3_encode(v) == want == code
 
 
 def test_e4m3_encode_saturates():
@@ -85,8 +86,10 @@ def test_fp4_to_fp8_dequant_table_matches_torch():
     for c in range(16):
         for s in range(256):
             sv = _torch_e4m3(s)
-            if np.isnan(sv):    # outside the defined domain: NaN in, the NaN code out (torch's NaN cast)
-                assert tab[c, s] == int(torch.tensor([float("nan")]).to(torch.float8_e4m3fn).view(torch.uint8)[0])
+            if np.isnan(sv):    # outside the defined domain: the NaN code carrying the product's sign
+                neg = bool(c & 8) != bool(s & 0x80)
+                nan = torch.tensor([-float("nan") if neg else float("nan")]).to(torch.float8_e4m3fn)
+                assert tab[c, s] == int(nan.view(torch.uint8)[0]), (c, s)
                 continue
             prod = np.float32(E2M1_VALUES[c & 7] * (-1 if c & 8 else 1) * sv)  # exact: <= 5 significant bits
             want = torch.tensor([np.clip(prod, -448, 448)], dtype=torch.float32).to(torch.float8_e4m3fn)
