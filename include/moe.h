@@ -170,12 +170,15 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
                       const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
                       void *const *stage_events);
 
-/* Diagnostic: writes the W4A8 dequant of every (e2m1 code c, e4m3 block scale s)
- * pair, as E4M3 codes, to out8 uint8 [2][16][256] (device): out8[0][c][s] with the
- * code in the even-K (low) nibble of its byte, out8[1][c][s] in the odd-K (high)
- * nibble.  Uses the same device routine as the W4A8 GEMMs (FlashInfer #6343: NVFP4
- * -> FP8 dequant; e2m1 value times scale, rounded to nearest even, saturating; a
- * NaN block scale, outside the defined domain, gives the NaN code 0x7F). */
+/* Diagnostic: the W4A8 dequant of every (e2m1 code, e4m3 block scale s) pair at
+ * every nibble position, through the same device routine as the W4A8 GEMMs
+ * (FlashInfer #6343: NVFP4 -> FP8 dequant; e2m1 value times scale, rounded to
+ * nearest even, saturating at +-448).  out8 is uint8 [8][16][256] (device):
+ * a dword holding code (c + p) mod 16 at nibble position p = 0..7 (low nibble
+ * first) is dequantised with scale s, and out8[p][c][s] receives result byte p,
+ * so out8[p][c][s] is the e4m3 code of code (c + p) mod 16 times scale s.  A NaN
+ * block scale, outside the defined domain, gives the NaN code with the product's
+ * sign. */
 int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
 
 #ifdef __cplusplus

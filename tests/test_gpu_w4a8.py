@@ -57,15 +57,15 @@ def sweep_case(T: int):
     return inp, DeviceProblem(inp)
 
 
-def test_dequant_table_both_nibbles_bit_exact():
-    out = torch.full((2, 16, 256), 0x55, dtype=torch.uint8, device=DEV)
+def test_dequant_table_every_nibble_position_bit_exact():
+    out = torch.full((8, 16, 256), 0x55, dtype=torch.uint8, device=DEV)
     tpg.moe_w4a8_dequant_table(out)
     got = out.cpu().numpy()
     ref = oracle.fp4_to_fp8_table()
-    bad = np.argwhere(got[0] != ref)
-    assert bad.size == 0, f"low nibble: first mismatches (code, scale) {bad[:8].tolist()}"
-    bad = np.argwhere(got[1] != ref)
-    assert bad.size == 0, f"high nibble: first mismatches (code, scale) {bad[:8].tolist()}"
+    for p in range(8):
+        want = ref[(np.arange(16) + p) % 16]
+        bad = np.argwhere(got[p] != want)
+        assert bad.size == 0, f"position {p}: first mismatches (c, scale) {bad[:8].tolist()}"
 
 
 @pytest.mark.parametrize("name", list(SMALL))

@@ -173,4 +173,7 @@ def moe_forward_timed(logits, slot_drop, x, x_scale, weights: Weights, problem: 
 
 
 def moe_w4a8_dequant_table(out8, stream=None):
+    """out8: device uint8 [8][16][256] (see include/moe.h)."""
+    if _nbytes(out8) < 8 * 16 * 256:
+        raise ValueError("moe_w4a8_dequant_table needs an 8*16*256-byte output")
     _check("moe_w4a8_dequant_table", load().moe_w4a8_dequant_table(_ptr(out8), _stream(stream)))

@@ -14,29 +14,32 @@
 //   2. re-quantisation of h per (row, 128 columns): s = amax/448 (1 if 0), q = e4m3(h / s)
 //   3. GEMM2: y = gs2_e * sum_kb hs[kb] * (h8 . w8), rounded to bf16
 //
-// GEMM tiling.  A workgroup (4 waves) owns one expert m-tile of 128 token rows and
-// 128 weight rows; wave w computes token block w (32 rows) against all 128 weight
-// rows (4 MFMA blocks).  K advances 256 per stage: the workgroup dequantises the
-// stage's 128 x 256 weights once into LDS (double buffered, one barrier per stage)
-// and every wave reads them from there; activation fragments come straight from
-// global memory (they are small and stay in L2).  The MFMA partial of each 128-wide
-// K block is kept apart and added to the accumulator times that block's activation
-// scale (fp32), so the per-128 scales are applied exactly as the definition states.
-// The workload is bound by streaming the packed weights: each weight byte of an
-// m-tile is read once.
+// The GEMMs stream packed weights, which is what bounds them at small token counts.
+// Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows and
+// 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every token of the
+// tile.  Weights are never shared between waves, so each wave loads its rows straight
+// into registers in the MFMA operand layout (lane l: row l % 32, one contiguous
+// 32-code run per 64-wide K step) and dequantises them there.  K advances 256 per
+// chunk; weights are loaded three chunks ahead (four register sets).  Activations are
+// shared by the four waves: each chunk of the tile's token rows, and its activation
+// scales, go straight from global memory into LDS by buffer-load DMA (four buffers,
+// swizzled), and each wave waits only for its own DMA before the chunk's barrier, so
+// the weight prefetch stays in flight across barriers.
+// K is visited so that both halves of a 64-wide MFMA step lie in one 128-wide
+// activation-scale block; the partial sum of each block is added to the accumulator
+// times that block's activation scale (fp32), as the definition states.
 //
-// Dequant.  Eight codes (one dword, low nibble first) and their block scale become
-// eight fp8 bytes: v_cvt_scalef32_pk_f32_fp4 (unit scale) gives the e2m1 values, an
-// fp32 multiply by the scale is exact, v_med3 saturates to +-448 and
-// v_cvt_pk_fp8_f32 rounds to nearest even.
+// Dequant.  A per-workgroup LDS table holds, for every e4m3 block-scale code, the
+// e4m3 codes of the eight e2m1 magnitudes times that scale (rounded to nearest even,
+// saturating at +-448; the products are exact in fp32).  Eight packed codes (one
+// dword, low nibble first) then become eight e4m3 bytes with two v_perm_b32 table
+// selects, a sign xor and two v_perm_b32 interleaves.
 //
 // Operand layout of v_mfma_*_32x32x64_f8f6f4 (checked on the device): lane l holds
 // row l % 32 and the 32 consecutive K bytes starting at 32 * (l / 32); the output
 // layout is that of the 32 x 32 bf16 MFMA.  The weight fragment is the first
 // operand, so a lane's accumulators are runs of 4 consecutive output columns of
 // one token row.
-#include <type_traits>
-
 #include "moe_internal.h"
 
 namespace tpg {
@@ -50,11 +53,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;       // token rows per m-tile (4 waves x 32)
-constexpr int kBN = 128;       // weight rows per tile
-constexpr int kKC = 256;       // K per stage
+constexpr int kBM = kGemmBMW4A8;  // token rows per m-tile (2 blocks of 32)
+constexpr int kBN = 128;          // weight rows per workgroup (4 waves x 32)
+constexpr int kKC = 256;          // K per chunk
+constexpr int kNBuf = 4;          // chunks in flight: activation buffers and weight register sets
 constexpr int kThreads = 256;
-constexpr int kStage = kBN * kKC;  // fp8 bytes of one dequantised stage (32 KB)
+constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB)
+static_assert(kBM == 64, "the tile holds at most two 32-token blocks");
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
 
@@ -66,52 +71,285 @@ __device__ __forceinline__ uint32_t to_fp8x2(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, kHi);
 }
 
-// eight packed e2m1 codes (low nibble first) with e4m3 block scale code `sc` -> eight
-// e4m3 bytes.  The code is converted at unit scale and multiplied in fp32, which is
-// exact (a 2-bit times a 4-bit significand), so the only rounding is the one to e4m3.
-// A NaN scale (0x7F / 0xFF) makes all eight the NaN code 0x7F.
-__device__ __forceinline__ u32x2 dequant8(uint32_t codes, uint32_t sc) {
-    const float scale = e4m3_to_f32(sc & 0xffu);
-    f32x2 p[4];
-    p[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-    p[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-    p[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-    p[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        p[i].x *= scale;
-        p[i].y *= scale;
-    }
-    u32x2 r;
-    r.x = to_fp8x2<true>(p[1].x, p[1].y, to_fp8x2<false>(p[0].x, p[0].y, 0u));
-    r.y = to_fp8x2<true>(p[3].x, p[3].y, to_fp8x2<false>(p[2].x, p[2].y, 0u));
-    if ((sc & 0x7fu) == 0x7fu) r = u32x2{0x7f7f7f7fu, 0x7f7f7f7fu};
-    return r;
+// byte m = e4m3 code of (e2m1 magnitude m) * e4m3(sc), m = 0..7.  A NaN scale gives
+// NaN codes with the scale's sign (the code's sign is applied by the xor in dequant8).
+__device__ __forceinline__ u32x2 scaled_e2m1_table(uint32_t sc) {
+    const float s = e4m3_to_f32(sc & 0xffu);
+    u32x2 t;
+    t.x = to_fp8x2<true>(1.0f * s, 1.5f * s, to_fp8x2<false>(0.0f * s, 0.5f * s, 0u));
+    t.y = to_fp8x2<true>(4.0f * s, 6.0f * s, to_fp8x2<false>(2.0f * s, 3.0f * s, 0u));
+    if ((sc & 0x7fu) == 0x7fu) t.x = t.y = (sc & 0x80u) ? 0xffffffffu : 0x7f7f7f7fu;
+    return t;
+}
+
+// eight e2m1 codes (low nibble first) -> eight e4m3 codes, through the table t of their
+// block scale.  v_perm_b32 selector bytes 0..3 pick bytes of the second source, 4..7 of
+// the first.
+__device__ __forceinline__ u32x2 dequant8(uint32_t x, u32x2 t) {
+    const uint32_t me = __builtin_amdgcn_perm(t.y, t.x, x & 0x07070707u);         // codes 0, 2, 4, 6
+    const uint32_t mo = __builtin_amdgcn_perm(t.y, t.x, (x >> 4) & 0x07070707u);  // codes 1, 3, 5, 7
+    const uint32_t ve = me ^ ((x << 4) & 0x80808080u);
+    const uint32_t vo = mo ^ (x & 0x80808080u);
+    return u32x2{__builtin_amdgcn_perm(vo, ve, 0x05010400u), __builtin_amdgcn_perm(vo, ve, 0x07030602u)};
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
-// LDS slot (16-byte granule) of granule g of weight row r: 16 granules per 256-byte row
-__device__ __forceinline__ int gslot(int r, int g) { return g ^ (r & 15); }
+// LDS slot (16-byte granule) of granule g of staged token row r: 16 granules per row
+__device__ __forceinline__ int aslot(int r, int g) { return g ^ (r & 15); }
+
+// Raw buffer resource (stride 0): reads at byte offsets >= num_records return zero.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 raw_rsrc(const void *base, uint32_t num_records) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)num_records, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// DMA of 16 (or 4) bytes per lane from a raw buffer straight into LDS: lane l writes
+// dst + l * bytes.  Written as inline assembly so that the compiler sees no LDS store
+// and adds no wait of its own before later LDS reads (it cannot tell the staging
+// buffers apart and would drain every outstanding load, the weight prefetch included);
+// the kernel orders each DMA before its readers with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, const void *dst) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "s"(lds_addr(dst))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, const void *dst) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "s"(lds_addr(dst))
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS barrier without a global-memory fence: register loads stay in flight across it
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct W4Args {
+    const uint8_t *A8;   // [S][K] fp8 activations, expert-contiguous rows
+    const float *As;     // [S][K/128] activation scales
+    const uint8_t *Wq;   // [E][N][K/2] e2m1 codes, low nibble = even k
+    const uint8_t *Wbs;  // [E][N][K/16] e4m3 block scales
+    const float *Wgs;    // [E] global scales
+    int K, N, I, il;
+    float clamp;
+    float *Hout;         // GEMM1: h fp32 [S][I]
+    uint16_t *Yout;      // GEMM2: y bf16 [S][ldy]
+    int ldy;
+};
+
+// weights of one 256-wide K chunk for one lane: 2 blocks of 128 K, 64 codes + 4 scales each
+struct WChunk {
+    u32x4 c[4];
+    uint32_t s[2];
+};
+
+template <bool kSwiGLU, int NTB>
+__device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin, int rows, int nt,
+                                          unsigned char *act, float *xsl, const u32x2 *lut) {
+    const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = g.K, kb_n = K / 128;
+    const int nc = K / kKC;
+
+    // ---- this lane's weight row
+    int wrow;
+    if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
+        const bool up = wave >= 2;
+        const int c = nt * (kBN / 2) + (wave & 1) * 32 + (lane & 31);
+        wrow = g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
+    } else {
+        wrow = nt * kBN + wave * 32 + (lane & 31);
+    }
+    // lane half h covers K [128 q + 64 h, +64) of every 128-wide block q
+    const uint8_t *wq = g.Wq + ((int64_t)e * g.N + wrow) * (K / 2) + half * 32;
+    const uint8_t *wbs = g.Wbs + ((int64_t)e * g.N + wrow) * (K / 16) + half * 4;
+    auto load_w = [&](WChunk &w, int c) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint8_t *p = wq + c * (kKC / 2) + q * 64;
+            w.c[2 * q] = *(const u32x4 *)p;
+            w.c[2 * q + 1] = *(const u32x4 *)(p + 16);
+            w.s[q] = *(const uint32_t *)(wbs + c * (kKC / 16) + q * 8);
+        }
+    };
+    constexpr int kWLoads = 6;  // global loads per load_w
+
+    // ---- activations and their scales: DMA into LDS.  Raw buffer resources bound the
+    // reads to the tile's live rows; rows past them read as zero.
+    const i32x4 rsA = raw_rsrc(g.A8 + (int64_t)row_begin * K, (uint32_t)(rows * K));
+    const i32x4 rsS = raw_rsrc(g.As + (int64_t)row_begin * kb_n, (uint32_t)(rows * kb_n * 4));
+    // op i of this wave fills token rows 4j .. 4j+3, j = wave + 4 i (lane l: row 4j + l/16, slot l%16)
+    uint32_t voffA[NTB * 2];
+#pragma unroll
+    for (int i = 0; i < NTB * 2; ++i) {
+        const int r = 4 * (wave + 4 * i) + (lane >> 4);
+        voffA[i] = (uint32_t)(r * K + (((lane & 15) ^ (r & 15)) * 16));
+    }
+    // scales: lanes < 32 of wave w fetch rows 16 w + l/2, block l%2 of the chunk
+    const uint32_t voffS = (uint32_t)(((16 * wave + (lane >> 1)) * kb_n + (lane & 1)) * 4);
+    auto load_a = [&](int c, int buf) {
+        unsigned char *dst = act + buf * kActBuf;
+#pragma unroll
+        for (int i = 0; i < NTB * 2; ++i) dma16(rsA, voffA[i], c * kKC, dst + (wave + 4 * i) * 1024);
+        if (lane < 32) dma4(rsS, voffS, c * 8, xsl + buf * (kBM * 2) + wave * 32);
+    };
+    constexpr int kALoads = NTB * 2 + 1;  // VMEM ops per load_a
+    constexpr int kLoads = kWLoads + kALoads;
+
+    f32x16 acc[NTB];
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[tb][v] = 0.f;
+
+    auto compute = [&](const WChunk &w, int buf) {
+        const unsigned char *ab = act + buf * kActBuf;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            float xs[NTB];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) xs[tb] = xsl[buf * (kBM * 2) + (tb * 32 + (lane & 31)) * 2 + q];
+            f32x16 part[NTB];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) part[tb][v] = 0.f;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {  // two 64-wide MFMA steps per 128-wide block
+                const u32x4 cw = w.c[2 * q + t];
+                const uint32_t sc = w.s[q] >> (16 * t);
+                const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
+                const u32x2 d0 = dequant8(cw.x, t0), d1 = dequant8(cw.y, t0);
+                const u32x2 d2 = dequant8(cw.z, t1), d3 = dequant8(cw.w, t1);
+                const i32x8 wa = {(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y,
+                                  (int)d2.x, (int)d2.y, (int)d3.x, (int)d3.y};
+                const int gk = 8 * q + 4 * half + 2 * t;  // granule of this lane's 32 K bytes
+#pragma unroll
+                for (int tb = 0; tb < NTB; ++tb) {
+                    const int r = tb * 32 + (lane & 31);
+                    const u32x4 lo = *(const u32x4 *)(ab + r * kKC + aslot(r, gk) * 16);
+                    const u32x4 hi = *(const u32x4 *)(ab + r * kKC + aslot(r, gk + 1) * 16);
+                    const i32x8 xb = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    part[tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, part[tb], 0, 0, 0, 127, 0,
+                                                                               127);
+                }
+            }
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[tb][v] = fmaf(part[tb][v], xs[tb], acc[tb][v]);
+        }
+    };
+
+    // ---- main loop.  Chunk c uses weight set c % 4 and activation buffer c % 4; after its
+    // compute, chunk c + 3 is requested into the set and buffer of chunk c - 1 (all waves
+    // passed chunk c - 1's barrier).  Before chunk c + 1's barrier each wave waits for its
+    // own DMA of chunk c + 1: only the requests of chunks c + 2 and c + 3 stay in flight.
+    // Every request is issued, also past the last chunk (it then repeats the last chunk,
+    // which hits in cache), so the number of memory operations in flight is the same on
+    // every path and the compiler's own waits for the weight registers never drain the
+    // prefetch.
+    WChunk w[kNBuf];
+#pragma unroll
+    for (int c = 0; c < kNBuf - 1; ++c) {
+        load_w(w[c], min(c, nc - 1));
+        load_a(min(c, nc - 1), c);
+    }
+    wait_vmcnt<2 * kLoads>();
+    lds_barrier();  // chunk 0 staged, scale table built
+    for (int c0 = 0; c0 < nc; c0 += kNBuf) {
+#pragma unroll
+        for (int sidx = 0; sidx < kNBuf; ++sidx) {
+            const int c = c0 + sidx;
+            if (c >= nc) break;
+            compute(w[sidx], sidx);
+            const int cn = min(c + 3, nc - 1);
+            load_w(w[(sidx + 3) % kNBuf], cn);
+            load_a(cn, (sidx + 3) % kNBuf);
+            wait_vmcnt<2 * kLoads>();
+            lds_barrier();
+        }
+    }
+    wait_vmcnt<0>();  // the trailing repeat requests still write LDS buffers
+    lds_barrier();
+
+    // ---- epilogue (every wave has passed the last chunk's barrier: the buffers are free)
+    const float gs = g.Wgs[e];
+    if (kSwiGLU) {
+        // the up waves hand their accumulators to the gate waves through LDS
+        float *xch = (float *)act;  // [2 waves][NTB][16][64]
+        if (wave >= 2)
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) xch[(((wave - 2) * NTB + tb) * 16 + v) * 64 + lane] = acc[tb][v];
+        lds_barrier();
+        if (wave < 2) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                const int tok = tb * 32 + (lane & 31);
+                if (tok >= rows) continue;
+                float *hrow = g.Hout + (int64_t)(row_begin + tok) * g.I;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c0 = nt * (kBN / 2) + wave * 32 + g4 * 8 + half * 4;
+                    f32x4 o;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int v = g4 * 4 + q;
+                        float gv = gs * acc[tb][v];
+                        float uv = gs * xch[((wave * NTB + tb) * 16 + v) * 64 + lane];
+                        if (g.clamp > 0.f) {
+                            gv = fminf(fmaxf(gv, -g.clamp), g.clamp);
+                            uv = fminf(fmaxf(uv, -g.clamp), g.clamp);
+                        }
+                        o[q] = gv / (1.0f + expf(-gv)) * uv;
+                    }
+                    *(f32x4 *)(hrow + c0) = o;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const int tok = tb * 32 + (lane & 31);
+            if (tok >= rows) continue;
+            uint16_t *yrow = g.Yout + (int64_t)(row_begin + tok) * g.ldy;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int c0 = nt * kBN + wave * 32 + g4 * 8 + half * 4;
+                u32x2 o;
+                o.x = pack_bf16x2(gs * acc[tb][g4 * 4 + 0], gs * acc[tb][g4 * 4 + 1]);
+                o.y = pack_bf16x2(gs * acc[tb][g4 * 4 + 2], gs * acc[tb][g4 * 4 + 3]);
+                *(u32x2 *)(yrow + c0) = o;
+            }
+        }
+    }
+}
 
 }  // namespace
 
 template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_w4a8_kernel(
-    const uint8_t *__restrict__ A8,      // [S][K] fp8 activations, expert-contiguous rows
-    const float *__restrict__ As,        // [S][K/128] activation scales
-    const uint8_t *__restrict__ Wq,      // [E][N][K/2] e2m1 codes, low nibble = even k
-    const uint8_t *__restrict__ Wbs,     // [E][N][K/16] e4m3 block scales
-    const float *__restrict__ Wgs,       // [E] global scales
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles, const int32_t *__restrict__ n_tiles,
-    int K, int N, int I, int il, float clamp,
-    float *__restrict__ Hout,            // kSwiGLU: h fp32 [S][I]
-    uint16_t *__restrict__ Yout, int ldy) {  // else: y bf16 [S][ldy]
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
+                                                                     const int32_t *__restrict__ tiles,
+                                                                     const int32_t *__restrict__ n_tiles) {
+    __shared__ __attribute__((aligned(1024))) unsigned char act[kNBuf * kActBuf];
+    __shared__ u32x2 lut[256];
+    __shared__ float xsl[kNBuf * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
 
-    const int nb_n = N / kBN;
+    const int nb_n = g.N / kBN;
     const int mt = blockIdx.x / nb_n;
     const int nt = blockIdx.x % nb_n;
     if (mt >= n_tiles[0]) return;
@@ -119,139 +357,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_w4a8_kernel(
     const int row_begin = offsets[e] + tiles[2 * mt + 1];
     const int rows = min(kBM, offsets[e + 1] - row_begin);
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int kb_n = K / 128;  // scale blocks per row
-
-    // ---- weights: thread t dequantises 128 codes of tile row t/2 (half t%2 of the stage)
-    const int wr_local = tid >> 1, whalf = tid & 1;
-    int wrow;
-    if (kSwiGLU) {  // tile rows [gate 32 | up 32 | gate 32 | up 32] for h columns nt*64 ..
-        const int a = wr_local >> 5;
-        const int c = nt * (kBN / 2) + (a >> 1) * 32 + (wr_local & 31);
-        const bool up = a & 1;
-        wrow = il == 0 ? (up ? I + c : c) : (c / il) * 2 * il + (up ? il : 0) + c % il;
-    } else {
-        wrow = nt * kBN + wr_local;
-    }
-    const uint8_t *wq = Wq + ((int64_t)e * N + wrow) * (K / 2) + whalf * 64;
-    const uint8_t *wbs = Wbs + ((int64_t)e * N + wrow) * (K / 16) + whalf * 8;
-
-    auto dequant_stage = [&](int kc, int buf) {
-        const u32x4 *src = (const u32x4 *)(wq + kc * (kKC / 2));
-        const u32x2 sc2 = *(const u32x2 *)(wbs + kc * (kKC / 16));
-        const uint32_t sc[2] = {sc2.x, sc2.y};
-        unsigned char *dst = lds + buf * kStage + wr_local * kKC;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {      // 16 bytes = 32 codes = 2 scale blocks
-            const u32x4 c = src[q];
-            const uint32_t s4 = sc[q >> 1] >> ((q & 1) * 16);
-            const u32x2 d0 = dequant8(c.x, s4), d1 = dequant8(c.y, s4);
-            const u32x2 d2 = dequant8(c.z, s4 >> 8), d3 = dequant8(c.w, s4 >> 8);
-            u32x4 g0, g1;  // 32 fp8 bytes = granules 4q .. 4q+1 of this half
-            g0.x = d0.x; g0.y = d0.y; g0.z = d1.x; g0.w = d1.y;
-            g1.x = d2.x; g1.y = d2.y; g1.z = d3.x; g1.w = d3.y;
-            const int g = whalf * 8 + q * 2;
-            *(u32x4 *)(dst + gslot(wr_local, g) * 16) = g0;
-            *(u32x4 *)(dst + gslot(wr_local, g + 1) * 16) = g1;
-        }
-    };
-
-    // ---- activations of this wave's token block, read straight from global memory
-    const int tok = wave * 32 + (lane & 31);  // token row within the tile (lane's MFMA column)
-    const bool tok_live = tok < rows;
-    const uint8_t *arow = A8 + (int64_t)(row_begin + (tok_live ? tok : 0)) * K + (lane >> 5) * 32;
-    const float *srow = As + (int64_t)(row_begin + (tok_live ? tok : 0)) * kb_n;
-
-    f32x16 acc[4], part[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[a][v] = 0.f;
-
-    const int nk = K / kKC;
-    const bool wave_live = wave * 32 < rows;
-    dequant_stage(0, 0);
-    __syncthreads();
-    for (int kc = 0; kc < nk; ++kc) {
-        const int buf = kc & 1;
-        if (kc + 1 < nk) dequant_stage(kc + 1, buf ^ 1);
-        if (wave_live) {
-            const unsigned char *sw = lds + buf * kStage;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {  // two 128-wide scale blocks per stage
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) part[a][v] = 0.f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {  // two 64-wide MFMA K steps per scale block
-                    const int ks = sb * 2 + h;
-                    i32x8 xb;
-                    {
-                        const u32x4 *p = (const u32x4 *)(arow + kc * kKC + ks * 64);
-                        u32x4 lo = tok_live ? p[0] : u32x4{0, 0, 0, 0};
-                        u32x4 hi = tok_live ? p[1] : u32x4{0, 0, 0, 0};
-                        xb = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    }
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const int r = a * 32 + (lane & 31);
-                        const int g = ks * 4 + (lane >> 5) * 2;
-                        const u32x4 lo = *(const u32x4 *)(sw + r * kKC + gslot(r, g) * 16);
-                        const u32x4 hi = *(const u32x4 *)(sw + r * kKC + gslot(r, g + 1) * 16);
-                        const i32x8 wa = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                        part[a] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, part[a], 0, 0, 0, 127, 0,
-                                                                                  127);
-                    }
-                }
-                const float xs = tok_live ? srow[kc * 2 + sb] : 0.f;
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[a][v] = fmaf(part[a][v], xs, acc[a][v]);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (!tok_live) return;
-    const float gs = Wgs[e];
-    const int half = lane >> 5;
-    const int64_t row = row_begin + tok;
-    if (kSwiGLU) {
-        float *hrow = Hout + row * I;
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c0 = nt * (kBN / 2) + pr * 32 + g4 * 8 + half * 4;
-                f32x4 o;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float g = gs * acc[2 * pr][g4 * 4 + q], u = gs * acc[2 * pr + 1][g4 * 4 + q];
-                    if (clamp > 0.f) {
-                        g = fminf(fmaxf(g, -clamp), clamp);
-                        u = fminf(fmaxf(u, -clamp), clamp);
-                    }
-                    o[q] = g / (1.0f + expf(-g)) * u;
-                }
-                *(f32x4 *)(hrow + c0) = o;
-            }
-    } else {
-        uint16_t *yrow = Yout + row * ldy;
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c0 = nt * kBN + a * 32 + g4 * 8 + half * 4;
-                u32x2 o;
-                o.x = pack_bf16x2(gs * acc[a][g4 * 4 + 0], gs * acc[a][g4 * 4 + 1]);
-                o.y = pack_bf16x2(gs * acc[a][g4 * 4 + 2], gs * acc[a][g4 * 4 + 3]);
-                *(u32x2 *)(yrow + c0) = o;
-            }
-    }
+    lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x);  // read after the first barrier of the tile
+    if (rows > 32)
+        w4a8_tile<kSwiGLU, 2>(g, e, row_begin, rows, nt, act, xsl, lut);
+    else
+        w4a8_tile<kSwiGLU, 1>(g, e, row_begin, rows, nt, act, xsl, lut);
 }
 
 // h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows: one wave per
@@ -276,16 +386,19 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(const float *__restric
     if (lane == 0) hs[row * nb + b] = s;
 }
 
-// the dequant of every (e2m1 code c, e4m3 scale s) pair through the GEMMs' device routine,
-// with the code in the even-k (low) nibble [0] and in the odd-k (high) nibble [1]
+// the dequant of every (e2m1 code, e4m3 scale s) pair through the GEMMs' device routine:
+// a dword holding code (c + p) mod 16 at nibble position p = 0..7 (low nibble first) is
+// dequantised with scale s, and byte p of the result goes to out8[p][c][s]
 __global__ void w4a8_dequant_table_kernel(uint8_t *out8) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;  // 16 * 256 entries
     if (i >= 16 * 256) return;
     const uint32_t c = (uint32_t)(i >> 8), s = (uint32_t)(i & 255);
-    const u32x2 lo = dequant8(c, s);       // code in nibble 0 (k even)
-    const u32x2 hi = dequant8(c << 4, s);  // code in nibble 1 (k odd)
-    out8[i] = (uint8_t)(lo.x & 0xff);
-    out8[16 * 256 + i] = (uint8_t)((hi.x >> 8) & 0xff);
+    uint32_t x = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) x |= ((c + p) & 15u) << (4 * p);
+    const u32x2 d = dequant8(x, scaled_e2m1_table(s));
+#pragma unroll
+    for (int p = 0; p < 8; ++p) out8[p * 16 * 256 + i] = (uint8_t)(((p < 4 ? d.x : d.y) >> (8 * (p & 3))) & 0xffu);
 }
 
 hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s) {
@@ -298,18 +411,20 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
                                    const moe_weights &w, const moe_problem &p, float *h32, uint8_t *h8, float *hs,
                                    uint16_t *y_perm, hipStream_t s) {
     const int H = p.H, I = p.I;
-    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<true>, dim3(max_tiles * (2 * I / kBN)), dim3(kThreads), 0, s, x_perm,
-                       x_perm_scale, (const uint8_t *)w.w1, (const uint8_t *)w.w1_bscale, w.w1_gscale, offsets, tiles,
-                       n_tiles, H, 2 * I, I, p.glu_interleave, p.swiglu_clamp, h32, (uint16_t *)nullptr, 0);
+    W4Args g1{x_perm, x_perm_scale, (const uint8_t *)w.w1, (const uint8_t *)w.w1_bscale, w.w1_gscale,
+              H, 2 * I, I, p.glu_interleave, p.swiglu_clamp, h32, nullptr, 0};
+    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<true>, dim3(max_tiles * (2 * I / kBN)), dim3(kThreads), 0, s, g1,
+                       offsets, tiles, n_tiles);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t items = n_slots(p) * (I / 128);
     hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<false>, dim3(max_tiles * (H / kBN)), dim3(kThreads), 0, s, h8, hs,
-                       (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale, w.w2_gscale, offsets, tiles, n_tiles, I,
-                       H, I, 0, 0.0f, (float *)nullptr, y_perm, H);
+    W4Args g2{h8, hs, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale, w.w2_gscale,
+              I, H, I, 0, 0.0f, nullptr, y_perm, H};
+    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<false>, dim3(max_tiles * (H / kBN)), dim3(kThreads), 0, s, g2,
+                       offsets, tiles, n_tiles);
     return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ struct WsLayout {
 constexpr int kChunk = 1024;
 // M tile (rows of one expert per workgroup) of the bf16 and of the W4A8 grouped GEMMs
 constexpr int kGemmBM = 256;
-constexpr int kGemmBMW4A8 = 128;
+constexpr int kGemmBMW4A8 = 64;
 
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
