@@ -21,10 +21,11 @@
 // into registers in the MFMA operand layout (lane l: row l % 32, one contiguous
 // 32-code run per 64-wide K step) and dequantises them there.  K advances 256 per
 // chunk; weights are loaded three chunks ahead (four register sets).  Activations are
-// shared by the four waves: each chunk of the tile's token rows, and its activation
-// scales, go straight from global memory into LDS by buffer-load DMA (four buffers,
-// swizzled), and each wave waits only for its own DMA before the chunk's barrier, so
-// the weight prefetch stays in flight across barriers.
+// shared by the four waves: each chunk of the tile's token rows and its activation
+// scales are loaded into registers two chunks ahead and written to LDS one chunk
+// ahead (two buffers, swizzled).  Every load is an ordinary register load, so the
+// compiler's own waits are exact: no wait drains the weight prefetch, and the chunk
+// barriers carry no memory fence.
 // K is visited so that both halves of a 64-wide MFMA step lie in one 128-wide
 // activation-scale block; the partial sum of each block is added to the accumulator
 // times that block's activation scale (fp32), as the definition states.
@@ -56,9 +57,9 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBM = kGemmBMW4A8;  // token rows per m-tile (2 blocks of 32)
 constexpr int kBN = 128;          // weight rows per workgroup (4 waves x 32)
 constexpr int kKC = 256;          // K per chunk
-constexpr int kNBuf = 4;          // chunks in flight: activation buffers and weight register sets
+constexpr int kNBuf = 4;          // weight register sets (weights three chunks ahead)
 constexpr int kThreads = 256;
-constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB)
+constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB, two buffers)
 static_assert(kBM == 64, "the tile holds at most two 32-token blocks");
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
@@ -99,38 +100,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // LDS slot (16-byte granule) of granule g of staged token row r: 16 granules per row
 __device__ __forceinline__ int aslot(int r, int g) { return g ^ (r & 15); }
-
-// Raw buffer resource (stride 0): reads at byte offsets >= num_records return zero.
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ i32x4 raw_rsrc(const void *base, uint32_t num_records) {
-    const uint64_t a = (uint64_t)base;
-    return i32x4{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xffffu), (int)num_records, 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
-// DMA of 16 (or 4) bytes per lane from a raw buffer straight into LDS: lane l writes
-// dst + l * bytes.  Written as inline assembly so that the compiler sees no LDS store
-// and adds no wait of its own before later LDS reads (it cannot tell the staging
-// buffers apart and would drain every outstanding load, the weight prefetch included);
-// the kernel orders each DMA before its readers with explicit vmcnt waits and barriers.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, const void *dst) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "s"(lds_addr(dst))
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t voff, uint32_t soff, const void *dst) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff),
-                 "s"(lds_addr(dst))
-                 : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // LDS barrier without a global-memory fence: register loads stay in flight across it
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -183,29 +152,36 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
             w.s[q] = *(const uint32_t *)(wbs + c * (kKC / 16) + q * 8);
         }
     };
-    constexpr int kWLoads = 6;  // global loads per load_w
 
-    // ---- activations and their scales: DMA into LDS.  Raw buffer resources bound the
-    // reads to the tile's live rows; rows past them read as zero.
-    const i32x4 rsA = raw_rsrc(g.A8 + (int64_t)row_begin * K, (uint32_t)(rows * K));
-    const i32x4 rsS = raw_rsrc(g.As + (int64_t)row_begin * kb_n, (uint32_t)(rows * kb_n * 4));
-    // op i of this wave fills token rows 4j .. 4j+3, j = wave + 4 i (lane l: row 4j + l/16, slot l%16)
-    uint32_t voffA[NTB * 2];
+    // ---- activations: thread t stages granule t % 16 of token rows t / 16 + 16 i, and thread
+    // r < 32 NTB the chunk's two activation scales of token row r.  Raw buffer resources
+    // bound the reads to the tile's live rows (rows past them read as zero), so every lane
+    // issues the same unconditional loads and the compiler's wait counts stay exact.
+    const int sg = tid & 15, sr = tid >> 4;
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.A8 + (int64_t)row_begin * K), (short)0, rows * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.As + (int64_t)row_begin * kb_n), (short)0, rows * kb_n * 4, 0x00020000);
+    uint32_t aoff[NTB * 2];
 #pragma unroll
-    for (int i = 0; i < NTB * 2; ++i) {
-        const int r = 4 * (wave + 4 * i) + (lane >> 4);
-        voffA[i] = (uint32_t)(r * K + (((lane & 15) ^ (r & 15)) * 16));
-    }
-    // scales: lanes < 32 of wave w fetch rows 16 w + l/2, block l%2 of the chunk
-    const uint32_t voffS = (uint32_t)(((16 * wave + (lane >> 1)) * kb_n + (lane & 1)) * 4);
-    auto load_a = [&](int c, int buf) {
+    for (int i = 0; i < NTB * 2; ++i) aoff[i] = (uint32_t)((sr + 16 * i) * K + sg * 16);
+    const uint32_t soff = (uint32_t)(min(tid, kBM - 1) * kb_n * 4);
+    u32x4 ar[NTB * 2];
+    u32x2 ars;
+    auto load_a = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < NTB * 2; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], c * kKC, 0);
+        ars = __builtin_amdgcn_raw_buffer_load_b64(rsS, soff, c * 8, 0);
+    };
+    auto store_a = [&](int buf) {
         unsigned char *dst = act + buf * kActBuf;
 #pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) dma16(rsA, voffA[i], c * kKC, dst + (wave + 4 * i) * 1024);
-        if (lane < 32) dma4(rsS, voffS, c * 8, xsl + buf * (kBM * 2) + wave * 32);
+        for (int i = 0; i < NTB * 2; ++i) {
+            const int r = sr + 16 * i;
+            *(u32x4 *)(dst + r * kKC + aslot(r, sg) * 16) = ar[i];
+        }
+        if (tid < NTB * 32) *(u32x2 *)(xsl + buf * (kBM * 2) + tid * 2) = ars;
     };
-    constexpr int kALoads = NTB * 2 + 1;  // VMEM ops per load_a
-    constexpr int kLoads = kWLoads + kALoads;
 
     f32x16 acc[NTB];
 #pragma unroll
@@ -215,11 +191,12 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
 
     auto compute = [&](const WChunk &w, int buf) {
         const unsigned char *ab = act + buf * kActBuf;
+        const float *xr = xsl + buf * (kBM * 2);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             float xs[NTB];
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) xs[tb] = xsl[buf * (kBM * 2) + (tb * 32 + (lane & 31)) * 2 + q];
+            for (int tb = 0; tb < NTB; ++tb) xs[tb] = xr[(tb * 32 + (lane & 31)) * 2 + q];
             f32x16 part[NTB];
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
@@ -253,37 +230,32 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
         }
     };
 
-    // ---- main loop.  Chunk c uses weight set c % 4 and activation buffer c % 4; after its
-    // compute, chunk c + 3 is requested into the set and buffer of chunk c - 1 (all waves
-    // passed chunk c - 1's barrier).  Before chunk c + 1's barrier each wave waits for its
-    // own DMA of chunk c + 1: only the requests of chunks c + 2 and c + 3 stay in flight.
-    // Every request is issued, also past the last chunk (it then repeats the last chunk,
-    // which hits in cache), so the number of memory operations in flight is the same on
-    // every path and the compiler's own waits for the weight registers never drain the
-    // prefetch.
+    // ---- main loop.  Chunk c computes from weight set c % 4 and activation buffer c % 2,
+    // then writes the staged activations of chunk c + 1 into the other buffer (last read
+    // by chunk c - 1, before the previous barrier), loads the activations of chunk c + 2
+    // and the weights of chunk c + 3 (into the set of chunk c - 1).  Requests past the
+    // last chunk repeat it (cache hits), so every path issues the same loads.
     WChunk w[kNBuf];
+    load_a(0);
 #pragma unroll
-    for (int c = 0; c < kNBuf - 1; ++c) {
-        load_w(w[c], min(c, nc - 1));
-        load_a(min(c, nc - 1), c);
-    }
-    wait_vmcnt<2 * kLoads>();
+    for (int c = 0; c < kNBuf - 1; ++c) load_w(w[c], min(c, nc - 1));
+    store_a(0);
+    load_a(min(1, nc - 1));
     lds_barrier();  // chunk 0 staged, scale table built
+    // Whole groups of four steps: a step past the last chunk skips only its compute (which
+    // issues no memory loads), so every path through the loop issues the same loads and
+    // the compiler's waits at the loop head see the regular pattern.
     for (int c0 = 0; c0 < nc; c0 += kNBuf) {
 #pragma unroll
         for (int sidx = 0; sidx < kNBuf; ++sidx) {
             const int c = c0 + sidx;
-            if (c >= nc) break;
-            compute(w[sidx], sidx);
-            const int cn = min(c + 3, nc - 1);
-            load_w(w[(sidx + 3) % kNBuf], cn);
-            load_a(cn, (sidx + 3) % kNBuf);
-            wait_vmcnt<2 * kLoads>();
+            if (c < nc) compute(w[sidx], sidx & 1);
+            store_a((sidx + 1) & 1);
+            load_a(min(c + 2, nc - 1));
+            load_w(w[(sidx + 3) % kNBuf], min(c + 3, nc - 1));
             lds_barrier();
         }
     }
-    wait_vmcnt<0>();  // the trailing repeat requests still write LDS buffers
-    lds_barrier();
 
     // ---- epilogue (every wave has passed the last chunk's barrier: the buffers are free)
     const float gs = g.Wgs[e];
@@ -345,9 +317,9 @@ template <bool kSwiGLU>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
-    __shared__ __attribute__((aligned(1024))) unsigned char act[kNBuf * kActBuf];
+    __shared__ __attribute__((aligned(1024))) unsigned char act[2 * kActBuf];
     __shared__ u32x2 lut[256];
-    __shared__ float xsl[kNBuf * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
+    __shared__ float xsl[2 * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
 
     const int nb_n = g.N / kBN;
     const int mt = blockIdx.x / nb_n;
