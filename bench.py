@@ -106,6 +106,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="skewed")
+    ap.add_argument("--tokens", type=int, default=None, help="token count override (e.g. the W4A8 sweep points)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -132,6 +133,8 @@ def main():
     from moe_synth import CONFIGS, generate
 
     cfg = CONFIGS[args.workload]
+    if args.tokens is not None:
+        cfg = cfg.with_tokens(args.tokens)
     t0 = time.perf_counter()
     inp = generate(cfg, seed=args.seed)
     log(f"generated {cfg.name} (seed {args.seed}) in {time.perf_counter() - t0:.1f} s")
@@ -197,14 +200,35 @@ def main():
     tflops = lambda f, ms: f / (ms * s) / 1e12  # noqa: E731
     gbs = lambda b, ms: b / (ms * s) / 1e9  # noqa: E731
 
-    g1 = tflops(gemm1_flops, stage_ms["gemm1_swiglu"])
-    roofline = {
-        "kernel": "grouped_gemm_bf16_kernel<true> (GEMM1 + SwiGLU)",
-        "bound": "mfma", "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-        "frac": round(g1 / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu"),
-        "algorithmic_per_launch": f"4*R*H*I = {gemm1_flops:.4g} flop (R={R} rows)",
-    }
+    if not w4:
+        g1 = tflops(gemm1_flops, stage_ms["gemm1_swiglu"])
+        roofline = {
+            "kernel": "grouped_gemm_bf16_kernel<true> (GEMM1 + SwiGLU)",
+            "bound": "mfma", "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(g1 / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu"),
+            "algorithmic_per_launch": f"4*R*H*I = {gemm1_flops:.4g} flop (R={R} rows)",
+        }
+    else:
+        # the W4A8 expert FFN streams the packed weights of every expert that has a row:
+        # W1 codes 2I*H/2 + scales 2I*H/16, W2 codes H*I/2 + scales H*I/16 bytes per expert,
+        # plus activations in (R*H fp8 + scales), h round trip and y out; the weights dominate
+        ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
+        if inp.get("slot_drop") is not None:
+            ids = np.where(inp["slot_drop"] == 1, -1, ids)
+        n_exp = len(np.unique(ids[ids >= 0]))
+        w_bytes = n_exp * (2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16)
+        act_bytes = R * H + R * (H // 128) * 4 + R * I * (4 + 4 + 1) + R * (I // 128) * 4 + R * H * 2
+        ffn_bytes = w_bytes + act_bytes
+        a = gbs(ffn_bytes, stage_ms["gemm1_swiglu"])
+        roofline = {
+            "kernel": "grouped W4A8 FFN (grouped_gemm_w4a8_kernel<true>, requant_fp8_kernel, "
+                      "grouped_gemm_w4a8_kernel<false>)",
+            "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_per_launch": f"{ffn_bytes} bytes ({n_exp} experts' packed weights {w_bytes} B "
+                                      f"+ activations {act_bytes} B)",
+        }
     result = {
         "metric": METRIC,
         "value": round(T / (step_ms * s), 1),
@@ -224,9 +248,10 @@ def main():
                                + (f", {cfg.drop_p:.0%} slots dropped" if cfg.drop_p else ""),
                    "T": T, "H": H, "I": I, "E": cfg.E, "k": k, "rows": R, "seed": args.seed},
         "tflops_forward": round(tflops(gemm1_flops + gemm2_flops, step_ms), 2),
+        # W4A8 runs both GEMMs (and the h re-quantisation) inside the gemm1_swiglu stage
         "tflops_gemms": round(tflops(gemm1_flops + gemm2_flops, gemm_ms), 2),
-        "mfma_frac_gemms": round(tflops(gemm1_flops + gemm2_flops, gemm_ms) / PEAK_BF16_TFLOPS, 4),
-        "gemm2_tflops": round(tflops(gemm2_flops, stage_ms["gemm2"]), 2),
+        "mfma_frac_gemms": None if w4 else round(tflops(gemm1_flops + gemm2_flops, gemm_ms) / PEAK_BF16_TFLOPS, 4),
+        "gemm2_tflops": None if w4 else round(tflops(gemm2_flops, stage_ms["gemm2"]), 2),
         "gather_gbs": round(gbs(gather_bytes, stage_ms["gather"]), 1),
         "gather_hbm_frac": round(gbs(gather_bytes, stage_ms["gather"]) / PEAK_HBM_GBS, 4),
         "combine_gbs": round(gbs(combine_bytes, stage_ms["combine"]), 1),
