@@ -235,12 +235,16 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     // by chunk c - 1, before the previous barrier), loads the activations of chunk c + 2
     // and the weights of chunk c + 3 (into the set of chunk c - 1).  Requests past the
     // last chunk repeat it (cache hits), so every path issues the same loads.
+    // The prologue ends like a loop step (activations of the next chunk, then one weight
+    // set), so the loads in flight at the loop head follow the same pattern on entry as on
+    // the back edge and the compiler's waits there stay exact.
     WChunk w[kNBuf];
     load_a(0);
-#pragma unroll
-    for (int c = 0; c < kNBuf - 1; ++c) load_w(w[c], min(c, nc - 1));
+    load_w(w[0], 0);
+    load_w(w[1], min(1, nc - 1));
     store_a(0);
     load_a(min(1, nc - 1));
+    load_w(w[2], min(2, nc - 1));
     lds_barrier();  // chunk 0 staged, scale table built
     // Whole groups of four steps: a step past the last chunk skips only its compute (which
     // issues no memory loads), so every path through the loop issues the same loads and
