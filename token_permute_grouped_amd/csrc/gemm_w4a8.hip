@@ -117,40 +117,59 @@ struct W4Args {
     int ldy;
 };
 
-// weights of one 256-wide K chunk for one lane: 2 blocks of 128 K, 64 codes + 4 scales each
+// weights of one 256-wide K chunk as one lane loads them (line-coalesced): 16 code bytes of
+// each of rows l/8 + 8i (i < 4) at byte 16 (l % 8), and 8 scale bytes of row l/2 at byte
+// 8 (l % 2), rows counted within the wave's 32
 struct WChunk {
     u32x4 c[4];
-    uint32_t s[2];
+    u32x2 s;
 };
+
+// per-wave LDS staging of one chunk's weights in rows: 32 code rows of 128 bytes padded to
+// 144 (so that 16 consecutive rows read at one column hit 16 distinct bank groups), then
+// 32 scale rows of 16 bytes
+constexpr int kWRow = 144;
+constexpr int kWScales = 32 * kWRow;
+constexpr int kWSlot = kWScales + 32 * 16;  // 5120 bytes per chunk and wave
 
 template <bool kSwiGLU, int NTB>
 __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin, int rows, int nt,
-                                          unsigned char *act, float *xsl, const u32x2 *lut) {
+                                          unsigned char *act, float *xsl, unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, kb_n = K / 128;
     const int nc = K / kKC;
 
-    // ---- this lane's weight row
-    int wrow;
-    if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
-        const bool up = wave >= 2;
-        const int c = nt * (kBN / 2) + (wave & 1) * 32 + (lane & 31);
-        wrow = g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
-    } else {
-        wrow = nt * kBN + wave * 32 + (lane & 31);
-    }
-    // lane half h covers K [128 q + 64 h, +64) of every 128-wide block q
-    const uint8_t *wq = g.Wq + ((int64_t)e * g.N + wrow) * (K / 2) + half * 32;
-    const uint8_t *wbs = g.Wbs + ((int64_t)e * g.N + wrow) * (K / 16) + half * 4;
+    // ---- weights.  Each wave streams its own 32 rows, in chunks of 256 K (128 code bytes
+    // + 16 scale bytes per row): loads cover whole 128-byte lines (8 lanes per row), and the
+    // wave transposes each chunk through its own LDS slot into the MFMA operand layout.
+    auto weight_row = [&](int rl) {  // weight matrix row of row rl of this wave
+        if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
+            const bool up = wave >= 2;
+            const int c = nt * (kBN / 2) + (wave & 1) * 32 + rl;
+            return g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
+        }
+        return nt * kBN + wave * 32 + rl;
+    };
+    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.Wq + (int64_t)e * g.N * (K / 2)), (short)0, g.N * (K / 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsWs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.Wbs + (int64_t)e * g.N * (K / 16)), (short)0, g.N * (K / 16), 0x00020000);
+    uint32_t woff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)(weight_row((lane >> 3) + 8 * i) * (K / 2) + (lane & 7) * 16);
+    const uint32_t wsoff = (uint32_t)(weight_row(lane >> 1) * (K / 16) + (lane & 1) * 8);
     auto load_w = [&](WChunk &w, int c) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint8_t *p = wq + c * (kKC / 2) + q * 64;
-            w.c[2 * q] = *(const u32x4 *)p;
-            w.c[2 * q + 1] = *(const u32x4 *)(p + 16);
-            w.s[q] = *(const uint32_t *)(wbs + c * (kKC / 16) + q * 8);
-        }
+        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rsW, woff[i], c * (kKC / 2), 0);
+        w.s = __builtin_amdgcn_raw_buffer_load_b64(rsWs, wsoff, c * (kKC / 16), 0);
+    };
+    unsigned char *const wl = wlds + wave * (2 * kWSlot);  // this wave's two staging slots
+    auto store_w = [&](const WChunk &w, int slot) {
+        unsigned char *d = wl + slot * kWSlot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(d + ((lane >> 3) + 8 * i) * kWRow + (lane & 7) * 16) = w.c[i];
+        *(u32x2 *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 8) = w.s;
     };
 
     // ---- activations: thread t stages granule t % 16 of token rows t / 16 + 16 i, and thread
@@ -189,9 +208,13 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[tb][v] = 0.f;
 
-    auto compute = [&](const WChunk &w, int buf) {
+    // lane (row r = l % 32, half h = l / 32) of 64-K step (q, t) takes code bytes
+    // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
+    auto compute = [&](int buf) {
         const unsigned char *ab = act + buf * kActBuf;
         const float *xr = xsl + buf * (kBM * 2);
+        const unsigned char *wr = wl + buf * kWSlot + (lane & 31) * kWRow + half * 32;
+        const unsigned char *wsr = wl + buf * kWSlot + kWScales + (lane & 31) * 16 + half * 4;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             float xs[NTB];
@@ -202,10 +225,11 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) part[tb][v] = 0.f;
+            const uint32_t sq = *(const uint32_t *)(wsr + 8 * q);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {  // two 64-wide MFMA steps per 128-wide block
-                const u32x4 cw = w.c[2 * q + t];
-                const uint32_t sc = w.s[q] >> (16 * t);
+                const u32x4 cw = *(const u32x4 *)(wr + 64 * q + 16 * t);
+                const uint32_t sc = sq >> (16 * t);
                 const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
                 const u32x2 d0 = dequant8(cw.x, t0), d1 = dequant8(cw.y, t0);
                 const u32x2 d2 = dequant8(cw.z, t1), d3 = dequant8(cw.w, t1);
@@ -245,7 +269,14 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     store_a(0);
     load_a(min(1, nc - 1));
     load_w(w[2], min(2, nc - 1));
+    store_w(w[0], 0);
     lds_barrier();  // chunk 0 staged, scale table built
+    // Chunk c computes from activation buffer c % 2 and this wave's weight slot c % 2, then
+    // stages the weights of chunk c + 1 (set (c + 1) % 4, loaded two steps ago) into the other
+    // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
+    // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
+    // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
+    // c + 3 (into the set of chunk c - 1).  Requests past the last chunk repeat it.
     // Whole groups of four steps: a step past the last chunk skips only its compute (which
     // issues no memory loads), so every path through the loop issues the same loads and
     // the compiler's waits at the loop head see the regular pattern.
@@ -253,7 +284,8 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
 #pragma unroll
         for (int sidx = 0; sidx < kNBuf; ++sidx) {
             const int c = c0 + sidx;
-            if (c < nc) compute(w[sidx], sidx & 1);
+            if (c < nc) compute(sidx & 1);
+            store_w(w[(sidx + 1) % kNBuf], (sidx + 1) & 1);
             store_a((sidx + 1) & 1);
             load_a(min(c + 2, nc - 1));
             load_w(w[(sidx + 3) % kNBuf], min(c + 3, nc - 1));
@@ -324,6 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
     __shared__ __attribute__((aligned(1024))) unsigned char act[2 * kActBuf];
     __shared__ u32x2 lut[256];
     __shared__ float xsl[2 * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
+    __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot];  // weight staging, 2 slots per wave
 
     const int nb_n = g.N / kBN;
     const int mt = blockIdx.x / nb_n;
@@ -335,9 +368,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
 
     lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x);  // read after the first barrier of the tile
     if (rows > 32)
-        w4a8_tile<kSwiGLU, 2>(g, e, row_begin, rows, nt, act, xsl, lut);
+        w4a8_tile<kSwiGLU, 2>(g, e, row_begin, rows, nt, act, xsl, wlds, lut);
     else
-        w4a8_tile<kSwiGLU, 1>(g, e, row_begin, rows, nt, act, xsl, lut);
+        w4a8_tile<kSwiGLU, 1>(g, e, row_begin, rows, nt, act, xsl, wlds, lut);
 }
 
 // h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows: one wave per
