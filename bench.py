@@ -6,10 +6,10 @@ experts, top-8, bf16, router logits N(0,1) plus a per-expert bias ln(rank^-1.2)
 (seed 0).  A step is one moe_forward call: route, permutation tables, row gather,
 GEMM1 + SwiGLU, GEMM2, combine, with every input already resident in HBM.
 
-Timing: W untimed warm-up steps, then K steps bracketed by device
-synchronisation; each timed step is the moe_forward_timed entry point (same
-kernels, plus a HIP event at every stage boundary on the library's stream), so the
-per-stage durations below are measured live over the timed region.
+Timing: W untimed warm-up steps, then K moe_forward steps bracketed by device
+synchronisation and HIP events on the library's stream (ms_per_step, value).  The
+per-stage durations come from K further steps through moe_forward_timed (same
+kernels plus a HIP event at every stage boundary), measured live in the same run.
 
 Prints one JSON line.  The CPU baseline is the fp64 oracle (test infrastructure)
 timed on a bounded sample of the same workload on the host cores.
@@ -51,6 +51,9 @@ class HipEvents:
         e = ctypes.c_void_p()
         assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
         return e.value
+
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) == 0
 
     def ms(self, a, b):
         f = ctypes.c_float()
@@ -171,22 +174,36 @@ def main():
     torch.cuda.synchronize()
     log(f"warm-up done ({args.warmup} steps)")
 
+    # timed region: K plain moe_forward calls, HIP events on the library's stream around them
     hip = HipEvents()
-    evs = [[hip.create() for _ in range(tpg.MOE_N_STAGE_EVENTS)] for _ in range(args.steps)]
+    e0, e1 = hip.create(), hip.create()
+    stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     w0 = time.perf_counter()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
+    step_ms = hip.ms(e0, e1) / args.steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    log(f"timed {args.steps} steps: {step_ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (wall)")
+
+    # stage breakdown: K more steps through moe_forward_timed (same kernels plus a HIP event at
+    # every stage boundary; each event adds a few microseconds, visible only at small T)
+    evs = [[hip.create() for _ in range(tpg.MOE_N_STAGE_EVENTS)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - w0) * 1e3 / args.steps
     stage_ms = {}
-    for s, name in enumerate(tpg.STAGES):
-        stage_ms[name] = float(np.mean([hip.ms(evs[i][s], evs[i][s + 1]) for i in range(args.steps)]))
-    step_ms = float(np.mean([hip.ms(evs[i][0], evs[i][-1]) for i in range(args.steps)]))
+    for s_, name in enumerate(tpg.STAGES):
+        stage_ms[name] = float(np.mean([hip.ms(evs[i][s_], evs[i][s_ + 1]) for i in range(args.steps)]))
     for row in evs:
         for e in row:
             hip.destroy(e)
-    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), {wall_ms:.3f} ms/step (wall)")
 
     T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
     R = T * k - (int(inp["slot_drop"].sum()) if inp.get("slot_drop") is not None else 0)

@@ -195,6 +195,25 @@ def test_forward_matches_oracle(name):
     assert err <= BF16_BAR
 
 
+@pytest.mark.parametrize("cfg", [
+    MoeConfig("front_tiny", T=64, H=128, I=256, E=8, k=2),
+    MoeConfig("front_drop", T=30, H=256, I=256, E=16, k=4, glu_interleave=32, drop_p=0.1),
+    MoeConfig("front_e256", T=32, H=128, I=128, E=256, k=32),             # exactly 1024 slots
+    MoeConfig("front_one", T=1, H=256, I=384, E=4, k=4),
+], ids=lambda c: c.name)
+def test_forward_small_front_end_matches_separate_steps(cfg):
+    """up to 1024 slots and 32 tokens the forward routes, builds the tables and the tile
+    list in one launch; it must give exactly what the separate entry points give"""
+    inp = generate(cfg, seed=2)
+    d = DeviceProblem(inp)
+    fused = bf16_host(d.forward())
+    idx, w = d.route()
+    offsets, row_src, slot_row, x_perm, x_perm_scale = d.permute(idx)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    steps = bf16_host(d.combine(y, slot_row, w))
+    assert (fused == steps).all()
+
+
 @pytest.mark.parametrize("name", ["tiny", "skewed"])
 def test_forward_is_deterministic(name):
     _, d = workload(name)

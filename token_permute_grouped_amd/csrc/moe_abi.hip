@@ -56,7 +56,7 @@ WsLayout ws_layout(const moe_problem &p) {
     L.tiles = o;
     o = align256(o + (size_t)max_m_tiles(p) * 2 * 4);
     L.n_tiles = o;
-    o = align256(o + 16);
+    o = align256(o + kTileMetaInts * 4);
     L.h = o;
     o = align256(o + S * (size_t)p.I * act);
     L.h_scale = o;
@@ -145,17 +145,28 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         return ev ? hip_status(hipEventRecord((hipEvent_t)ev[i], s)) : MOE_OK;
     };
     const bool w4 = is_w4a8(p);
+    // up to kChunk slots and 32 tokens (one workgroup routes 16 tokens at a time, so beyond
+    // that the separate multi-workgroup router is faster): routing, tables and tile list in
+    // one launch (stage marks 1, 2 and the tile-list stage then take no time of their own)
+    const bool small = n_slots(*p) <= kChunk && p->T <= 32;
     if ((st = mark(0))) return st;
-    if ((st = hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, s)))) return st;
+    if (small) {
+        if ((st = hip_status(launch_frontend_small(logits, slot_drop, p->T, p->E, p->k, gemm_bm(*p), topk_idx,
+                                                   topk_w, offsets, row_src, slot_row, tiles, n_tiles, s))))
+            return st;
+    } else if ((st = hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, s)))) {
+        return st;
+    }
     if ((st = mark(1))) return st;
-    if ((st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row, s))))
+    if (!small &&
+        (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row, s))))
         return st;
     if ((st = mark(2))) return st;
     if ((st = hip_status(launch_permute(x, w4 ? x_scale : nullptr, slot_row, p->T, p->k, p->H, w4 ? 1 : 2, x_perm,
                                         x_perm_scale, s))))
         return st;
     if ((st = mark(3))) return st;
-    if ((st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), tiles, n_tiles, s)))) return st;
+    if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), tiles, n_tiles, s)))) return st;
     if ((st = mark(4))) return st;
     if (w4) {
         if ((st = hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,

@@ -19,7 +19,7 @@ constexpr int kWave = 64;
 struct WsLayout {
     size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
     size_t tiles;         // int32 [2 * max_tiles]  grouped GEMMs: (expert, first row) per m-tile
-    size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count
+    size_t n_tiles;       // int32 [kTileMetaInts]  grouped GEMMs: tile count, then the GEMMs' XCD round counters
     size_t h;             // bf16 [S][I]  or (W4A8) fp8 [S][I]
     size_t h_scale;       // W4A8: fp32 [S][I/128]
     size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation)
@@ -40,6 +40,12 @@ constexpr int kChunk = 1024;
 constexpr int kGemmBM = 256;
 constexpr int kGemmBMW4A8 = 64;
 
+// tile metadata: [0] tile count; from kSyncBase, two counter sets (GEMM1, GEMM2) of 8 XCDs,
+// one 64-byte line per counter, zeroed by the tile-list kernel before the GEMMs run
+constexpr int kSyncBase = 64;
+constexpr int kSyncSet = 8 * 16;
+constexpr int kTileMetaInts = kSyncBase + 2 * kSyncSet;
+
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
 inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_W4A8 ? kGemmBMW4A8 : kGemmBM; }
@@ -59,6 +65,11 @@ hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *sl
                           int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);
 
 hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
+
+// routing + tables + tile list in one workgroup, for at most kChunk slots
+hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
+                                 int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *row_src,
+                                 int32_t *slot_row, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
 
 hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,

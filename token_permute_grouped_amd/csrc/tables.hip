@@ -12,7 +12,11 @@
 //                  then 64 slots at a time, a slot's rank among equal ids of lower lanes
 //                  comes from 9 ballots (one per bit of id+1) and a popcount.
 // The GEMM tile list (expert, m-tile) is built from offsets by build_tiles.
-#include "moe_internal.h"
+//
+// For up to kChunk slots the forward runs all of this (and the routing) in one workgroup
+// instead: frontend_small, with the expert ids kept in LDS between the steps.  At small
+// token counts the five launches it replaces cost more than their work.
+#include "route_token.h"
 
 namespace tpg {
 
@@ -136,29 +140,156 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ i
 }
 
 // tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert (tiles of bm rows);
-// n_tiles[0] = count.
-// One thread per expert; tiles are listed expert by expert.
+// n_tiles[0] = count.  Full tiles come first (expert by expert), then each expert's partial
+// last tile, so tiles that run side by side tend to have the same amount of work.  Also
+// zeroes the grouped GEMMs' round counters (n_tiles[kSyncBase ..]).
+// One thread per expert.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E, int bm,
                                                           int32_t *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles) {
-    __shared__ int nt[256];
+    __shared__ int nf[256], np[256];
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int mine = (cnt + bm - 1) / bm;
-    nt[e] = mine;
+    const int full = cnt / bm, part = (cnt % bm) ? 1 : 0;
+    nf[e] = full;
+    np[e] = part;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {  // inclusive scans of both counts
+        const int af = e >= d ? nf[e - d] : 0, ap = e >= d ? np[e - d] : 0;
+        __syncthreads();
+        nf[e] += af;
+        np[e] += ap;
+        __syncthreads();
+    }
+    const int total_full = nf[255];
+    const int f0 = nf[e] - full;
+    for (int m = 0; m < full; ++m) {
+        tiles[2 * (f0 + m)] = e;
+        tiles[2 * (f0 + m) + 1] = m * bm;
+    }
+    if (part) {
+        const int pos = total_full + np[e] - 1;
+        tiles[2 * pos] = e;
+        tiles[2 * pos + 1] = full * bm;
+    }
+    if (e == 255) n_tiles[0] = total_full + np[255];
+    for (int i = threadIdx.x; i < 2 * kSyncSet; i += 256) n_tiles[kSyncBase + i] = 0;
+}
+
+// Routing, tables and tile list of at most kChunk slots in one workgroup of 16 waves: the same
+// results as route_topk + chunk_hist + scan + rank + build_tiles.  Slot s is thread s.
+constexpr int kFrontWaves = kChunk / kWave;  // 16
+__global__ __launch_bounds__(kChunk) void frontend_small_kernel(
+    const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop, int T, int E, int k, int bm,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ row_src, int32_t *__restrict__ slot_row, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ n_tiles) {
+    __shared__ int32_t sid[kChunk];          // expert id (or -1) of every slot
+    __shared__ int cnt[kFrontWaves][256];    // per-wave counts, then per-wave bases
+    __shared__ int off[257];
+    __shared__ int sa[256], sb[256];         // scan buffers
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int S = T * k;
+
+    // routing: one wave per token
+    for (int t = w; t < T; t += kFrontWaves) route_token(logits, slot_drop, t, E, k, lane, topk_idx, topk_w, sid + t * k);
+    for (int i = tid; i < kFrontWaves * 256; i += kChunk) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+
+    // per-wave histograms
+    const int x = tid < S ? valid_id(sid[tid], E) : -1;
+    if (x >= 0) atomicAdd(&cnt[w][x], 1);
+    __syncthreads();
+
+    // per expert: exclusive bases over the waves and the total; exclusive scan over experts
+    int tot = 0;
+    if (tid < 256) {
+        for (int ww = 0; ww < kFrontWaves; ++ww) {
+            const int v = cnt[ww][tid];
+            cnt[ww][tid] = tot;
+            tot += v;
+        }
+        sa[tid] = tot;
+    }
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
-        const int add = e >= d ? nt[e - d] : 0;
+        const int add = (tid < 256 && tid >= d) ? sa[tid - d] : 0;
         __syncthreads();
-        nt[e] += add;
+        if (tid < 256) sa[tid] += add;
         __syncthreads();
     }
-    const int start = nt[e] - mine;
-    for (int m = 0; m < mine; ++m) {
-        tiles[2 * (start + m)] = e;
-        tiles[2 * (start + m) + 1] = m * bm;
+    if (tid < E) {
+        off[tid] = sa[tid] - tot;
+        offsets[tid] = sa[tid] - tot;
     }
-    if (e == 255) n_tiles[0] = nt[255];
+    if (tid == E - 1) {
+        off[E] = sa[tid];
+        offsets[E] = sa[tid];
+    }
+    __syncthreads();
+
+    // rank of the slot among equal ids of lower lanes: 9 ballots (one per bit of id+1)
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const unsigned key = (unsigned)(x + 1);
+    uint64_t peers = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt);
+    const int R = off[E];
+    if (tid < S) {
+        const int r = x >= 0 ? off[x] + cnt[w][x] + rank : -1;
+        slot_row[tid] = r;
+        if (r >= 0) row_src[r] = tid;
+        if (tid >= R) row_src[tid] = -1;  // rows past the live count (r < R never lands here)
+    }
+
+    // GEMM tile list (as build_tiles_kernel): full tiles first, then partial ones
+    int full = 0, part = 0;
+    if (tid < 256) {
+        const int c = tid < E ? off[tid + 1] - off[tid] : 0;
+        full = c / bm;
+        part = (c % bm) ? 1 : 0;
+        sa[tid] = full;
+        sb[tid] = part;
+    }
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+        const int af = (tid < 256 && tid >= d) ? sa[tid - d] : 0;
+        const int ap = (tid < 256 && tid >= d) ? sb[tid - d] : 0;
+        __syncthreads();
+        if (tid < 256) {
+            sa[tid] += af;
+            sb[tid] += ap;
+        }
+        __syncthreads();
+    }
+    if (tid < 256) {
+        const int total_full = sa[255];
+        const int f0 = sa[tid] - full;
+        for (int m = 0; m < full; ++m) {
+            tiles[2 * (f0 + m)] = tid;
+            tiles[2 * (f0 + m) + 1] = m * bm;
+        }
+        if (part) {
+            const int pos = total_full + sb[tid] - 1;
+            tiles[2 * pos] = tid;
+            tiles[2 * pos + 1] = full * bm;
+        }
+        if (tid == 255) n_tiles[0] = total_full + sb[255];
+    }
+    for (int i = tid; i < 2 * kSyncSet; i += kChunk) n_tiles[kSyncBase + i] = 0;
+}
+
+hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
+                                 int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *row_src,
+                                 int32_t *slot_row, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(frontend_small_kernel, dim3(1), dim3(kChunk), 0, s, logits, slot_drop, T, E, k, bm, topk_idx,
+                       topk_w, offsets, row_src, slot_row, tiles, n_tiles);
+    return hipGetLastError();
 }
 
 hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *chunk_counts, int32_t *offsets,
