@@ -57,7 +57,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBM = kGemmBMW4A8;  // token rows per m-tile (2 blocks of 32)
 constexpr int kBN = 128;          // weight rows per workgroup (4 waves x 32)
 constexpr int kKC = 256;          // K per chunk
-constexpr int kNBuf = 4;          // weight register sets (weights three chunks ahead)
+constexpr int kNBuf = 4;          // weight register sets (weights kNBuf - 1 chunks ahead)
 constexpr int kThreads = 256;
 constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB, two buffers)
 static_assert(kBM == 64, "the tile holds at most two 32-token blocks");
@@ -264,11 +264,11 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     // the back edge and the compiler's waits there stay exact.
     WChunk w[kNBuf];
     load_a(0);
-    load_w(w[0], 0);
-    load_w(w[1], min(1, nc - 1));
+#pragma unroll
+    for (int c = 0; c < kNBuf - 2; ++c) load_w(w[c], min(c, nc - 1));
     store_a(0);
     load_a(min(1, nc - 1));
-    load_w(w[2], min(2, nc - 1));
+    load_w(w[kNBuf - 2], min(kNBuf - 2, nc - 1));
     store_w(w[0], 0);
     lds_barrier();  // chunk 0 staged, scale table built
     // Chunk c computes from activation buffer c % 2 and this wave's weight slot c % 2, then
@@ -276,7 +276,7 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
     // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
     // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
-    // c + 3 (into the set of chunk c - 1).  Requests past the last chunk repeat it.
+    // c + kNBuf - 1 (into the set of chunk c - 1).  Requests past the last chunk repeat it.
     // Whole groups of four steps: a step past the last chunk skips only its compute (which
     // issues no memory loads), so every path through the loop issues the same loads and
     // the compiler's waits at the loop head see the regular pattern.
@@ -284,11 +284,11 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
 #pragma unroll
         for (int sidx = 0; sidx < kNBuf; ++sidx) {
             const int c = c0 + sidx;
-            if (c < nc) compute(sidx & 1);
-            store_w(w[(sidx + 1) % kNBuf], (sidx + 1) & 1);
-            store_a((sidx + 1) & 1);
+            if (c < nc) compute(c & 1);
+            store_w(w[(sidx + 1) % kNBuf], (c + 1) & 1);
+            store_a((c + 1) & 1);
             load_a(min(c + 2, nc - 1));
-            load_w(w[(sidx + 3) % kNBuf], min(c + 3, nc - 1));
+            load_w(w[(sidx + kNBuf - 1) % kNBuf], min(c + kNBuf - 1, nc - 1));
             lds_barrier();
         }
     }

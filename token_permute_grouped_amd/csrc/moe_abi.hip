@@ -56,7 +56,7 @@ WsLayout ws_layout(const moe_problem &p) {
     L.tiles = o;
     o = align256(o + (size_t)max_m_tiles(p) * 2 * 4);
     L.n_tiles = o;
-    o = align256(o + kTileMetaInts * 4);
+    o = align256(o + 16);
     L.h = o;
     o = align256(o + S * (size_t)p.I * act);
     L.h_scale = o;

@@ -19,7 +19,7 @@ constexpr int kWave = 64;
 struct WsLayout {
     size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
     size_t tiles;         // int32 [2 * max_tiles]  grouped GEMMs: (expert, first row) per m-tile
-    size_t n_tiles;       // int32 [kTileMetaInts]  grouped GEMMs: tile count, then the GEMMs' XCD round counters
+    size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count
     size_t h;             // bf16 [S][I]  or (W4A8) fp8 [S][I]
     size_t h_scale;       // W4A8: fp32 [S][I/128]
     size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation)
@@ -39,12 +39,6 @@ constexpr int kChunk = 1024;
 // M tile (rows of one expert per workgroup) of the bf16 and of the W4A8 grouped GEMMs
 constexpr int kGemmBM = 256;
 constexpr int kGemmBMW4A8 = 64;
-
-// tile metadata: [0] tile count; from kSyncBase, two counter sets (GEMM1, GEMM2) of 8 XCDs,
-// one 64-byte line per counter, zeroed by the tile-list kernel before the GEMMs run
-constexpr int kSyncBase = 64;
-constexpr int kSyncSet = 8 * 16;
-constexpr int kTileMetaInts = kSyncBase + 2 * kSyncSet;
 
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }

@@ -141,8 +141,7 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ i
 
 // tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert (tiles of bm rows);
 // n_tiles[0] = count.  Full tiles come first (expert by expert), then each expert's partial
-// last tile, so tiles that run side by side tend to have the same amount of work.  Also
-// zeroes the grouped GEMMs' round counters (n_tiles[kSyncBase ..]).
+// last tile, so tiles that run side by side tend to have the same amount of work.
 // One thread per expert.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E, int bm,
                                                           int32_t *__restrict__ tiles,
@@ -173,7 +172,6 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
         tiles[2 * pos + 1] = full * bm;
     }
     if (e == 255) n_tiles[0] = total_full + np[255];
-    for (int i = threadIdx.x; i < 2 * kSyncSet; i += 256) n_tiles[kSyncBase + i] = 0;
 }
 
 // Routing, tables and tile list of at most kChunk slots in one workgroup of 16 waves: the same
@@ -281,7 +279,6 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
         }
         if (tid == 255) n_tiles[0] = total_full + sb[255];
     }
-    for (int i = tid; i < 2 * kSyncSet; i += kChunk) n_tiles[kSyncBase + i] = 0;
 }
 
 hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
