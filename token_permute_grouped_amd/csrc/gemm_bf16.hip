@@ -7,15 +7,18 @@
 // Rows r of expert e are [offsets[e], offsets[e+1]): one ragged group per expert,
 // with no padding of the groups (Megatron-LM's "skip routed expert padding").
 //
-// Tiling.  One workgroup of 4 waves (one per SIMD) owns a 256 x 256 output tile:
-// kBM token rows of one expert x kBN weight rows; each wave computes 128 x 128 as
-// 4 x 4 blocks of 32 x 32 (16 independent MFMAs per 16-wide K step, accumulators
-// in AGPRs).  Both operands are K-contiguous in HBM; K advances kBK = 64 per stage.
+// Tiling.  One workgroup of 8 waves (two per SIMD) owns a 256 x 256 output tile:
+// kBM token rows of one expert x kBN weight rows; each wave computes 128 token rows
+// x 64 weight rows as 4 x 2 blocks of 32 x 32 (8 independent MFMAs per 16-wide K
+// step).  Two waves per SIMD let one issue MFMAs while the other waits on LDS or
+// global memory; with one wave per SIMD (128 x 128 each) the same loop ran ~10%
+// slower.  Both operands are K-contiguous in HBM; K advances kBK = 64 per stage.
 //
 // Pipeline.  LDS holds two stages (128 KB).  Global loads go to registers first:
 // while the MFMAs of stage k run, the wave writes stage k+1 from its register set
 // into the free LDS buffer and refills the set with the loads of stage k+2, so a
-// load has about one stage of MFMAs to land.  Per stage there is one
+// load has about one stage of MFMAs to land.  The LDS writes of a stage are split
+// over two K steps (a burst of them stalls the MFMA issue).  Per stage there is one
 // barrier, taken before the last 16-wide K step so that the next stage's first
 // fragments load under that step's MFMAs and the MFMA issue does not drain.
 // Fragment reads of step s+1 are interleaved with the MFMAs of step s.
@@ -30,8 +33,9 @@
 // row (8-byte bf16 stores).
 //
 // SwiGLU fusion.  For GEMM1 an n-tile holds the weight rows of 128 output columns
-// c0..c0+127 ordered [gate 32 | up 32] x 4, so gate and up of a column are in the
-// same lane of two blocks and silu(g) * u is formed in registers.  With the
+// c0..c0+127 ordered [gate 32 | up 32] x 4 (one pair per wave column), so gate and
+// up of a column are in the same lane of two blocks and silu(g) * u is formed in
+// registers.  With the
 // interleave-32 layout these 256 rows are one contiguous slice of W1; with
 // [gate | up] they are two 128-row slices I rows apart.
 //
@@ -65,15 +69,18 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBM = kGemmBM;  // token rows per tile (256)
 constexpr int kBN = 256;      // weight rows per tile
 constexpr int kBK = 64;       // K per stage
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;     // two per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveN = 4;     // waves along the weight rows; each wave owns 128 token x 64 weight rows
 constexpr int kGroupM = 2;    // m-tiles swept together along N
 constexpr int kRowBytes = kBK * 2;                    // 128: one row of one stage
 constexpr int kAStage = kBM * kRowBytes;               // 32 KB: activation rows of one stage
 constexpr int kBStage = kBN * kRowBytes;               // 32 KB: weight rows of one stage
 constexpr int kBStages = 3;                            // weight ring depth (DMA two stages ahead)
 constexpr int kBBase = 2 * kAStage;                    // weights follow the two activation stages
-constexpr int kLoads = kBM * kRowBytes / 16 / kThreads;  // 16-byte activation loads per thread (8)
-constexpr int kOpsB = kBStage / 1024 / 4;              // 1 KB weight DMAs per wave per stage (8)
+constexpr int kLoads = kBM * kRowBytes / 16 / kThreads;  // 16-byte activation loads per thread (4)
+constexpr int kOpsB = kBStage / 1024 / kWaves;         // 1 KB weight DMAs per wave per stage (4)
+constexpr int kLRows = kThreads / 8;                   // tile rows one activation load covers (64)
 
 __device__ __forceinline__ int slot(int r, int kc) { return kc ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWaveN, wn = wave % kWaveN;
 
     // ---- activations: global -> registers -> LDS.  Thread loads chunk (tid & 7) of tile rows
     //      (tid >> 3) + 32 i.  Weights: DMA straight into LDS, wave w filling rows w*64 .. w*64+63,
@@ -173,16 +180,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         (void *)(W + (int64_t)e * N * K), (short)0, N * K * 2, 0x00020000);
     uint32_t offA[kLoads], offB[kOpsB];
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) offA[i] = (uint32_t)((lrow + 32 * i) * K + lkc * 8) * 2u;
+    for (int i = 0; i < kLoads; ++i) offA[i] = (uint32_t)((lrow + kLRows * i) * K + lkc * 8) * 2u;
 #pragma unroll
     for (int i = 0; i < kOpsB; ++i) {
-        const int r = wave * 64 + i * 8 + (lane >> 3);  // tile weight row
+        const int r = wave * (kBN / kWaves) + i * 8 + (lane >> 3);  // tile weight row
         int wr;
         if (kSwiGLU) {
-            // tile row r: wave column r >> 7, gate/up block (r >> 5) & 3 -> [g | u | g | u]
-            const int a = (r >> 5) & 3;
-            const int c = nt * (kBN / 2) + (r >> 7) * 64 + (a >> 1) * 32 + (r & 31);
-            const bool up = a & 1;
+            // tile row r: wave column r >> 6, gate/up block (r >> 5) & 1 -> [g | u]
+            const int c = nt * (kBN / 2) + (r >> 6) * 32 + (r & 31);
+            const bool up = (r >> 5) & 1;
             wr = il == 0 ? (up ? I + c : c) : (c / il) * 2 * il + (up ? il : 0) + c % il;
         } else {
             wr = nt * kBN + r;  // rows >= N read as zero
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         const int kc = slot(r, lane & 7);  // the logical chunk LDS slot (lane & 7) holds
         offB[i] = (uint32_t)(wr * K + kc * 8) * 2u;
     }
-    // LDS byte offset of this thread's activation writes (same slot for rows lrow + 32 i)
+    // LDS byte offset of this thread's activation writes (same slot for rows lrow + 64 i)
     const int wofs = lrow * kRowBytes + slot(lrow, lkc) * 16;
 
     u32x4 RA0[kLoads], RA1[kLoads];
@@ -198,20 +204,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) R[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[i], kt * kRowBytes, 0);
     };
-    auto lwriteA = [&](const u32x4 *R, int astage) {
+    auto lwriteA = [&](const u32x4 *R, int astage, int i0, int n) {
         unsigned char *base = lds + astage * kAStage + wofs;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) *(u32x4 *)(base + i * 32 * kRowBytes) = R[i];
+        for (int i = i0; i < i0 + n; ++i) *(u32x4 *)(base + i * kLRows * kRowBytes) = R[i];
     };
     auto dmaB = [&](int kt, int bstage) {
-        unsigned char *dst = lds + kBBase + bstage * kBStage + wave * 64 * kRowBytes;
+        unsigned char *dst = lds + kBBase + bstage * kBStage + wave * (kBN / kWaves) * kRowBytes;
 #pragma unroll
         for (int i = 0; i < kOpsB; ++i) dma16(rsB, offB[i], kt * kRowBytes, dst + i * 1024);
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -224,17 +230,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 
     auto mainloop = [&](auto nb_tag) {
         constexpr int NB = decltype(nb_tag)::value;
-        constexpr int NR = 4 + NB;  // fragment reads per K step
-        constexpr int NM = 4 * NB;  // MFMAs per K step
-        bf16x8 fw[2][4], fx[2][NB > 0 ? NB : 1];
+        constexpr int NR = 2 + NB;  // fragment reads per K step
+        constexpr int NM = 2 * NB;  // MFMAs per K step
+        bf16x8 fw[2][2], fx[2][NB > 0 ? NB : 1];
         auto load = [&](int buf, int astage, int bstage, int ks) {
             if constexpr (NB > 0) {
                 const u32x4 *sa = (const u32x4 *)(lds + astage * kAStage);
                 const u32x4 *sb = (const u32x4 *)(lds + kBBase + bstage * kBStage);
                 const int kc = ks * 2 + fk;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const int r = wn * 128 + a * 32 + fr;
+                for (int a = 0; a < 2; ++a) {
+                    const int r = wn * 64 + a * 32 + fr;
                     fw[buf][a] = __builtin_bit_cast(bf16x8, sb[r * 8 + slot(r, kc)]);
                 }
 #pragma unroll
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
+                for (int a = 0; a < 2; ++a)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][a], fx[buf][b], acc[a][b], 0, 0, 0);
         };
 
@@ -269,16 +275,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
                 dmaB(kt + 2, bs2);
                 __builtin_amdgcn_sched_group_barrier(0x020, kOpsB, 0);
             }
-            // K step 0: fragments of step 1 under the MFMAs of step 0
+            // K steps 0 and 1: fragments of the next step under the MFMAs, and the activations
+            // of stage kt+1 into the free LDS buffer, half under each step
+            if constexpr (kNext) lwriteA(Rn, P ^ 1, 0, kLoads / 2);
             load(1, P, bs, 1);
             mfmas(0);
-            if constexpr (NB > 0) interleave_ds_mfma<NR, NM>();
-            // K step 1: activations of stage kt+1 into the free LDS buffer
-            if constexpr (kNext) lwriteA(Rn, P ^ 1);
+            if constexpr (NB > 0) {
+                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
+                else interleave_ds_mfma<NR, NM>();
+            }
+            if constexpr (kNext) lwriteA(Rn, P ^ 1, kLoads / 2, kLoads / 2);
             load(0, P, bs, 2);
             mfmas(1);
             if constexpr (NB > 0) {
-                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads, NR, NM>();
+                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
                 else interleave_ds_mfma<NR, NM>();
             }
             // K step 2: refill the register set with the activations of stage kt+3
@@ -313,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         dmaB(1, 1);
         gloadA(RA0, 0);
         gloadA(RA1, 1);
-        lwriteA(RA0, 0);
+        lwriteA(RA0, 0, 0, kLoads);
         if (nk > 2) gloadA(RA0, 2);
         wait_vmcnt<0>();
         lds_barrier();
@@ -349,25 +359,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         uint16_t *crow = C + (int64_t)(row_begin + tr) * ldc;
         if (kSwiGLU) {
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr)
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int c0 = nt * (kBN / 2) + wn * 32 + g4 * 8 + half * 4;
+                float hv[4];
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = nt * (kBN / 2) + wn * 64 + pr * 32 + g4 * 8 + half * 4;
-                    float hv[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        hv[q] = silu_mul(acc[2 * pr][b][g4 * 4 + q], acc[2 * pr + 1][b][g4 * 4 + q], clamp);
-                    u32x2 o;
-                    o.x = pack2(hv[0], hv[1]);
-                    o.y = pack2(hv[2], hv[3]);
-                    *(u32x2 *)(crow + c0) = o;
-                }
+                for (int q = 0; q < 4; ++q) hv[q] = silu_mul(acc[0][b][g4 * 4 + q], acc[1][b][g4 * 4 + q], clamp);
+                u32x2 o;
+                o.x = pack2(hv[0], hv[1]);
+                o.y = pack2(hv[2], hv[3]);
+                *(u32x2 *)(crow + c0) = o;
+            }
         } else {
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = nt * kBN + wn * 128 + a * 32 + g4 * 8 + half * 4;
+                    const int c0 = nt * kBN + wn * 64 + a * 32 + g4 * 8 + half * 4;
                     if (c0 >= N) continue;
                     u32x2 o;
                     o.x = pack2(acc[a][b][g4 * 4 + 0], acc[a][b][g4 * 4 + 1]);
