@@ -45,13 +45,8 @@
 // is instantiated per live-block count, so it stays branch-free) and only live
 // rows are stored.
 //
-// Scheduling.  The device-side tile list gives the m-tiles (expert, first row).
-// Workgroups take tiles in launch order, swept in groups of kGroupM m-tiles along N,
-// so the ~256 tiles resident at once (one per CU, round-robin over the 8 XCDs)
-// cover a compact block of one expert: its weight rows and activation rows stay in
-// the 256 MB last-level (MALL) cache while all XCDs work on them.  (Measured on the
-// skewed workload: giving each XCD its own contiguous range of tiles instead is
-// 10% slower; its eight scattered working sets do not fit the MALL together.)
+// Scheduling.  The device-side tile list gives the m-tiles (expert, first row);
+// tile_map assigns them to workgroups by band and XCD rectangle (below).
 // Workgroups past the tile count exit before any barrier.
 #include <type_traits>
 
@@ -72,7 +67,6 @@ constexpr int kBK = 64;       // K per stage
 constexpr int kWaves = 8;     // two per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveN = 4;     // waves along the weight rows; each wave owns 128 token x 64 weight rows
-constexpr int kGroupM = 2;    // m-tiles swept together along N
 constexpr int kRowBytes = kBK * 2;                    // 128: one row of one stage
 constexpr int kAStage = kBM * kRowBytes;               // 32 KB: activation rows of one stage
 constexpr int kBStage = kBN * kRowBytes;               // 32 KB: weight rows of one stage
@@ -81,6 +75,21 @@ constexpr int kBBase = 2 * kAStage;                    // weights follow the two
 constexpr int kLoads = kBM * kRowBytes / 16 / kThreads;  // 16-byte activation loads per thread (4)
 constexpr int kOpsB = kBStage / 1024 / kWaves;         // 1 KB weight DMAs per wave per stage (4)
 constexpr int kLRows = kThreads / 8;                   // tile rows one activation load covers (64)
+
+// Workgroup -> tile map.  Workgroup b runs on XCD b % 8.  Bands of tm.gm m-tiles take
+// tm.per_band workgroups each; a band is cut into 8 rectangles (xm rows of m-tiles x xn
+// columns of n-tiles, about 32 tiles each: one per CU of an XCD), and XCD x takes
+// rectangle x.  The 32 tiles an XCD runs at once then share ~8 activation slabs and ~4
+// weight slabs in its L2, and all XCDs stay on one band (a few experts) in the MALL.
+struct TileMap {
+    int xn, nc, gm, per_band;  // rectangle columns, n-tiles per column, band m-tiles, workgroups per band
+};
+__host__ __device__ inline TileMap tile_map(int nb_n) {
+    const int xn = nb_n >= 4 ? 4 : nb_n >= 2 ? 2 : 1;
+    const int nc = (nb_n + xn - 1) / xn;
+    const int rm = 32 / nc > 1 ? 32 / nc : 1;  // m-tiles per rectangle
+    return {xn, nc, (8 / xn) * rm, 8 * rm * nc};
+}
 
 __device__ __forceinline__ int slot(int r, int kc) { return kc ^ ((r & 7) ^ ((r >> 3) & 1)); }
 
@@ -147,18 +156,27 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     uint16_t *__restrict__ C, int ldc) {   // [S][ldc]
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kBBase + kBStages * kBStage];  // 160 KB
 
-    // ---- tile of this workgroup (launch order, groups of kGroupM m-tiles swept along N)
+    // ---- tile of this workgroup: band of m-tiles, XCD rectangle within the band, tile within it
     const int nb_n = (N + kBN - 1) / kBN;
-    const int total = n_tiles[0] * nb_n;
-    const int t = blockIdx.x;
-    if (t >= total) return;
+    const TileMap tm = tile_map(nb_n);
     const int n_mt = n_tiles[0];
-    const int group = t / (kGroupM * nb_n);
-    const int first_m = group * kGroupM;
-    const int gsize = min(kGroupM, n_mt - first_m);
-    const int in_group = t - group * kGroupM * nb_n;
-    const int mt = first_m + in_group % gsize;
-    const int nt = in_group / gsize;
+    const int band = blockIdx.x / tm.per_band, p = blockIdx.x % tm.per_band;
+    const int first_m = band * tm.gm;
+    const int gm = min(tm.gm, n_mt - first_m);  // m-tiles in this band
+    const int xm = 8 / tm.xn;
+    const int ma = (gm + xm - 1) / xm;          // m-tiles per rectangle row
+    const int x = p & 7, q = p >> 3;            // XCD (blockIdx % 8) and position on it
+    const int mi = q / tm.nc, ni = q % tm.nc;
+    const int v = first_m + (x / tm.xn) * ma + mi;  // position in the interleaved m-tile order
+    const int nt = (x % tm.xn) * tm.nc + ni;
+    if (gm <= 0 || mi >= ma || v >= first_m + gm || nt >= nb_n) return;
+    // The list holds the full m-tiles, then one partial m-tile per expert.  A partial tile
+    // does little MFMA work for the weights it streams, so partial tiles are spread evenly
+    // through the order (position v is partial when floor(v P / n) steps) and their weight
+    // streaming overlaps the full tiles' MFMAs instead of forming a memory-bound tail.
+    const int n_part = n_mt - n_tiles[1];
+    const int cp = (int)((int64_t)v * n_part / n_mt), cp1 = (int)((int64_t)(v + 1) * n_part / n_mt);
+    const int mt = cp1 > cp ? n_tiles[1] + cp : v - cp;
 
     const int e = tiles[2 * mt];
     const int row_begin = offsets[e] + tiles[2 * mt + 1];
@@ -391,7 +409,8 @@ hipError_t launch(const uint16_t *A, const uint16_t *W, const int32_t *offsets, 
                   const int32_t *n_tiles, int64_t max_tiles, int K, int N, int I, int il, float clamp, uint16_t *C,
                   int ldc, hipStream_t s) {
     const int nb_n = (N + kBN - 1) / kBN;
-    const int64_t blocks = max_tiles * nb_n;
+    const TileMap tm = tile_map(nb_n);
+    const int64_t blocks = (max_tiles + tm.gm - 1) / tm.gm * tm.per_band;
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kSwiGLU>, dim3(blocks), dim3(kThreads), 0, s, A, W, offsets, tiles,
                        n_tiles, K, N, I, il, clamp, C, ldc);
     return hipGetLastError();

@@ -19,7 +19,7 @@ constexpr int kWave = 64;
 struct WsLayout {
     size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
     size_t tiles;         // int32 [2 * max_tiles]  grouped GEMMs: (expert, first row) per m-tile
-    size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count
+    size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count, full-tile count
     size_t h;             // bf16 [S][I]  or (W4A8) fp8 [S][I]
     size_t h_scale;       // W4A8: fp32 [S][I/128]
     size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation)

@@ -171,7 +171,10 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
         tiles[2 * pos] = e;
         tiles[2 * pos + 1] = full * bm;
     }
-    if (e == 255) n_tiles[0] = total_full + np[255];
+    if (e == 255) {
+        n_tiles[0] = total_full + np[255];
+        n_tiles[1] = total_full;
+    }
 }
 
 // Routing, tables and tile list of at most kChunk slots in one workgroup of 16 waves: the same
@@ -277,7 +280,10 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
             tiles[2 * pos] = tid;
             tiles[2 * pos + 1] = full * bm;
         }
-        if (tid == 255) n_tiles[0] = total_full + sb[255];
+        if (tid == 255) {
+            n_tiles[0] = total_full + sb[255];
+            n_tiles[1] = total_full;
+        }
     }
 }
 
