@@ -368,37 +368,51 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     }
 
     // ---- epilogue: lane holds token row (lane & 31) of block b and weight rows
-    //      m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) of block a
+    //      m = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3) of block a.  The bf16 tile goes through
+    //      LDS (16-byte chunk c of row r at chunk c ^ (r & 15)), so that every global store
+    //      writes whole rows of the tile: direct 8-byte stores from the MFMA layout touch 32
+    //      rows per instruction and took ~15% of a GEMM2 tile.
+    constexpr int kCols = kSwiGLU ? kBN / 2 : kBN;  // output columns of the tile
+    constexpr int kChunks = kCols / 8;              // 16-byte chunks per row: 16 or 32
+    auto cofs = [](int r, int c) { return r * (kCols * 2) + ((c ^ (r & 15)) << 4); };
     const int half = lane >> 5;
+    lds_barrier();  // every wave is done with the last stage's operands
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int tr = wm * 128 + b * 32 + (lane & 31);
-        if (tr >= rows) continue;
-        uint16_t *crow = C + (int64_t)(row_begin + tr) * ldc;
         if (kSwiGLU) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-                const int c0 = nt * (kBN / 2) + wn * 32 + g4 * 8 + half * 4;
                 float hv[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) hv[q] = silu_mul(acc[0][b][g4 * 4 + q], acc[1][b][g4 * 4 + q], clamp);
                 u32x2 o;
                 o.x = pack2(hv[0], hv[1]);
                 o.y = pack2(hv[2], hv[3]);
-                *(u32x2 *)(crow + c0) = o;
+                *(u32x2 *)(lds + cofs(tr, wn * 4 + g4) + half * 8) = o;  // columns wn*32 + g4*8 + half*4 ..
             }
         } else {
 #pragma unroll
             for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = nt * kBN + wn * 64 + a * 32 + g4 * 8 + half * 4;
-                    if (c0 >= N) continue;
                     u32x2 o;
                     o.x = pack2(acc[a][b][g4 * 4 + 0], acc[a][b][g4 * 4 + 1]);
                     o.y = pack2(acc[a][b][g4 * 4 + 2], acc[a][b][g4 * 4 + 3]);
-                    *(u32x2 *)(crow + c0) = o;
+                    *(u32x2 *)(lds + cofs(tr, wn * 8 + a * 4 + g4) + half * 8) = o;  // columns wn*64 + a*32 + ..
                 }
+        }
+    }
+    lds_barrier();
+    constexpr int kRowsPerOp = 64 / kChunks;  // tile rows one store instruction covers: 4 or 2
+    const int sc = lane % kChunks, sr = lane / kChunks;
+    const int c0 = nt * kCols + sc * 8;
+    if (kSwiGLU || c0 < N) {
+#pragma unroll 4
+        for (int r0 = wave * kRowsPerOp; r0 < kBM; r0 += kWaves * kRowsPerOp) {
+            const int tr = r0 + sr;
+            if (tr < rows)
+                *(u32x4 *)(C + (int64_t)(row_begin + tr) * ldc + c0) = *(const u32x4 *)(lds + cofs(tr, sc));
         }
     }
 }
