@@ -103,7 +103,7 @@ __device__ __forceinline__ float silu_mul(float g, float u, float clamp) {
 }
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    return pack_bf16x2(a, b);
 }
 
 // one 16-byte-per-lane DMA from a raw buffer straight into LDS (1 KB per wave, lane-linear)

@@ -94,9 +94,6 @@ __device__ __forceinline__ u32x2 dequant8(uint32_t x, u32x2 t) {
     return u32x2{__builtin_amdgcn_perm(vo, ve, 0x05010400u), __builtin_amdgcn_perm(vo, ve, 0x07030602u)};
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
 
 // LDS slot (16-byte granule) of granule g of staged token row r: 16 granules per row
 __device__ __forceinline__ int aslot(int r, int g) { return g ^ (r & 15); }
