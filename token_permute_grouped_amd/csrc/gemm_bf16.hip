@@ -335,15 +335,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         using Y = std::true_type;
         using F = std::false_type;
 
-        // prologue: weights of stages 0 and 1 in flight, activations of 0 and 1 in flight,
-        // activations of 0 written, activations of 2 in flight
+        // prologue: stage 0 (weights, activations), then stage 1, in issue order; activations
+        // of 0 written, activations of 2 in flight.  The barrier waits for stage 0 only: the
+        // weights of stage 1 land by the end of stage 0 like every later stage.
         dmaB(0, 0);
-        dmaB(1, 1);
+        asm volatile("" ::: "memory");  // keep the issue order: loads complete in it
         gloadA(RA0, 0);
+        asm volatile("" ::: "memory");
+        dmaB(1, 1);
+        asm volatile("" ::: "memory");
         gloadA(RA1, 1);
+        asm volatile("" ::: "memory");
         lwriteA(RA0, 0, 0, kLoads);
-        if (nk > 2) gloadA(RA0, 2);
-        wait_vmcnt<0>();
+        if (nk > 2) {
+            gloadA(RA0, 2);
+            wait_vmcnt<kOpsB + 2 * kLoads>();  // weights 1, activations 1 and 2 may be in flight
+        } else {
+            wait_vmcnt<kOpsB + kLoads>();
+        }
         lds_barrier();
         load(0, 0, 0, 0);
         int bs = 0;
