@@ -17,8 +17,9 @@
 // Pipeline.  LDS holds two stages (128 KB).  Global loads go to registers first:
 // while the MFMAs of stage k run, the wave writes stage k+1 from its register set
 // into the free LDS buffer and refills the set with the loads of stage k+2, so a
-// load has about one stage of MFMAs to land.  The LDS writes of a stage are split
-// over two K steps (a burst of them stalls the MFMA issue).  Per stage there is one
+// load has about one stage of MFMAs to land.  The LDS writes of a stage (activation
+// stores and weight DMAs) are split over two K steps: a burst of them stalls the MFMA
+// issue.  Per stage there is one
 // barrier, taken before the last 16-wide K step so that the next stage's first
 // fragments load under that step's MFMAs and the MFMA issue does not drain.
 // Fragment reads of step s+1 are interleaved with the MFMAs of step s.
@@ -227,10 +228,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
         for (int i = i0; i < i0 + n; ++i) *(u32x4 *)(base + i * kLRows * kRowBytes) = R[i];
     };
-    auto dmaB = [&](int kt, int bstage) {
+    auto dmaB = [&](int kt, int bstage, int i0 = 0, int n = kOpsB) {
         unsigned char *dst = lds + kBBase + bstage * kBStage + wave * (kBN / kWaves) * kRowBytes;
 #pragma unroll
-        for (int i = 0; i < kOpsB; ++i) dma16(rsB, offB[i], kt * kRowBytes, dst + i * 1024);
+        for (int i = i0; i < i0 + n; ++i) dma16(rsB, offB[i], kt * kRowBytes, dst + i * 1024);
     };
 
     f32x16 acc[2][4];
@@ -290,8 +291,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
             const int bs1 = bs + 1 == kBStages ? 0 : bs + 1;
             const int bs2 = bs1 + 1 == kBStages ? 0 : bs1 + 1;
             if constexpr (kIssue) {
-                dmaB(kt + 2, bs2);
-                __builtin_amdgcn_sched_group_barrier(0x020, kOpsB, 0);
+                dmaB(kt + 2, bs2, 0, kOpsB / 2);
+                __builtin_amdgcn_sched_group_barrier(0x020, kOpsB / 2, 0);
             }
             // K steps 0 and 1: fragments of the next step under the MFMAs, and the activations
             // of stage kt+1 into the free LDS buffer, half under each step
@@ -301,6 +302,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
             if constexpr (NB > 0) {
                 if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
                 else interleave_ds_mfma<NR, NM>();
+            }
+            if constexpr (kIssue) {
+                dmaB(kt + 2, bs2, kOpsB / 2, kOpsB / 2);
+                __builtin_amdgcn_sched_group_barrier(0x020, kOpsB / 2, 0);
             }
             if constexpr (kNext) lwriteA(Rn, P ^ 1, kLoads / 2, kLoads / 2);
             load(0, P, bs, 2);
