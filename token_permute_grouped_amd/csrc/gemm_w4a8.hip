@@ -355,11 +355,20 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
     __shared__ float xsl[2 * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
     __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot];  // weight staging, 2 slots per wave
 
+    // Block -> tile.  The tile list holds each expert's m-tiles together.  Expert e's blocks are
+    // [first * nb_n, (first + nm) * nb_n); they run in units of G n-tiles, the nm m-tiles of an
+    // n-tile G blocks apart: with G = 8 those land on one XCD (block b runs on XCD b mod 8) at
+    // the same time, so the weights an expert's second m-tile streams are L2 hits.
     const int nb_n = g.N / kBN;
-    const int mt = blockIdx.x / nb_n;
-    const int nt = blockIdx.x % nb_n;
-    if (mt >= n_tiles[0]) return;
-    const int e = tiles[2 * mt];
+    const int tq = blockIdx.x / nb_n;  // a tile of the expert this block works for
+    if (tq >= n_tiles[0]) return;
+    const int e = tiles[2 * tq];
+    const int first = tq - tiles[2 * tq + 1] / kBM;
+    const int nm = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+    const int G = nb_n % 8 == 0 ? 8 : nb_n % 4 == 0 ? 4 : nb_n % 2 == 0 ? 2 : 1;
+    const int r = blockIdx.x - first * nb_n, unit = nm * G;
+    const int mt = first + (r % unit) / G;
+    const int nt = (r / unit) * G + (r % unit) % G;
     const int row_begin = offsets[e] + tiles[2 * mt + 1];
     const int rows = min(kBM, offsets[e + 1] - row_begin);
 

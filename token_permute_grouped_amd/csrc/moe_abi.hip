@@ -102,7 +102,7 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
     int32_t *tiles = (int32_t *)(ws + L.tiles);
     int32_t *n_tiles = (int32_t *)(ws + L.n_tiles);
     const int64_t max_tiles = max_m_tiles(p);
-    int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), tiles, n_tiles, s));
+    int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), is_w4a8(&p), tiles, n_tiles, s));
     if (st) return st;
     if (is_w4a8(&p))
         return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,
@@ -151,7 +151,7 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
     const bool small = n_slots(*p) <= kChunk && p->T <= 32;
     if ((st = mark(0))) return st;
     if (small) {
-        if ((st = hip_status(launch_frontend_small(logits, slot_drop, p->T, p->E, p->k, gemm_bm(*p), topk_idx,
+        if ((st = hip_status(launch_frontend_small(logits, slot_drop, p->T, p->E, p->k, gemm_bm(*p), is_w4a8(p), topk_idx,
                                                    topk_w, offsets, row_src, slot_row, tiles, n_tiles, s))))
             return st;
     } else if ((st = hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, s)))) {
@@ -166,7 +166,7 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
                                         x_perm_scale, s))))
         return st;
     if ((st = mark(3))) return st;
-    if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), tiles, n_tiles, s)))) return st;
+    if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s)))) return st;
     if ((st = mark(4))) return st;
     if (w4) {
         if ((st = hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,

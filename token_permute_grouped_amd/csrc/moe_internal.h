@@ -58,12 +58,15 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
 hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *slot_row, int T, int k, int H,
                           int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);
 
-hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
+// GEMM m-tile list; by_expert: each expert's tiles together (W4A8), else full tiles first (bf16)
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int by_expert, int32_t *tiles,
+                              int32_t *n_tiles, hipStream_t s);
 
 // routing + tables + tile list in one workgroup, for at most kChunk slots
 hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
-                                 int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *row_src,
-                                 int32_t *slot_row, int32_t *tiles, int32_t *n_tiles, hipStream_t s);
+                                 int by_expert, int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                 int32_t *row_src, int32_t *slot_row, int32_t *tiles, int32_t *n_tiles,
+                                 hipStream_t s);
 
 hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,

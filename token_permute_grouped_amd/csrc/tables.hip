@@ -140,16 +140,17 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ i
 }
 
 // tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert (tiles of bm rows);
-// n_tiles[0] = count.  Full tiles come first (expert by expert), then each expert's partial
-// last tile, so tiles that run side by side tend to have the same amount of work.
-// One thread per expert.
+// n_tiles[0] = count, n_tiles[1] = tiles before the partial section.  Default order: full
+// tiles first (expert by expert), then each expert's partial last tile.  by_expert: every
+// expert's tiles together in row order (n_tiles[1] = count).  One thread per expert.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E, int bm,
-                                                          int32_t *__restrict__ tiles,
+                                                          int by_expert, int32_t *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles) {
     __shared__ int nf[256], np[256];
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int full = cnt / bm, part = (cnt % bm) ? 1 : 0;
+    const int full = by_expert ? (cnt + bm - 1) / bm : cnt / bm;
+    const int part = !by_expert && (cnt % bm) ? 1 : 0;
     nf[e] = full;
     np[e] = part;
     __syncthreads();
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
 // results as route_topk + chunk_hist + scan + rank + build_tiles.  Slot s is thread s.
 constexpr int kFrontWaves = kChunk / kWave;  // 16
 __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
-    const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop, int T, int E, int k, int bm,
+    const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop, int T, int E, int k, int bm, int by_expert,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ offsets,
     int32_t *__restrict__ row_src, int32_t *__restrict__ slot_row, int32_t *__restrict__ tiles,
     int32_t *__restrict__ n_tiles) {
@@ -248,12 +249,12 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
         if (tid >= R) row_src[tid] = -1;  // rows past the live count (r < R never lands here)
     }
 
-    // GEMM tile list (as build_tiles_kernel): full tiles first, then partial ones
+    // GEMM tile list (as build_tiles_kernel)
     int full = 0, part = 0;
     if (tid < 256) {
         const int c = tid < E ? off[tid + 1] - off[tid] : 0;
-        full = c / bm;
-        part = (c % bm) ? 1 : 0;
+        full = by_expert ? (c + bm - 1) / bm : c / bm;
+        part = !by_expert && (c % bm) ? 1 : 0;
         sa[tid] = full;
         sb[tid] = part;
     }
@@ -288,10 +289,11 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
 }
 
 hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
-                                 int32_t *topk_idx, float *topk_w, int32_t *offsets, int32_t *row_src,
-                                 int32_t *slot_row, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
-    hipLaunchKernelGGL(frontend_small_kernel, dim3(1), dim3(kChunk), 0, s, logits, slot_drop, T, E, k, bm, topk_idx,
-                       topk_w, offsets, row_src, slot_row, tiles, n_tiles);
+                                 int by_expert, int32_t *topk_idx, float *topk_w, int32_t *offsets,
+                                 int32_t *row_src, int32_t *slot_row, int32_t *tiles, int32_t *n_tiles,
+                                 hipStream_t s) {
+    hipLaunchKernelGGL(frontend_small_kernel, dim3(1), dim3(kChunk), 0, s, logits, slot_drop, T, E, k, bm, by_expert,
+                       topk_idx, topk_w, offsets, row_src, slot_row, tiles, n_tiles);
     return hipGetLastError();
 }
 
@@ -306,8 +308,9 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
     return hipGetLastError();
 }
 
-hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int32_t *tiles, int32_t *n_tiles, hipStream_t s) {
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, bm, tiles, n_tiles);
+hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int by_expert, int32_t *tiles,
+                              int32_t *n_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, E, bm, by_expert, tiles, n_tiles);
     return hipGetLastError();
 }
 
