@@ -10,6 +10,8 @@ Timing: W untimed warm-up steps, then K moe_forward steps bracketed by device
 synchronisation and HIP events on the library's stream (ms_per_step, value).  The
 per-stage durations come from K further steps through moe_forward_timed (same
 kernels plus a HIP event at every stage boundary), measured live in the same run.
+On bf16 data the forward folds the row gather into GEMM1; the permute kernel's own
+HBM rate comes from K calls of moe_permute_timed on the same routing.
 
 Prints one JSON line.  The CPU baseline is the fp64 oracle (test infrastructure)
 timed on a bounded sample of the same workload on the host cores.
@@ -205,6 +207,39 @@ def main():
         for e in row:
             hip.destroy(e)
 
+    # the permute (tables + row gather) on its own, on the forward's routing: the gather kernel's
+    # HBM rate (the bf16 forward runs no separate gather)
+    S = cfg.T * cfg.k
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    tpg.moe_route_topk(d["logits"], d["slot_drop"], p, idx, tw)
+    offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+    rsrc = torch.empty(S, dtype=torch.int32, device=dev)
+    srow = torch.empty(S, dtype=torch.int32, device=dev)
+    x_perm = torch.empty((S, cfg.H), dtype=torch.uint8 if w4 else torch.int16, device=dev)
+    x_perm_scale = torch.empty((S, cfg.H // 128), dtype=torch.float32, device=dev) if w4 else None
+    pws = torch.empty(max(1, tpg.moe_workspace_bytes(p, tpg.MOE_WS_PERMUTE)), dtype=torch.uint8, device=dev)
+    def permute_run(after_forward):
+        pev = [[hip.create() for _ in range(tpg.MOE_N_PERMUTE_EVENTS)] for _ in range(args.steps + 2)]
+        for i in range(args.steps + 2):  # the first two are warm-up
+            if after_forward:
+                step()
+            tpg.moe_permute_timed(d["x"], d["x_scale"], idx, p, offs, rsrc, srow, x_perm, x_perm_scale, pws, pev[i])
+        torch.cuda.synchronize()
+        tab = float(np.mean([hip.ms(pev[i][0], pev[i][1]) for i in range(2, args.steps + 2)]))
+        gat = float(np.mean([hip.ms(pev[i][1], pev[i][2]) for i in range(2, args.steps + 2)]))
+        for row in pev:
+            for e in row:
+                hip.destroy(e)
+        return tab, gat
+
+    # back to back: each call also pays the write-back of the previous call's x_perm from the
+    # last-level cache (the steady state of a loop of permutes)
+    permute_tables_ms, permute_gather_ms = permute_run(False)
+    # right after a forward, as the permute would run inside a layer's pipeline
+    _, permute_gather_after_fwd_ms = permute_run(True)
+    del x_perm, x_perm_scale, pws
+
     T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
     R = T * k - (int(inp["slot_drop"].sum()) if inp.get("slot_drop") is not None else 0)
     act_b = 1 if w4 else 2
@@ -269,8 +304,14 @@ def main():
         "tflops_gemms": round(tflops(gemm1_flops + gemm2_flops, gemm_ms), 2),
         "mfma_frac_gemms": None if w4 else round(tflops(gemm1_flops + gemm2_flops, gemm_ms) / PEAK_BF16_TFLOPS, 4),
         "gemm2_tflops": None if w4 else round(tflops(gemm2_flops, stage_ms["gemm2"]), 2),
-        "gather_gbs": round(gbs(gather_bytes, stage_ms["gather"]), 1),
-        "gather_hbm_frac": round(gbs(gather_bytes, stage_ms["gather"]) / PEAK_HBM_GBS, 4),
+        # permute_kernel measured on its own (moe_permute_timed); the bf16 forward folds it into GEMM1
+        "gather_ms": round(permute_gather_ms, 4),
+        "gather_gbs": round(gbs(gather_bytes, permute_gather_ms), 1),
+        "gather_hbm_frac": round(gbs(gather_bytes, permute_gather_ms) / PEAK_HBM_GBS, 4),
+        "gather_after_forward_ms": round(permute_gather_after_fwd_ms, 4),
+        "gather_after_forward_hbm_frac": round(gbs(gather_bytes, permute_gather_after_fwd_ms) / PEAK_HBM_GBS, 4),
+        "gather_in_forward": "separate kernel" if w4 else "folded into GEMM1 (x read through row_src)",
+        "permute_tables_ms": round(permute_tables_ms, 4),
         "combine_gbs": round(gbs(combine_bytes, stage_ms["combine"]), 1),
         "combine_hbm_frac": round(gbs(combine_bytes, stage_ms["combine"]) / PEAK_HBM_GBS, 4),
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},

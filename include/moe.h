@@ -139,6 +139,16 @@ int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, co
                 int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, void *ws,
                 size_t ws_bytes, void *stream);
 
+/* moe_permute with timing marks: identical work, plus hipEventRecord of
+ * stage_events[i] (MOE_N_PERMUTE_EVENTS hipEvent_t handles, created by the
+ * caller) on `stream`: [0] tables [1] row gather [2].  For measurement of the
+ * gather kernel on its own (moe_forward on bf16 data folds the gather into the
+ * first GEMM, see moe_forward). */
+#define MOE_N_PERMUTE_EVENTS 3
+int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
+                      int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale,
+                      void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
+
 /* Grouped expert FFN.  For every expert e and row r in [offsets[e], offsets[e+1]):
  * y_perm[r] = (silu(g) * u) W2_e^T with [g | u] = x_perm[r] W1_e^T (clamped if
  * swiglu_clamp > 0).  x_perm as produced by moe_permute; y_perm bf16 [T*k][H];
@@ -154,7 +164,12 @@ int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const flo
                           void *out, void *stream);
 
 /* The whole forward: route, permute, grouped FFN, combine, on one stream, with
- * every intermediate in ws (at least moe_workspace_bytes(p, MOE_WS_FORWARD)). */
+ * every intermediate in ws (at least moe_workspace_bytes(p, MOE_WS_FORWARD)).
+ * On bf16 data with T*H*2 < 2^31 the row gather is folded into GEMM1, which reads
+ * row r of the expert-major order straight from x[row_src[r] / k] (the permute
+ * fused into the expert kernel, as Megatron-LM "add permute fusion into hybrid ep"
+ * fuses it into dispatch); no x_perm is written and the workspace holds none.  The
+ * result is bitwise the same as moe_permute + moe_grouped_ffn + combine. */
 int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
                 const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream);
 
@@ -163,7 +178,8 @@ int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, co
  * on `stream` at each stage boundary:
  *   [0] route [1] permutation tables [2] row gather [3] GEMM tile list [4]
  *   GEMM1 + SwiGLU [5] GEMM2 [6] combine [7]
- * (for W4A8 the two GEMMs run between marks 4 and 5 and mark 6 follows at once).
+ * (for W4A8 the two GEMMs run between marks 4 and 5 and mark 6 follows at once;
+ * where the gather is folded into GEMM1, mark 3 follows mark 2 at once).
  * For measurement; the marks add no work to the kernels. */
 #define MOE_N_STAGE_EVENTS 8
 int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,

@@ -57,6 +57,9 @@ def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     w = ctypes.byref(tpg.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
     assert lib.moe_route_topk(FAKE, None, p, FAKE, FAKE, None) == status
     assert lib.moe_permute(FAKE, FAKE, FAKE, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == status
+    ev = (ctypes.c_void_p * tpg.MOE_N_PERMUTE_EVENTS)(*[FAKE] * tpg.MOE_N_PERMUTE_EVENTS)
+    assert lib.moe_permute_timed(FAKE, FAKE, FAKE, p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None,
+                                 ev) == status
     assert lib.moe_grouped_ffn(FAKE, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
     assert lib.moe_unpermute_combine(FAKE, FAKE, FAKE, p, FAKE, None) == status
     assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
@@ -77,6 +80,10 @@ def test_null_pointers_are_rejected():
     assert lib.moe_unpermute_combine(FAKE, FAKE, None, p, FAKE, None) == NULL
     assert lib.moe_forward(FAKE, None, None, None, w, p, FAKE, FAKE, 1 << 40, None) == NULL
     assert lib.moe_w4a8_dequant_table(None, None) == NULL
+    ev = (ctypes.c_void_p * tpg.MOE_N_PERMUTE_EVENTS)(FAKE, None, FAKE)
+    assert lib.moe_permute_timed(FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, ev) == NULL
+    assert lib.moe_permute_timed(FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None,
+                                 None) == NULL
     # W4A8 needs the scale arrays too
     p4 = ctypes.byref(_p(prec=tpg.MOE_PREC_W4A8, H=256))
     assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p4, FAKE, FAKE, 1 << 40, None) == NULL
@@ -92,6 +99,9 @@ def test_small_workspace_is_rejected():
     for which, call in [
         (tpg.MOE_WS_PERMUTE, lambda n: lib.moe_permute(FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, n,
                                                        None)),
+        (tpg.MOE_WS_PERMUTE, lambda n: lib.moe_permute_timed(
+            FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, n, None,
+            (ctypes.c_void_p * tpg.MOE_N_PERMUTE_EVENTS)(*[FAKE] * tpg.MOE_N_PERMUTE_EVENTS))),
         (tpg.MOE_WS_GROUPED_FFN, lambda n: lib.moe_grouped_ffn(FAKE, None, FAKE, w, p, FAKE, FAKE, n, None)),
         (tpg.MOE_WS_FORWARD, lambda n: lib.moe_forward(FAKE, None, FAKE, None, w, p, FAKE, FAKE, n, None)),
     ]:
@@ -115,8 +125,15 @@ def test_workspace_sizes():
     big = _p(T=32768, H=7168, I=2048, E=32, k=8, glu_interleave=32)
     n = tpg.moe_workspace_bytes(big, tpg.MOE_WS_FORWARD)
     S = 32768 * 8
-    # holds x_perm, y_perm (bf16 [S][H]) and h (bf16 [S][I]) at least; sized by shape only
-    assert n >= S * (7168 * 2 * 2 + 2048 * 2)
+    # the bf16 forward gathers inside GEMM1 (T*H*2 < 2^31): it holds y_perm (bf16 [S][H]) and
+    # h (bf16 [S][I]) but no x_perm; sized by shape only
+    assert S * (7168 * 2 + 2048 * 2) <= n < S * (7168 * 2 * 2 + 2048 * 2)
+    # too many token rows for 31-bit offsets into x: the forward runs the separate gather
+    unfused = _p(T=131072, H=8192, I=1024, E=8, k=2)
+    assert tpg.moe_workspace_bytes(unfused, tpg.MOE_WS_FORWARD) >= 131072 * 2 * (8192 * 2 * 2 + 1024 * 2)
+    # W4A8 keeps its fp8 x_perm and scales
+    w4 = _p(T=256, H=7168, I=2048, E=32, k=8, prec=tpg.MOE_PREC_W4A8, swiglu_clamp=10.0)
+    assert tpg.moe_workspace_bytes(w4, tpg.MOE_WS_FORWARD) >= 256 * 8 * (7168 + 7168 // 128 * 4 + 7168 * 2)
     assert tpg.moe_workspace_bytes(big, tpg.MOE_WS_PERMUTE) < tpg.moe_workspace_bytes(big, tpg.MOE_WS_GROUPED_FFN) < n
     assert tpg.moe_workspace_bytes(big, 99) == 0
 

@@ -214,6 +214,22 @@ def test_forward_small_front_end_matches_separate_steps(cfg):
     assert (fused == steps).all()
 
 
+@pytest.mark.parametrize("name", ["ragged_tiles", "interleaved_drop", "clamped", "max_experts"] + FULL)
+def test_forward_gather_in_gemm1_equals_separate_steps(name):
+    """the bf16 forward reads x through row_src inside GEMM1 instead of gathering x_perm first;
+    its output must be bitwise what route + permute + grouped FFN + combine give"""
+    inp, d = workload(name)
+    fused = bf16_host(d.forward())
+    idx, w = d.route()
+    offsets, row_src, slot_row, x_perm, x_perm_scale = d.permute(idx, canary=False)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    steps = bf16_host(d.combine(y, slot_row, w))
+    del y, x_perm
+    n_diff = int((fused != steps).sum())
+    print(f"[gpu parity] {name}: fused-gather forward vs separate steps, {n_diff} differing elements")
+    assert n_diff == 0
+
+
 @pytest.mark.parametrize("name", ["tiny", "skewed"])
 def test_forward_is_deterministic(name):
     _, d = workload(name)

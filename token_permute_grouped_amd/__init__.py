@@ -21,9 +21,10 @@ MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_workspace_bytes", "moe_status_str", "moe_last_hip_error", "moe_route_topk", "moe_permute",
-    "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_w4a8_dequant_table",
+    "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_w4a8_dequant_table",
 )
 MOE_N_STAGE_EVENTS = 8
+MOE_N_PERMUTE_EVENTS = 3
 STAGES = ("route", "tables", "gather", "tile_list", "gemm1_swiglu", "gemm2", "combine")
 
 
@@ -70,12 +71,13 @@ def load() -> ctypes.CDLL:
     lib.moe_last_hip_error.restype = I32
     lib.moe_route_topk.argtypes = [P, P, PP, P, P, P]
     lib.moe_permute.argtypes = [P, P, P, PP, P, P, P, P, P, P, SZ, P]
+    lib.moe_permute_timed.argtypes = [P, P, P, PP, P, P, P, P, P, P, SZ, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.moe_grouped_ffn.argtypes = [P, P, P, PW, PP, P, P, SZ, P]
     lib.moe_unpermute_combine.argtypes = [P, P, P, PP, P, P]
     lib.moe_forward.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P]
     lib.moe_forward_timed.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.moe_w4a8_dequant_table.argtypes = [P, P]
-    for name in ("moe_route_topk", "moe_permute", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward",
+    for name in ("moe_route_topk", "moe_permute", "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward",
                  "moe_forward_timed", "moe_w4a8_dequant_table"):
         getattr(lib, name).restype = I32
     _lib = lib
@@ -136,6 +138,18 @@ def moe_permute(x, x_scale, topk_idx, problem: Problem, offsets, row_src, slot_r
     _check("moe_permute", load().moe_permute(_ptr(x), _ptr(x_scale), _ptr(topk_idx), ctypes.byref(problem),
                                              _ptr(offsets), _ptr(row_src), _ptr(slot_row), _ptr(x_perm),
                                              _ptr(x_perm_scale), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_permute_timed(x, x_scale, topk_idx, problem: Problem, offsets, row_src, slot_row, x_perm, x_perm_scale, ws,
+                      stage_events, ws_bytes=None, stream=None):
+    """stage_events: MOE_N_PERMUTE_EVENTS raw hipEvent_t handles (ints)"""
+    if ws_bytes is None:
+        ws_bytes = _nbytes(ws)
+    ev = (ctypes.c_void_p * MOE_N_PERMUTE_EVENTS)(*stage_events)
+    _check("moe_permute_timed", load().moe_permute_timed(_ptr(x), _ptr(x_scale), _ptr(topk_idx),
+                                                         ctypes.byref(problem), _ptr(offsets), _ptr(row_src),
+                                                         _ptr(slot_row), _ptr(x_perm), _ptr(x_perm_scale), _ptr(ws),
+                                                         ws_bytes, _stream(stream), ev))
 
 
 def moe_grouped_ffn(x_perm, x_perm_scale, offsets, weights: Weights, problem: Problem, y_perm, ws, ws_bytes=None,

@@ -46,6 +46,13 @@
 // is instantiated per live-block count, so it stays branch-free) and only live
 // rows are stored.
 //
+// Fused gather.  GEMM1 can read its activation rows straight from the token rows x
+// [T][K] through the row_src table (row r of the expert-major order is token
+// row_src[r] / k), so the forward needs no separate permuted copy of x: the permute
+// of Megatron-LM "add permute fusion into hybrid ep" then happens in the tile loads,
+// the way the FlashInfer split kernels fold dispatch into their first GEMM.  Each
+// 128-byte piece of a row is still one whole cache line, so the loads stay coalesced.
+//
 // Scheduling.  The device-side tile list gives the m-tiles (expert, first row);
 // tile_map assigns them to workgroups by band and XCD rectangle (below).
 // Workgroups past the tile count exit before any barrier.
@@ -148,7 +155,10 @@ __device__ __forceinline__ void interleave_x_ds_mfma() {
 
 template <bool kSwiGLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
-    const uint16_t *__restrict__ A,        // [S][K] activations in expert-contiguous row order
+    const uint16_t *__restrict__ A,        // [S][K] activations in expert-contiguous row order, or
+                                           // with row_src: the token rows [a_rows][K]
+    const int32_t *__restrict__ row_src,   // NULL, or [S]: row r reads token row row_src[r] / gather_k
+    int gather_k, int a_rows,
     const uint16_t *__restrict__ W,        // [E][N][K] expert weights
     const int32_t *__restrict__ offsets,   // [E+1]
     const int32_t *__restrict__ tiles,     // [2 * n_tiles]: expert, first row within the expert
@@ -193,13 +203,37 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     //      8 rows per 1 KB op (row lane/8, slot lane%8).  Raw buffer resources bound every read:
     //      rows past the tile's live rows, and weight rows past N, read as zero.
     const int lrow = tid >> 3, lkc = tid & 7;
+    const bool gather = row_src != nullptr;
+    // source rows of this thread's activation loads (fused gather): issued first, used after
+    // the first weight DMA so that their latency overlaps it
+    // (no lane-dependent branch or select touches these before their use, which keeps the
+    // compiler from waiting for them early and the buffer descriptors in scalar registers)
+    int src[kLoads] = {};
+    if (gather) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) src[i] = row_src[row_begin + min(lrow + kLRows * i, rows - 1)];
+    }
     const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A + (int64_t)row_begin * K), (short)0, rows * K * 2, 0x00020000);
+        (void *)(A + (gather ? 0 : (int64_t)row_begin * K)), (short)0, gather ? a_rows * K * 2 : rows * K * 2,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(W + (int64_t)e * N * K), (short)0, N * K * 2, 0x00020000);
     uint32_t offA[kLoads], offB[kOpsB];
+    // Byte offsets of the activation loads.  Rows past the tile's live rows get an offset
+    // beyond the buffer (a_rows * K * 2 < 2^31, checked by the host), so they read zero.
+    // Token of slot s = t*k + j: s / k in double precision, exact for integers below 2^31 (the
+    // fractional part of a non-integer quotient is at least 1/k, far above the rounding error).
+    auto init_offA = [&]() {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) offA[i] = (uint32_t)((lrow + kLRows * i) * K + lkc * 8) * 2u;
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = lrow + kLRows * i;
+            asm volatile("" : "+v"(src[i])::"memory");  // consumed here, after the first weight DMA
+            const int t = (int)((double)src[i] / (double)gather_k);
+            offA[i] = !gather ? (uint32_t)(r * K + lkc * 8) * 2u
+                      : r >= rows ? 0x80000000u  // a row past the tile: read as zero
+                                  : (uint32_t)(t * K + lkc * 8) * 2u;
+        }
+    };
 #pragma unroll
     for (int i = 0; i < kOpsB; ++i) {
         const int r = wave * (kBN / kWaves) + i * 8 + (lane >> 3);  // tile weight row
@@ -345,6 +379,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         // weights of stage 1 land by the end of stage 0 like every later stage.
         dmaB(0, 0);
         asm volatile("" ::: "memory");  // keep the issue order: loads complete in it
+        init_offA();
         gloadA(RA0, 0);
         asm volatile("" ::: "memory");
         dmaB(1, 1);
@@ -433,14 +468,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
 
 namespace {
 template <bool kSwiGLU>
-hipError_t launch(const uint16_t *A, const uint16_t *W, const int32_t *offsets, const int32_t *tiles,
-                  const int32_t *n_tiles, int64_t max_tiles, int K, int N, int I, int il, float clamp, uint16_t *C,
-                  int ldc, hipStream_t s) {
+hipError_t launch(const uint16_t *A, const int32_t *row_src, int gather_k, int a_rows, const uint16_t *W,
+                  const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int K,
+                  int N, int I, int il, float clamp, uint16_t *C, int ldc, hipStream_t s) {
     const int nb_n = (N + kBN - 1) / kBN;
     const TileMap tm = tile_map(nb_n);
     const int64_t blocks = (max_tiles + tm.gm - 1) / tm.gm * tm.per_band;
-    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kSwiGLU>, dim3(blocks), dim3(kThreads), 0, s, A, W, offsets, tiles,
-                       n_tiles, K, N, I, il, clamp, C, ldc);
+    hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kSwiGLU>, dim3(blocks), dim3(kThreads), 0, s, A, row_src, gather_k,
+                       a_rows, W, offsets, tiles, n_tiles, K, N, I, il, clamp, C, ldc);
     return hipGetLastError();
 }
 }  // namespace
@@ -448,13 +483,23 @@ hipError_t launch(const uint16_t *A, const uint16_t *W, const int32_t *offsets, 
 hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, const int32_t *offsets,
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
                                     int glu_interleave, float clamp, uint16_t *h, hipStream_t s) {
-    return launch<true>(x_perm, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave, clamp, h, I, s);
+    return launch<true>(x_perm, nullptr, 1, 0, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave,
+                        clamp, h, I, s);
+}
+
+hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row_src, int T, int k,
+                                           const uint16_t *w1, const int32_t *offsets, const int32_t *tiles,
+                                           const int32_t *n_tiles, int64_t max_tiles, int H, int I,
+                                           int glu_interleave, float clamp, uint16_t *h, hipStream_t s) {
+    if (!gather_fits(T, H)) return hipErrorInvalidValue;
+    return launch<true>(x, row_src, k, T, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave, clamp,
+                        h, I, s);
 }
 
 hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
                              hipStream_t s) {
-    return launch<false>(h, w2, offsets, tiles, n_tiles, max_tiles, I, H, I, 0, 0.0f, y_perm, H, s);
+    return launch<false>(h, nullptr, 1, 0, w2, offsets, tiles, n_tiles, max_tiles, I, H, I, 0, 0.0f, y_perm, H, s);
 }
 
 }  // namespace tpg

@@ -74,8 +74,8 @@ WsLayout ws_layout(const moe_problem &p) {
     o = align256(o + S * 4);
     L.slot_row = o;
     o = align256(o + S * 4);
-    L.x_perm = o;
-    o = align256(o + S * (size_t)p.H * act);
+    L.x_perm = o;  // the bf16 forward gathers inside GEMM1 and needs no x_perm
+    if (!fused_gather(p)) o = align256(o + S * (size_t)p.H * act);
     L.x_perm_scale = o;
     if (is_w4a8(&p)) o = align256(o + S * (size_t)(p.H / 128) * 4);
     L.y_perm = o;
@@ -87,13 +87,19 @@ WsLayout ws_layout(const moe_problem &p) {
 namespace {
 
 int run_permute(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem &p, int32_t *offsets,
-                int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, char *ws, hipStream_t s) {
+                int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, char *ws, hipStream_t s,
+                void *const *ev = nullptr) {
     const WsLayout L = ws_layout(p);
     int32_t *chunk_counts = (int32_t *)(ws + L.chunk_counts);
-    int st = hip_status(launch_tables(topk_idx, p.T, p.k, p.E, chunk_counts, offsets, row_src, slot_row, s));
-    if (st) return st;
-    return hip_status(launch_permute(x, is_w4a8(&p) ? x_scale : nullptr, slot_row, p.T, p.k, p.H,
-                                     is_w4a8(&p) ? 1 : 2, x_perm, x_perm_scale, s));
+    auto mark = [&](int i) -> int { return ev ? hip_status(hipEventRecord((hipEvent_t)ev[i], s)) : MOE_OK; };
+    int st = mark(0);
+    if (!st) st = hip_status(launch_tables(topk_idx, p.T, p.k, p.E, chunk_counts, offsets, row_src, slot_row, s));
+    if (!st) st = mark(1);
+    if (!st)
+        st = hip_status(launch_permute(x, is_w4a8(&p) ? x_scale : nullptr, slot_row, p.T, p.k, p.H,
+                                       is_w4a8(&p) ? 1 : 2, x_perm, x_perm_scale, s));
+    if (!st) st = mark(2);
+    return st;
 }
 
 int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t *offsets, const moe_weights &w,
@@ -162,8 +168,9 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row, s))))
         return st;
     if ((st = mark(2))) return st;
-    if ((st = hip_status(launch_permute(x, w4 ? x_scale : nullptr, slot_row, p->T, p->k, p->H, w4 ? 1 : 2, x_perm,
-                                        x_perm_scale, s))))
+    const bool fused = fused_gather(*p);
+    if (!fused && (st = hip_status(launch_permute(x, w4 ? x_scale : nullptr, slot_row, p->T, p->k, p->H, w4 ? 1 : 2,
+                                                  x_perm, x_perm_scale, s))))
         return st;
     if ((st = mark(3))) return st;
     if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s)))) return st;
@@ -176,10 +183,16 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         if ((st = mark(5))) return st;
     } else {
         uint16_t *h = (uint16_t *)(b + L.h);
-        if ((st = hip_status(launch_gemm1_swiglu_bf16((const uint16_t *)x_perm, (const uint16_t *)w->w1, offsets,
-                                                      tiles, n_tiles, max_tiles, p->H, p->I, p->glu_interleave,
-                                                      p->swiglu_clamp, h, s))))
-            return st;
+        if (fused)
+            st = hip_status(launch_gemm1_swiglu_gather_bf16((const uint16_t *)x, row_src, p->T, p->k,
+                                                            (const uint16_t *)w->w1, offsets, tiles, n_tiles,
+                                                            max_tiles, p->H, p->I, p->glu_interleave,
+                                                            p->swiglu_clamp, h, s));
+        else
+            st = hip_status(launch_gemm1_swiglu_bf16((const uint16_t *)x_perm, (const uint16_t *)w->w1, offsets,
+                                                     tiles, n_tiles, max_tiles, p->H, p->I, p->glu_interleave,
+                                                     p->swiglu_clamp, h, s));
+        if (st) return st;
         if ((st = mark(5))) return st;
         if ((st = hip_status(launch_gemm2_bf16(h, (const uint16_t *)w->w2, offsets, tiles, n_tiles, max_tiles, p->H,
                                                p->I, (uint16_t *)y_perm, s))))
@@ -245,6 +258,22 @@ int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, co
     if (ws_bytes < moe_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
     return run_permute(x, x_scale, topk_idx, *p, offsets, row_src, slot_row, x_perm, x_perm_scale, (char *)ws,
                        (hipStream_t)stream);
+}
+
+int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
+                      int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale,
+                      void *ws, size_t ws_bytes, void *stream, void *const *stage_events) {
+    if (!stage_events) return MOE_ERR_NULL;
+    for (int i = 0; i < MOE_N_PERMUTE_EVENTS; ++i)
+        if (!stage_events[i]) return MOE_ERR_NULL;
+    int st = check_problem(p);
+    if (st) return st;
+    if (p->T == 0) return MOE_OK;
+    if (!x || !topk_idx || !offsets || !row_src || !slot_row || !x_perm || !ws) return MOE_ERR_NULL;
+    if (is_w4a8(p) && (!x_scale || !x_perm_scale)) return MOE_ERR_NULL;
+    if (ws_bytes < moe_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
+    return run_permute(x, x_scale, topk_idx, *p, offsets, row_src, slot_row, x_perm, x_perm_scale, (char *)ws,
+                       (hipStream_t)stream, stage_events);
 }
 
 int moe_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t *offsets, const moe_weights *w,

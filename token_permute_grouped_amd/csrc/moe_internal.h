@@ -72,6 +72,16 @@ hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, 
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
                                     int glu_interleave, float clamp, uint16_t *h, hipStream_t s);
 
+// GEMM1 + SwiGLU reading its activation rows from the token rows x [T][H] through row_src
+// (the gather fused into the tile loads); needs gather_fits(T, H)
+inline bool gather_fits(int64_t T, int64_t H) { return T * H * 2 <= 0x7FFFFFFF; }
+// moe_forward (bf16) skips the separate row gather and runs GEMM1 on x through row_src
+inline bool fused_gather(const moe_problem &p) { return p.prec == MOE_PREC_BF16 && gather_fits(p.T, p.H); }
+hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row_src, int T, int k,
+                                           const uint16_t *w1, const int32_t *offsets, const int32_t *tiles,
+                                           const int32_t *n_tiles, int64_t max_tiles, int H, int I,
+                                           int glu_interleave, float clamp, uint16_t *h, hipStream_t s);
+
 hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
                              hipStream_t s);
