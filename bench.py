@@ -105,6 +105,36 @@ def cpu_baseline(inp, budget_s):
                       f"{dt:.1f} s"}
 
 
+def dense_gemm_reference(args):
+    """hipBLASLt (through torch.matmul) on dense GEMMs of the grouped GEMMs' sizes: M = T*k rows,
+    GEMM1 [M, H] x [2I, H]^T and GEMM2 [M, I] x [H, I]^T, bf16, both operands K-contiguous."""
+    import torch
+    from moe_synth import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    M = cfg.T * cfg.k
+    dev = torch.device("cuda:0")
+    out = {"dense_gemm_reference": f"torch.matmul bf16 (hipBLASLt), {args.workload} sizes", "results": []}
+    for name, N, K in (("gemm1", 2 * cfg.I, cfg.H), ("gemm2", cfg.H, cfg.I)):
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        for _ in range(args.warmup):
+            c = a @ b.t()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            c = a @ b.t()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+        out["results"].append({"gemm": name, "M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(tf, 1),
+                               "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del a, b, c
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +147,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference kernel for HBM byte counters)")
+    ap.add_argument("--dense-gemm-reference", action="store_true",
+                    help="only time the vendor library's dense bf16 GEMMs (torch.matmul, hipBLASLt) with the grouped "
+                         "GEMMs' total rows and shapes, as a reference point for the MFMA fraction on this device")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
@@ -132,6 +165,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4, "copy_calibration_bytes_written": b.numel() * 4}))
+        return
+
+    if args.dense_gemm_reference:
+        dense_gemm_reference(args)
         return
 
     import token_permute_grouped_amd as tpg
