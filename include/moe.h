@@ -142,8 +142,8 @@ int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, co
 /* moe_permute with timing marks: identical work, plus hipEventRecord of
  * stage_events[i] (MOE_N_PERMUTE_EVENTS hipEvent_t handles, created by the
  * caller) on `stream`: [0] tables [1] row gather [2].  For measurement of the
- * gather kernel on its own (moe_forward on bf16 data folds the gather into the
- * first GEMM, see moe_forward). */
+ * gather kernel on its own (moe_forward folds the gather into the first GEMM, see
+ * moe_forward). */
 #define MOE_N_PERMUTE_EVENTS 3
 int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
                       int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale,
@@ -165,11 +165,13 @@ int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const flo
 
 /* The whole forward: route, permute, grouped FFN, combine, on one stream, with
  * every intermediate in ws (at least moe_workspace_bytes(p, MOE_WS_FORWARD)).
- * On bf16 data with T*H*2 < 2^31 the row gather is folded into GEMM1, which reads
- * row r of the expert-major order straight from x[row_src[r] / k] (the permute
- * fused into the expert kernel, as Megatron-LM "add permute fusion into hybrid ep"
- * fuses it into dispatch); no x_perm is written and the workspace holds none.  The
- * result is bitwise the same as moe_permute + moe_grouped_ffn + combine. */
+ * Whenever the byte offsets into x fit 31 bits (T*H*2 < 2^31 for bf16, T*H < 2^31
+ * for W4A8) the row gather is folded into GEMM1, which reads row r of the
+ * expert-major order (and, for W4A8, its activation scales) straight from
+ * x[row_src[r] / k] (the permute fused into the expert kernel, as Megatron-LM "add
+ * permute fusion into hybrid ep" fuses it into dispatch); no x_perm is written and
+ * the workspace holds none.  The result is bitwise the same as moe_permute +
+ * moe_grouped_ffn + moe_unpermute_combine. */
 int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
                 const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream);
 

@@ -130,6 +130,21 @@ def test_forward_token_sweep(T):
     assert err <= W4A8_BAR
 
 
+@pytest.mark.parametrize("case", list(SMALL) + ["T1", "T16", "T256"])
+def test_forward_gather_in_gemm1_equals_separate_steps(case):
+    """the W4A8 forward reads the fp8 rows and their scales through row_src inside GEMM1 instead
+    of gathering x_perm first; its output must be bitwise what the separate entry points give"""
+    inp, d = small(case) if case in SMALL else sweep_case(int(case[1:]))
+    fused = bf16_host(d.forward())
+    idx, w = d.route()
+    offsets, row_src, slot_row, x_perm, x_perm_scale = d.permute(idx, canary=False)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    steps = bf16_host(d.combine(y, slot_row, w))
+    n_diff = int((fused != steps).sum())
+    print(f"[gpu w4a8] {case}: fused-gather forward vs separate steps, {n_diff} differing elements")
+    assert n_diff == 0
+
+
 def test_grouped_ffn_full_layer_sampled_rows():
     inp, d = sweep_case(256)
     cfg = inp["cfg"]

@@ -102,8 +102,11 @@ __device__ __forceinline__ int aslot(int r, int g) { return g ^ (r & 15); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct W4Args {
-    const uint8_t *A8;   // [S][K] fp8 activations, expert-contiguous rows
-    const float *As;     // [S][K/128] activation scales
+    const uint8_t *A8;   // [S][K] fp8 activations, expert-contiguous rows, or with row_src the
+                         // token rows [a_rows][K]
+    const float *As;     // [S][K/128] activation scales (with row_src: [a_rows][K/128])
+    const int32_t *row_src;  // NULL, or [S]: row r reads token row row_src[r] / gather_k
+    int gather_k, a_rows;
     const uint8_t *Wq;   // [E][N][K/2] e2m1 codes, low nibble = even k
     const uint8_t *Wbs;  // [E][N][K/16] e4m3 block scales
     const float *Wgs;    // [E] global scales
@@ -171,17 +174,40 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
 
     // ---- activations: thread t stages granule t % 16 of token rows t / 16 + 16 i, and thread
     // r < 32 NTB the chunk's two activation scales of token row r.  Raw buffer resources
-    // bound the reads to the tile's live rows (rows past them read as zero), so every lane
-    // issues the same unconditional loads and the compiler's wait counts stay exact.
+    // bound the reads (rows past the tile's live rows read as zero), so every lane issues the
+    // same unconditional loads and the compiler's wait counts stay exact.  With row_src (the
+    // gather fused into GEMM1) a row is read from token row_src[r] / k of x; the row_src loads
+    // are issued now, unconditionally (a row past the tile reads the last live row's slot and
+    // gets an out-of-range offset), and consumed after the first weight chunk's loads.
     const int sg = tid & 15, sr = tid >> 4;
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.A8 + (int64_t)row_begin * K), (short)0, rows * K, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.As + (int64_t)row_begin * kb_n), (short)0, rows * kb_n * 4, 0x00020000);
-    uint32_t aoff[NTB * 2];
+    const bool gather = g.row_src != nullptr;
+    const int srow = min(tid, kBM - 1);
+    int src[NTB * 2 + 1] = {};
+    if (gather) {
 #pragma unroll
-    for (int i = 0; i < NTB * 2; ++i) aoff[i] = (uint32_t)((sr + 16 * i) * K + sg * 16);
-    const uint32_t soff = (uint32_t)(min(tid, kBM - 1) * kb_n * 4);
+        for (int i = 0; i < NTB * 2; ++i) src[i] = g.row_src[row_begin + min(sr + 16 * i, rows - 1)];
+        src[NTB * 2] = g.row_src[row_begin + min(srow, rows - 1)];
+    }
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.A8 + (gather ? 0 : (int64_t)row_begin * K)), (short)0, gather ? g.a_rows * K : rows * K,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(g.As + (gather ? 0 : (int64_t)row_begin * kb_n)), (short)0,
+        (gather ? g.a_rows : rows) * kb_n * 4, 0x00020000);
+    uint32_t aoff[NTB * 2], soff;
+    auto init_aoff = [&]() {
+        // token of slot s = t*k + j: s / k in double precision, exact for integers below 2^31
+#pragma unroll
+        for (int i = 0; i < NTB * 2 + 1; ++i) asm volatile("" : "+v"(src[i])::"memory");
+#pragma unroll
+        for (int i = 0; i < NTB * 2; ++i) {
+            const int r = sr + 16 * i;
+            const int t = (int)((double)src[i] / (double)g.gather_k);
+            aoff[i] = !gather ? (uint32_t)(r * K + sg * 16) : r >= rows ? 0x80000000u : (uint32_t)(t * K + sg * 16);
+        }
+        const int ts = (int)((double)src[NTB * 2] / (double)g.gather_k);
+        soff = !gather ? (uint32_t)(srow * kb_n * 4) : srow >= rows ? 0x80000000u : (uint32_t)(ts * kb_n * 4);
+    };
     u32x4 ar[NTB * 2];
     u32x2 ars;
     auto load_a = [&](int c) {
@@ -260,9 +286,11 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     // set), so the loads in flight at the loop head follow the same pattern on entry as on
     // the back edge and the compiler's waits there stay exact.
     WChunk w[kNBuf];
+    load_w(w[0], 0);
+    init_aoff();  // the row_src loads land under the first weight chunk's
     load_a(0);
 #pragma unroll
-    for (int c = 0; c < kNBuf - 2; ++c) load_w(w[c], min(c, nc - 1));
+    for (int c = 1; c < kNBuf - 2; ++c) load_w(w[c], min(c, nc - 1));
     store_a(0);
     load_a(min(1, nc - 1));
     load_w(w[kNBuf - 2], min(kNBuf - 2, nc - 1));
@@ -421,13 +449,14 @@ hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *offsets,
-                                   const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles,
-                                   const moe_weights &w, const moe_problem &p, float *h32, uint8_t *h8, float *hs,
-                                   uint16_t *y_perm, hipStream_t s) {
+hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
+                                   const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
+                                   int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
+                                   uint8_t *h8, float *hs, uint16_t *y_perm, hipStream_t s) {
     const int H = p.H, I = p.I;
-    W4Args g1{x_perm, x_perm_scale, (const uint8_t *)w.w1, (const uint8_t *)w.w1_bscale, w.w1_gscale,
-              H, 2 * I, I, p.glu_interleave, p.swiglu_clamp, h32, nullptr, 0};
+    if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
+    W4Args g1{x_perm, x_perm_scale, row_src, p.k, p.T, (const uint8_t *)w.w1, (const uint8_t *)w.w1_bscale,
+              w.w1_gscale, H, 2 * I, I, p.glu_interleave, p.swiglu_clamp, h32, nullptr, 0};
     hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<true>, dim3(max_tiles * (2 * I / kBN)), dim3(kThreads), 0, s, g1,
                        offsets, tiles, n_tiles);
     hipError_t err = hipGetLastError();
@@ -436,7 +465,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    W4Args g2{h8, hs, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale, w.w2_gscale,
+    W4Args g2{h8, hs, nullptr, 1, 0, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale, w.w2_gscale,
               I, H, I, 0, 0.0f, nullptr, y_perm, H};
     hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<false>, dim3(max_tiles * (H / kBN)), dim3(kThreads), 0, s, g2,
                        offsets, tiles, n_tiles);

@@ -74,10 +74,10 @@ WsLayout ws_layout(const moe_problem &p) {
     o = align256(o + S * 4);
     L.slot_row = o;
     o = align256(o + S * 4);
-    L.x_perm = o;  // the bf16 forward gathers inside GEMM1 and needs no x_perm
+    L.x_perm = o;  // the forward gathers inside GEMM1 where the offsets into x fit: no x_perm then
     if (!fused_gather(p)) o = align256(o + S * (size_t)p.H * act);
     L.x_perm_scale = o;
-    if (is_w4a8(&p)) o = align256(o + S * (size_t)(p.H / 128) * 4);
+    if (is_w4a8(&p) && !fused_gather(p)) o = align256(o + S * (size_t)(p.H / 128) * 4);
     L.y_perm = o;
     o = align256(o + S * (size_t)p.H * 2);
     L.forward_end = o;
@@ -111,9 +111,10 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
     int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), is_w4a8(&p), tiles, n_tiles, s));
     if (st) return st;
     if (is_w4a8(&p))
-        return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,
-                                                  max_tiles, w, p, (float *)(ws + L.h32), (uint8_t *)(ws + L.h),
-                                                  (float *)(ws + L.h_scale), (uint16_t *)y_perm, s));
+        return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, nullptr, offsets, tiles,
+                                                  n_tiles, max_tiles, w, p, (float *)(ws + L.h32),
+                                                  (uint8_t *)(ws + L.h), (float *)(ws + L.h_scale),
+                                                  (uint16_t *)y_perm, s));
     uint16_t *h = (uint16_t *)(ws + L.h);
     st = hip_status(launch_gemm1_swiglu_bf16((const uint16_t *)x_perm, (const uint16_t *)w.w1, offsets, tiles,
                                              n_tiles, max_tiles, p.H, p.I, p.glu_interleave, p.swiglu_clamp, h, s));
@@ -176,7 +177,9 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
     if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s)))) return st;
     if ((st = mark(4))) return st;
     if (w4) {
-        if ((st = hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, offsets, tiles, n_tiles,
+        const uint8_t *a8 = fused ? (const uint8_t *)x : (const uint8_t *)x_perm;
+        const float *as = fused ? x_scale : x_perm_scale;
+        if ((st = hip_status(launch_grouped_ffn_w4a8(a8, as, fused ? row_src : nullptr, offsets, tiles, n_tiles,
                                                      max_tiles, *w, *p, (float *)(b + L.h32), (uint8_t *)(b + L.h),
                                                      (float *)(b + L.h_scale), (uint16_t *)y_perm, s))))
             return st;

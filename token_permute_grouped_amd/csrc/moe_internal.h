@@ -75,8 +75,11 @@ hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, 
 // GEMM1 + SwiGLU reading its activation rows from the token rows x [T][H] through row_src
 // (the gather fused into the tile loads); needs gather_fits(T, H)
 inline bool gather_fits(int64_t T, int64_t H) { return T * H * 2 <= 0x7FFFFFFF; }
-// moe_forward (bf16) skips the separate row gather and runs GEMM1 on x through row_src
-inline bool fused_gather(const moe_problem &p) { return p.prec == MOE_PREC_BF16 && gather_fits(p.T, p.H); }
+inline bool gather_fits_fp8(int64_t T, int64_t H) { return T * H <= 0x7FFFFFFF; }
+// moe_forward skips the separate row gather and runs GEMM1 on x (and x_scale) through row_src
+inline bool fused_gather(const moe_problem &p) {
+    return p.prec == MOE_PREC_BF16 ? gather_fits(p.T, p.H) : gather_fits_fp8(p.T, p.H);
+}
 hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row_src, int T, int k,
                                            const uint16_t *w1, const int32_t *offsets, const int32_t *tiles,
                                            const int32_t *n_tiles, int64_t max_tiles, int H, int I,
@@ -86,10 +89,12 @@ hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
                              hipStream_t s);
 
-hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *offsets,
-                                   const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles,
-                                   const moe_weights &w, const moe_problem &p, float *h32, uint8_t *h8, float *hs,
-                                   uint16_t *y_perm, hipStream_t s);
+// row_src NULL: x_perm / x_perm_scale are the expert-ordered rows; else x / x_scale token rows
+// read through row_src (the gather fused into GEMM1; needs gather_fits_fp8(T, H))
+hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
+                                   const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
+                                   int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
+                                   uint8_t *h8, float *hs, uint16_t *y_perm, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,
                           uint16_t *out, hipStream_t s);
