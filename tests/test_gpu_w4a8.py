@@ -32,6 +32,10 @@ SMALL = {
                                      glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
     "w4_ragged_no_clamp": MoeConfig("w4_ragged_no_clamp", T=300, H=768, I=768, E=5, k=2, prec="w4a8"),
     "w4_tight_clamp": MoeConfig("w4_tight_clamp", T=90, H=512, I=256, E=4, k=2, prec="w4a8", swiglu_clamp=0.5),
+    # K a multiple of 1024 and T <= 32: the persistent GEMMs, ~1000 GEMM1 blocks over the grid (several
+    # tiles per workgroup, each next tile's first chunks prefetched), interleave-32 and dropped slots
+    "w4_persistent_il_drop": MoeConfig("w4_persistent_il_drop", T=32, H=1024, I=1024, E=64, k=8, prec="w4a8",
+                                       glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
 }
 
 

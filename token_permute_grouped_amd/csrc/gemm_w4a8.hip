@@ -41,6 +41,8 @@
 // layout is that of the 32 x 32 bf16 MFMA.  The weight fragment is the first
 // operand, so a lane's accumulators are runs of 4 consecutive output columns of
 // one token row.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace tpg {
@@ -106,11 +108,11 @@ struct W4Args {
                          // token rows [a_rows][K]
     const float *As;     // [S][K/128] activation scales (with row_src: [a_rows][K/128])
     const int32_t *row_src;  // NULL, or [S]: row r reads token row row_src[r] / gather_k
-    int gather_k, a_rows;
+    int gather_k, a_rows;    // rows of A8 / As: T with row_src, else S
     const uint8_t *Wq;   // [E][N][K/2] e2m1 codes, low nibble = even k
     const uint8_t *Wbs;  // [E][N][K/16] e4m3 block scales
     const float *Wgs;    // [E] global scales
-    int K, N, I, il;
+    int K, N, I, il, E;
     float clamp;
     float *Hout;         // GEMM1: h fp32 [S][I]
     uint16_t *Yout;      // GEMM2: y bf16 [S][ldy]
@@ -132,37 +134,130 @@ constexpr int kWRow = 144;
 constexpr int kWScales = 32 * kWRow;
 constexpr int kWSlot = kWScales + 32 * 16;  // 5120 bytes per chunk and wave
 
-template <bool kSwiGLU, int NTB>
-__device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin, int rows, int nt,
-                                          unsigned char *act, float *xsl, unsigned char *wlds, const u32x2 *lut) {
+// One work item of the block -> tile map: expert, first row, live rows, n-tile.
+struct W4Tile {
+    bool valid;
+    int e, row_begin, rows, nt;
+};
+
+// Virtual block v -> tile.  The tile list holds each expert's m-tiles together.  Expert e's
+// blocks are [first * nb_n, (first + nm) * nb_n); they run in units of G n-tiles, the nm
+// m-tiles of an n-tile G blocks apart: with G = 8 those land on one XCD (block b runs on XCD
+// b mod 8, and the persistent grid's stride is a multiple of 8) at the same time, so the
+// weights an expert's second m-tile streams are L2 hits.
+__device__ __forceinline__ W4Tile w4a8_tile_of(int v, int nb_n, const int32_t *__restrict__ offsets,
+                                              const int32_t *__restrict__ tiles, int n_mt) {
+    W4Tile t{};
+    const int tq = v / nb_n;  // a tile of the expert this block works for
+    t.valid = tq < n_mt;
+    if (!t.valid) return t;
+    t.e = tiles[2 * tq];
+    const int first = tq - tiles[2 * tq + 1] / kBM;
+    const int nm = (offsets[t.e + 1] - offsets[t.e] + kBM - 1) / kBM;
+    const int G = nb_n % 8 == 0 ? 8 : nb_n % 4 == 0 ? 4 : nb_n % 2 == 0 ? 2 : 1;
+    const int r = v - first * nb_n, unit = nm * G;
+    const int mt = first + (r % unit) / G;
+    t.nt = (r / unit) * G + (r % unit) % G;
+    t.row_begin = offsets[t.e] + tiles[2 * mt + 1];
+    t.rows = min(kBM, offsets[t.e + 1] - t.row_begin);
+    return t;
+}
+
+// The tiles of virtual blocks v0, v0 + stride, ... (kLoop), or of v0 alone.  With kLoop the
+// loads a tile's last steps would issue past its last chunk fetch the next tile's first
+// chunks instead, so the pipeline runs on across tiles and only the first tile pays for a
+// prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at the same
+// register set and buffer phase).
+template <bool kSwiGLU, int NTB, bool kLoop>
+__device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, const int32_t *__restrict__ offsets,
+                                           const int32_t *__restrict__ tiles, int n_mt, unsigned char *act,
+                                           float *xsl, unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, kb_n = K / 128;
     const int nc = K / kKC;
+    const int nb_n = g.N / kBN;
+    const int sg = tid & 15, sr = tid >> 4;
+    const int srow = min(tid, kBM - 1);
+    const bool gather = g.row_src != nullptr;
 
-    // ---- weights.  Each wave streams its own 32 rows, in chunks of 256 K (128 code bytes
-    // + 16 scale bytes per row): loads cover whole 128-byte lines (8 lanes per row), and the
-    // wave transposes each chunk through its own LDS slot into the MFMA operand layout.
-    auto weight_row = [&](int rl) {  // weight matrix row of row rl of this wave
-        if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
-            const bool up = wave >= 2;
-            const int c = nt * (kBN / 2) + (wave & 1) * 32 + rl;
-            return g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
-        }
-        return nt * kBN + wave * 32 + rl;
+    // ---- addressing of one tile.  Weights: each wave streams its own 32 rows, in chunks of
+    // 256 K (128 code bytes + 16 scale bytes per row); loads cover whole 128-byte lines (8 lanes
+    // per row), and the wave transposes each chunk through its own LDS slot into the MFMA
+    // operand layout.  Activations: thread t stages granule t % 16 of token rows t / 16 + 16 i,
+    // and thread r < 32 NTB the chunk's two activation scales of token row r.  Raw buffer
+    // resources bound every read (rows past the tile's live rows read as zero), so every lane
+    // issues the same unconditional loads and the compiler's wait counts stay exact.  With
+    // row_src (the gather fused into GEMM1) row r is read from token row_src[r] / k of x: the
+    // row_src loads are issued first, unconditionally (a row past the tile reads the last live
+    // row's slot and gets an out-of-range offset), and consumed later (finish()).
+    // Buffer descriptors: per tile (its expert's matrices, its rows), or with kLoop one set
+    // over the whole arrays for every tile (the host checks that all byte offsets fit 31 bits),
+    // so that a tile's addressing is just the per-lane offsets below.
+    struct Rs {
+        __amdgpu_buffer_rsrc_t W, Ws, A, S;
     };
-    const __amdgpu_buffer_rsrc_t rsW = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.Wq + (int64_t)e * g.N * (K / 2)), (short)0, g.N * (K / 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsWs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.Wbs + (int64_t)e * g.N * (K / 16)), (short)0, g.N * (K / 16), 0x00020000);
-    uint32_t woff[4];
+    auto make_rs = [&](const W4Tile &t) {
+        Rs r;
+        const int64_t w0 = kLoop ? 0 : (int64_t)t.e * g.N;  // first weight row the descriptor starts at
+        const int64_t nw = kLoop ? (int64_t)g.E * g.N : g.N;
+        r.W = __builtin_amdgcn_make_buffer_rsrc((void *)(g.Wq + w0 * (K / 2)), (short)0, (int)(nw * (K / 2)),
+                                                0x00020000);
+        r.Ws = __builtin_amdgcn_make_buffer_rsrc((void *)(g.Wbs + w0 * (K / 16)), (short)0, (int)(nw * (K / 16)),
+                                                 0x00020000);
+        const bool whole = gather || kLoop;  // rows addressed from the start of the array
+        const int64_t a0 = whole ? 0 : t.row_begin;
+        const int na = gather ? g.a_rows : kLoop ? g.a_rows : t.rows;
+        r.A = __builtin_amdgcn_make_buffer_rsrc((void *)(g.A8 + a0 * K), (short)0, na * K, 0x00020000);
+        r.S = __builtin_amdgcn_make_buffer_rsrc((void *)(g.As + a0 * kb_n), (short)0, na * kb_n * 4, 0x00020000);
+        return r;
+    };
+    struct Addr {
+        uint32_t woff[4], wsoff, aoff[NTB * 2], soff;
+        int src[NTB * 2 + 1];
+    };
+    auto start_addr = [&](Addr &a, const W4Tile &t) {
+        auto weight_row = [&](int rl) {  // weight matrix row of row rl of this wave
+            if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
+                const bool up = wave >= 2;
+                const int c = t.nt * (kBN / 2) + (wave & 1) * 32 + rl;
+                return g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
+            }
+            return t.nt * kBN + wave * 32 + rl;
+        };
+        const int er = kLoop ? t.e * g.N : 0;  // expert's first row within the descriptor
 #pragma unroll
-    for (int i = 0; i < 4; ++i) woff[i] = (uint32_t)(weight_row((lane >> 3) + 8 * i) * (K / 2) + (lane & 7) * 16);
-    const uint32_t wsoff = (uint32_t)(weight_row(lane >> 1) * (K / 16) + (lane & 1) * 8);
-    auto load_w = [&](WChunk &w, int c) {
+        for (int i = 0; i < 4; ++i)
+            a.woff[i] = (uint32_t)((er + weight_row((lane >> 3) + 8 * i)) * (K / 2) + (lane & 7) * 16);
+        a.wsoff = (uint32_t)((er + weight_row(lane >> 1)) * (K / 16) + (lane & 1) * 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rsW, woff[i], c * (kKC / 2), 0);
-        w.s = __builtin_amdgcn_raw_buffer_load_b64(rsWs, wsoff, c * (kKC / 16), 0);
+        for (int i = 0; i < NTB * 2 + 1; ++i) a.src[i] = 0;
+        if (gather) {
+#pragma unroll
+            for (int i = 0; i < NTB * 2; ++i) a.src[i] = g.row_src[t.row_begin + min(sr + 16 * i, t.rows - 1)];
+            a.src[NTB * 2] = g.row_src[t.row_begin + min(srow, t.rows - 1)];
+        }
+    };
+    auto finish_addr = [&](Addr &a, const W4Tile &t) {
+        // token of slot s = t*k + j: s / k in double precision, exact for integers below 2^31
+#pragma unroll
+        for (int i = 0; i < NTB * 2 + 1; ++i) asm volatile("" : "+v"(a.src[i])::"memory");
+        const int rb = kLoop ? t.row_begin : 0;  // tile's first row within the descriptor (no gather)
+#pragma unroll
+        for (int i = 0; i < NTB * 2; ++i) {
+            const int r = sr + 16 * i;
+            const int tok = (int)((double)a.src[i] / (double)g.gather_k);
+            a.aoff[i] = r >= t.rows ? 0x80000000u : (uint32_t)((gather ? tok : rb + r) * K + sg * 16);
+        }
+        const int ts = (int)((double)a.src[NTB * 2] / (double)g.gather_k);
+        a.soff = srow >= t.rows ? 0x80000000u : (uint32_t)((gather ? ts : rb + srow) * kb_n * 4);
+    };
+
+    Rs rs;
+    auto load_w = [&](WChunk &w, const Addr &a, int c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], c * (kKC / 2), 0);
+        w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * (kKC / 16), 0);
     };
     unsigned char *const wl = wlds + wave * (2 * kWSlot);  // this wave's two staging slots
     auto store_w = [&](const WChunk &w, int slot) {
@@ -171,49 +266,12 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
         for (int i = 0; i < 4; ++i) *(u32x4 *)(d + ((lane >> 3) + 8 * i) * kWRow + (lane & 7) * 16) = w.c[i];
         *(u32x2 *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 8) = w.s;
     };
-
-    // ---- activations: thread t stages granule t % 16 of token rows t / 16 + 16 i, and thread
-    // r < 32 NTB the chunk's two activation scales of token row r.  Raw buffer resources
-    // bound the reads (rows past the tile's live rows read as zero), so every lane issues the
-    // same unconditional loads and the compiler's wait counts stay exact.  With row_src (the
-    // gather fused into GEMM1) a row is read from token row_src[r] / k of x; the row_src loads
-    // are issued now, unconditionally (a row past the tile reads the last live row's slot and
-    // gets an out-of-range offset), and consumed after the first weight chunk's loads.
-    const int sg = tid & 15, sr = tid >> 4;
-    const bool gather = g.row_src != nullptr;
-    const int srow = min(tid, kBM - 1);
-    int src[NTB * 2 + 1] = {};
-    if (gather) {
-#pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) src[i] = g.row_src[row_begin + min(sr + 16 * i, rows - 1)];
-        src[NTB * 2] = g.row_src[row_begin + min(srow, rows - 1)];
-    }
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.A8 + (gather ? 0 : (int64_t)row_begin * K)), (short)0, gather ? g.a_rows * K : rows * K,
-        0x00020000);
-    const __amdgpu_buffer_rsrc_t rsS = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(g.As + (gather ? 0 : (int64_t)row_begin * kb_n)), (short)0,
-        (gather ? g.a_rows : rows) * kb_n * 4, 0x00020000);
-    uint32_t aoff[NTB * 2], soff;
-    auto init_aoff = [&]() {
-        // token of slot s = t*k + j: s / k in double precision, exact for integers below 2^31
-#pragma unroll
-        for (int i = 0; i < NTB * 2 + 1; ++i) asm volatile("" : "+v"(src[i])::"memory");
-#pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) {
-            const int r = sr + 16 * i;
-            const int t = (int)((double)src[i] / (double)g.gather_k);
-            aoff[i] = !gather ? (uint32_t)(r * K + sg * 16) : r >= rows ? 0x80000000u : (uint32_t)(t * K + sg * 16);
-        }
-        const int ts = (int)((double)src[NTB * 2] / (double)g.gather_k);
-        soff = !gather ? (uint32_t)(srow * kb_n * 4) : srow >= rows ? 0x80000000u : (uint32_t)(ts * kb_n * 4);
-    };
     u32x4 ar[NTB * 2];
     u32x2 ars;
-    auto load_a = [&](int c) {
+    auto load_a = [&](const Addr &a, int c) {
 #pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, aoff[i], c * kKC, 0);
-        ars = __builtin_amdgcn_raw_buffer_load_b64(rsS, soff, c * 8, 0);
+        for (int i = 0; i < NTB * 2; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, a.aoff[i], c * kKC, 0);
+        ars = __builtin_amdgcn_raw_buffer_load_b64(rs.S, a.soff, c * 8, 0);
     };
     auto store_a = [&](int buf) {
         unsigned char *dst = act + buf * kActBuf;
@@ -226,10 +284,6 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
     };
 
     f32x16 acc[NTB];
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[tb][v] = 0.f;
 
     // lane (row r = l % 32, half h = l / 32) of 64-K step (q, t) takes code bytes
     // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
@@ -277,135 +331,169 @@ __device__ __forceinline__ void w4a8_tile(const W4Args &g, int e, int row_begin,
         }
     };
 
-    // ---- main loop.  Chunk c computes from weight set c % 4 and activation buffer c % 2,
-    // then writes the staged activations of chunk c + 1 into the other buffer (last read
-    // by chunk c - 1, before the previous barrier), loads the activations of chunk c + 2
-    // and the weights of chunk c + 3 (into the set of chunk c - 1).  Requests past the
-    // last chunk repeat it (cache hits), so every path issues the same loads.
-    // The prologue ends like a loop step (activations of the next chunk, then one weight
-    // set), so the loads in flight at the loop head follow the same pattern on entry as on
-    // the back edge and the compiler's waits there stay exact.
-    WChunk w[kNBuf];
-    load_w(w[0], 0);
-    init_aoff();  // the row_src loads land under the first weight chunk's
-    load_a(0);
+    // ---- epilogue of tile t.  xch: LDS the up waves hand their accumulators to the gate waves
+    // through (an activation buffer no chunk still needs).
+    auto epilogue = [&](const W4Tile &t, float *xch) {
+        const float gs = g.Wgs[t.e];
+        if (kSwiGLU) {
+            if (wave >= 2)
 #pragma unroll
-    for (int c = 1; c < kNBuf - 2; ++c) load_w(w[c], min(c, nc - 1));
-    store_a(0);
-    load_a(min(1, nc - 1));
-    load_w(w[kNBuf - 2], min(kNBuf - 2, nc - 1));
-    store_w(w[0], 0);
-    lds_barrier();  // chunk 0 staged, scale table built
-    // Chunk c computes from activation buffer c % 2 and this wave's weight slot c % 2, then
-    // stages the weights of chunk c + 1 (set (c + 1) % 4, loaded two steps ago) into the other
-    // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
-    // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
-    // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
-    // c + kNBuf - 1 (into the set of chunk c - 1).  Requests past the last chunk repeat it.
-    // Whole groups of four steps: a step past the last chunk skips only its compute (which
-    // issues no memory loads), so every path through the loop issues the same loads and
-    // the compiler's waits at the loop head see the regular pattern.
-    for (int c0 = 0; c0 < nc; c0 += kNBuf) {
+                for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-        for (int sidx = 0; sidx < kNBuf; ++sidx) {
-            const int c = c0 + sidx;
-            if (c < nc) compute(c & 1);
-            store_w(w[(sidx + 1) % kNBuf], (c + 1) & 1);
-            store_a((c + 1) & 1);
-            load_a(min(c + 2, nc - 1));
-            load_w(w[(sidx + kNBuf - 1) % kNBuf], min(c + kNBuf - 1, nc - 1));
+                    for (int v = 0; v < 16; ++v) xch[(((wave - 2) * NTB + tb) * 16 + v) * 64 + lane] = acc[tb][v];
             lds_barrier();
-        }
-    }
-
-    // ---- epilogue (every wave has passed the last chunk's barrier: the buffers are free)
-    const float gs = g.Wgs[e];
-    if (kSwiGLU) {
-        // the up waves hand their accumulators to the gate waves through LDS
-        float *xch = (float *)act;  // [2 waves][NTB][16][64]
-        if (wave >= 2)
+            if (wave < 2) {
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
+                for (int tb = 0; tb < NTB; ++tb) {
+                    const int tok = tb * 32 + (lane & 31);
+                    if (tok >= t.rows) continue;
+                    float *hrow = g.Hout + (int64_t)(t.row_begin + tok) * g.I;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) xch[(((wave - 2) * NTB + tb) * 16 + v) * 64 + lane] = acc[tb][v];
-        lds_barrier();
-        if (wave < 2) {
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        const int c0 = t.nt * (kBN / 2) + wave * 32 + g4 * 8 + half * 4;
+                        f32x4 o;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int v = g4 * 4 + q;
+                            float gv = gs * acc[tb][v];
+                            float uv = gs * xch[((wave * NTB + tb) * 16 + v) * 64 + lane];
+                            if (g.clamp > 0.f) {
+                                gv = fminf(fmaxf(gv, -g.clamp), g.clamp);
+                                uv = fminf(fmaxf(uv, -g.clamp), g.clamp);
+                            }
+                            o[q] = gv / (1.0f + expf(-gv)) * uv;
+                        }
+                        *(f32x4 *)(hrow + c0) = o;
+                    }
+                }
+            }
+        } else {
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
                 const int tok = tb * 32 + (lane & 31);
-                if (tok >= rows) continue;
-                float *hrow = g.Hout + (int64_t)(row_begin + tok) * g.I;
+                if (tok >= t.rows) continue;
+                uint16_t *yrow = g.Yout + (int64_t)(t.row_begin + tok) * g.ldy;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = nt * (kBN / 2) + wave * 32 + g4 * 8 + half * 4;
-                    f32x4 o;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int v = g4 * 4 + q;
-                        float gv = gs * acc[tb][v];
-                        float uv = gs * xch[((wave * NTB + tb) * 16 + v) * 64 + lane];
-                        if (g.clamp > 0.f) {
-                            gv = fminf(fmaxf(gv, -g.clamp), g.clamp);
-                            uv = fminf(fmaxf(uv, -g.clamp), g.clamp);
-                        }
-                        o[q] = gv / (1.0f + expf(-gv)) * uv;
-                    }
-                    *(f32x4 *)(hrow + c0) = o;
+                    const int c0 = t.nt * kBN + wave * 32 + g4 * 8 + half * 4;
+                    u32x2 o;
+                    o.x = pack_bf16x2(gs * acc[tb][g4 * 4 + 0], gs * acc[tb][g4 * 4 + 1]);
+                    o.y = pack_bf16x2(gs * acc[tb][g4 * 4 + 2], gs * acc[tb][g4 * 4 + 3]);
+                    *(u32x2 *)(yrow + c0) = o;
                 }
             }
         }
-    } else {
+    };
+
+    W4Tile cur = w4a8_tile_of(v0, nb_n, offsets, tiles, n_mt);
+    if (!cur.valid) return;  // before any barrier: the whole workgroup leaves
+    rs = make_rs(cur);
+    Addr A;
+    start_addr(A, cur);
+
+    // ---- prologue (first tile only).  The row_src loads land under the first weight chunk's.
+    // It ends like a loop step (activations of the next chunk, then one weight set), so the
+    // loads in flight at the loop head follow the same pattern on entry as on the back edge
+    // and the compiler's waits there stay exact.
+    WChunk w[kNBuf];
+    load_w(w[0], A, 0);
+    finish_addr(A, cur);
+    load_a(A, 0);
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const int tok = tb * 32 + (lane & 31);
-            if (tok >= rows) continue;
-            uint16_t *yrow = g.Yout + (int64_t)(row_begin + tok) * g.ldy;
+    for (int c = 1; c < kNBuf - 2; ++c) load_w(w[c], A, min(c, nc - 1));
+    store_a(0);
+    load_a(A, min(1, nc - 1));
+    load_w(w[kNBuf - 2], A, min(kNBuf - 2, nc - 1));
+    store_w(w[0], 0);
+    lds_barrier();  // chunk 0 staged, scale table built
+
+    int v = v0;
+    for (;;) {
+        // the next tile's addressing (kLoop only; otherwise requests past the last chunk repeat
+        // it).  Its row_src loads are issued now and consumed at step 2, when every older load in
+        // flight is one this tile needs by then anyway; its first request comes at step nc - 2.
+        W4Tile nxt{};
+        Addr B = A;
+        if (kLoop) {
+            nxt = w4a8_tile_of(v + stride, nb_n, offsets, tiles, n_mt);
+            if (nxt.valid) start_addr(B, nxt);
+        }
+        const bool go_on = kLoop && nxt.valid;
+        // request c of this tile: chunk c below nc, else chunk c - nc of the next tile (or this
+        // tile's last chunk again)
+        auto req = [&](int c) { return c < nc ? c : go_on ? c - nc : nc - 1; };
 #pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int c0 = nt * kBN + wave * 32 + g4 * 8 + half * 4;
-                u32x2 o;
-                o.x = pack_bf16x2(gs * acc[tb][g4 * 4 + 0], gs * acc[tb][g4 * 4 + 1]);
-                o.y = pack_bf16x2(gs * acc[tb][g4 * 4 + 2], gs * acc[tb][g4 * 4 + 3]);
-                *(u32x2 *)(yrow + c0) = o;
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[tb][q] = 0.f;
+
+        // Chunk c computes from activation buffer c % 2 and this wave's weight slot c % 2, then
+        // stages the weights of chunk c + 1 (set (c + 1) % 4, loaded two steps ago) into the other
+        // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
+        // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
+        // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
+        // c + kNBuf - 1 (into the set of chunk c - 1).  Whole groups of four steps: a step past
+        // the last chunk (single-tile form with K / kKC not a multiple of four) skips only its
+        // compute (which issues no memory loads), so every path through the loop issues the same
+        // loads and the compiler's waits at the loop head see the regular pattern.
+        for (int c0 = 0; c0 < nc; c0 += kNBuf) {
+#pragma unroll
+            for (int sidx = 0; sidx < kNBuf; ++sidx) {
+                const int c = c0 + sidx;
+                if (kLoop && sidx == 2 && c0 == 0 && go_on) finish_addr(B, nxt);
+                if (c < nc) compute(c & 1);
+                store_w(w[(sidx + 1) % kNBuf], (c + 1) & 1);
+                store_a((c + 1) & 1);
+                const int ca = req(c + 2), cw = req(c + kNBuf - 1);
+                load_a(c + 2 < nc ? A : B, ca);
+                load_w(w[(sidx + kNBuf - 1) % kNBuf], c + kNBuf - 1 < nc ? A : B, cw);
+                lds_barrier();
             }
         }
+        // every wave has passed the last chunk's barrier; buffer nc % 2 holds the next tile's
+        // first chunk (kLoop: nc is even), so the exchange uses the other one
+        epilogue(cur, (float *)(act + ((nc + 1) & 1) * kActBuf));
+        if (!go_on) break;
+        lds_barrier();  // the exchange buffer is read before chunk 1 of the next tile is staged in it
+        cur = nxt;
+        A = B;
+        v += stride;
     }
 }
 
 }  // namespace
 
+#define TPG_W4A8_LDS                                                                                   \
+    __shared__ __attribute__((aligned(1024))) unsigned char act[2 * kActBuf];                          \
+    __shared__ u32x2 lut[256];                                                                         \
+    __shared__ float xsl[2 * kBM * 2]; /* activation scales of the staged chunks [buf][row][block] */ \
+    __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot]; /* 2 slots per wave */ \
+    lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after the first barrier of a tile */
+
+// one tile per workgroup; its token-block count from its own rows
 template <bool kSwiGLU>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
-    __shared__ __attribute__((aligned(1024))) unsigned char act[2 * kActBuf];
-    __shared__ u32x2 lut[256];
-    __shared__ float xsl[2 * kBM * 2];  // activation scales of the staged chunks [buf][row][block]
-    __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot];  // weight staging, 2 slots per wave
-
-    // Block -> tile.  The tile list holds each expert's m-tiles together.  Expert e's blocks are
-    // [first * nb_n, (first + nm) * nb_n); they run in units of G n-tiles, the nm m-tiles of an
-    // n-tile G blocks apart: with G = 8 those land on one XCD (block b runs on XCD b mod 8) at
-    // the same time, so the weights an expert's second m-tile streams are L2 hits.
-    const int nb_n = g.N / kBN;
-    const int tq = blockIdx.x / nb_n;  // a tile of the expert this block works for
-    if (tq >= n_tiles[0]) return;
-    const int e = tiles[2 * tq];
-    const int first = tq - tiles[2 * tq + 1] / kBM;
-    const int nm = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
-    const int G = nb_n % 8 == 0 ? 8 : nb_n % 4 == 0 ? 4 : nb_n % 2 == 0 ? 2 : 1;
-    const int r = blockIdx.x - first * nb_n, unit = nm * G;
-    const int mt = first + (r % unit) / G;
-    const int nt = (r / unit) * G + (r % unit) % G;
-    const int row_begin = offsets[e] + tiles[2 * mt + 1];
-    const int rows = min(kBM, offsets[e + 1] - row_begin);
-
-    lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x);  // read after the first barrier of the tile
-    if (rows > 32)
-        w4a8_tile<kSwiGLU, 2>(g, e, row_begin, rows, nt, act, xsl, wlds, lut);
+    TPG_W4A8_LDS
+    const int n_mt = n_tiles[0];
+    const W4Tile t = w4a8_tile_of(blockIdx.x, g.N / kBN, offsets, tiles, n_mt);
+    if (!t.valid) return;
+    if (t.rows > 32)
+        w4a8_tiles<kSwiGLU, 2, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
     else
-        w4a8_tile<kSwiGLU, 1>(g, e, row_begin, rows, nt, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, 1, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
 }
+
+// persistent (at most 32 rows per tile): workgroup b takes virtual blocks b, b + gridDim.x, ...
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kernel(
+    W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles) {
+    TPG_W4A8_LDS
+    w4a8_tiles<kSwiGLU, 1, true>(g, blockIdx.x, gridDim.x, offsets, tiles, n_tiles[0], act, xsl, wlds, lut);
+}
+#undef TPG_W4A8_LDS
 
 // h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows: one wave per
 // (row, 128 columns); s = amax / 448 (1 if that is 0), q = e4m3(h / s), decided in fp32.
@@ -449,26 +537,65 @@ hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s) {
     return hipGetLastError();
 }
 
+namespace {
+// Grid and mode of one W4A8 GEMM launch.  With T <= 32 (an expert holds at most T rows, so
+// every m-tile fits one 32-row block) and K / kKC a multiple of kNBuf the kernel is
+// persistent: two workgroups per CU (the kernel's occupancy) walk the virtual blocks with the
+// grid as stride and prefetch each next tile's first chunks under the current one's last
+// steps (W4A8 layer, T = 16: 223 -> 214 us per forward).  Above 32 tokens a persistent
+// kernel would have to fix two token blocks for every tile (most tiles then hold under 32
+// rows at T = 64) and measured slower; there and for other K, one tile per workgroup.
+struct W4Launch {
+    int64_t grid;
+    bool persistent;
+};
+W4Launch w4_launch(int64_t max_tiles, int N, int K, int E, int a_rows, int T) {
+    const int64_t blocks = max_tiles * (N / kBN);
+    // the persistent form addresses every expert's codes and every activation row from one
+    // descriptor each: their byte offsets must stay below 2^31
+    const bool fits = (int64_t)E * N * (K / 2) <= 0x7FFFFFFF && (int64_t)a_rows * K <= 0x7FFFFFFF;
+    if (T > 32 || (K / kKC) % kNBuf != 0 || !fits) return {blocks, false};
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                  hipSuccess || n_cu <= 0)
+        return {blocks, false};
+    return {std::min<int64_t>(blocks, 2 * (int64_t)n_cu), true};
+}
+
+template <bool kSwiGLU>
+void launch_w4a8_gemm(const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
+                      const int32_t *n_tiles, hipStream_t s) {
+    if (l.persistent)
+        hipLaunchKernelGGL(grouped_gemm_w4a8_persistent_kernel<kSwiGLU>, dim3(l.grid), dim3(kThreads), 0, s, g,
+                           offsets, tiles, n_tiles);
+    else
+        hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<kSwiGLU>, dim3(l.grid), dim3(kThreads), 0, s, g, offsets, tiles,
+                           n_tiles);
+}
+}  // namespace
+
 hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
                                    const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
                                    int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
                                    uint8_t *h8, float *hs, uint16_t *y_perm, hipStream_t s) {
     const int H = p.H, I = p.I;
     if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
-    W4Args g1{x_perm, x_perm_scale, row_src, p.k, p.T, (const uint8_t *)w.w1, (const uint8_t *)w.w1_bscale,
-              w.w1_gscale, H, 2 * I, I, p.glu_interleave, p.swiglu_clamp, h32, nullptr, 0};
-    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<true>, dim3(max_tiles * (2 * I / kBN)), dim3(kThreads), 0, s, g1,
-                       offsets, tiles, n_tiles);
+    const int S = (int)n_slots(p);
+    const W4Launch l1 = w4_launch(max_tiles, 2 * I, H, p.E, row_src ? p.T : S, p.T),
+                   l2 = w4_launch(max_tiles, H, I, p.E, S, p.T);
+    W4Args g1{x_perm, x_perm_scale, row_src, p.k, row_src ? p.T : S, (const uint8_t *)w.w1,
+              (const uint8_t *)w.w1_bscale, w.w1_gscale, H, 2 * I, I, p.glu_interleave, p.E, p.swiglu_clamp, h32,
+              nullptr, 0};
+    launch_w4a8_gemm<true>(l1, g1, offsets, tiles, n_tiles, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t items = n_slots(p) * (I / 128);
     hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    W4Args g2{h8, hs, nullptr, 1, 0, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale, w.w2_gscale,
-              I, H, I, 0, 0.0f, nullptr, y_perm, H};
-    hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<false>, dim3(max_tiles * (H / kBN)), dim3(kThreads), 0, s, g2,
-                       offsets, tiles, n_tiles);
+    W4Args g2{h8, hs, nullptr, 1, S, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale,
+              w.w2_gscale, I, H, I, 0, p.E, 0.0f, nullptr, y_perm, H};
+    launch_w4a8_gemm<false>(l2, g2, offsets, tiles, n_tiles, s);
     return hipGetLastError();
 }
 
