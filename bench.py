@@ -7,7 +7,9 @@ experts, top-8, bf16, router logits N(0,1) plus a per-expert bias ln(rank^-1.2)
 GEMM1 + SwiGLU, GEMM2, combine, with every input already resident in HBM.
 
 Timing: W untimed warm-up steps, then K moe_forward steps bracketed by device
-synchronisation and HIP events on the library's stream (ms_per_step, value).  The
+synchronisation and HIP events on the library's stream (ms_per_step, value).  Then K
+single forwards, each after a 512 MB write that flushes the caches (median:
+cold_cache_ms_per_step).  The
 per-stage durations come from K further steps through moe_forward_timed (same
 kernels plus a HIP event at every stage boundary), measured live in the same run.
 On bf16 data the forward folds the row gather into GEMM1; the permute kernel's own
@@ -230,6 +232,24 @@ def main():
     hip.destroy(e1)
     log(f"timed {args.steps} steps: {step_ms:.4f} ms/step (events), {wall_ms:.4f} ms/step (wall)")
 
+    # cold caches: before each of K single forwards, overwrite a 512 MB buffer (evicts the L2s
+    # and the 256 MB last-level cache), then time the forward alone between HIP events; median
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        c0, c1 = hip.create(), hip.create()
+        hip.record(c0, stream)
+        step()
+        hip.record(c1, stream)
+        torch.cuda.synchronize()
+        cold.append(hip.ms(c0, c1))
+        hip.destroy(c0)
+        hip.destroy(c1)
+    del flush
+    cold_ms = float(np.median(cold))
+    log(f"cold caches: median {cold_ms:.4f} ms per forward over {args.steps}")
+
     # stage breakdown: K more steps through moe_forward_timed (same kernels plus a HIP event at
     # every stage boundary; each event adds a few microseconds, visible only at small T)
     evs = [[hip.create() for _ in range(tpg.MOE_N_STAGE_EVENTS)] for _ in range(args.steps)]
@@ -353,6 +373,7 @@ def main():
         "combine_hbm_frac": round(gbs(combine_bytes, stage_ms["combine"]) / PEAK_HBM_GBS, 4),
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "wall_ms_per_step": round(wall_ms, 4),
+        "cold_cache_ms_per_step": round(cold_ms, 4),  # median, caches flushed before each forward
         "roofline": roofline,
         "cpu_baseline": None,
     }
