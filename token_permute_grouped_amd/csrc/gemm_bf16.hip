@@ -83,6 +83,14 @@ constexpr int kBBase = 2 * kAStage;                    // weights follow the two
 constexpr int kLoads = kBM * kRowBytes / 16 / kThreads;  // 16-byte activation loads per thread (4)
 constexpr int kOpsB = kBStage / 1024 / kWaves;         // 1 KB weight DMAs per wave per stage (4)
 constexpr int kLRows = kThreads / 8;                   // tile rows one activation load covers (64)
+// Sparse tiles (at most 64 live rows): activation stages of 64 rows (8 KB, one load per thread)
+// leave room for a fourth weight slot, so the weights are requested three stages ahead.
+constexpr int kSpRows = 64;
+constexpr int kAStageSp = kSpRows * kRowBytes;        // 8 KB
+constexpr int kBBaseSp = 2 * kAStageSp;               // 16 KB
+constexpr int kBStagesSp = 4;
+static_assert(kBBaseSp + kBStagesSp * kBStage <= kBBase + kBStages * kBStage, "sparse layout fits the LDS");
+static_assert(kSpRows == kLRows, "a sparse stage is the first activation load of every thread");
 
 // Workgroup -> tile map.  Workgroup b runs on XCD b % 8.  Bands of tm.gm m-tiles take
 // tm.per_band workgroups each; a band is cut into 8 rectangles (xm rows of m-tiles x xn
@@ -253,17 +261,20 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int wofs = lrow * kRowBytes + slot(lrow, lkc) * 16;
 
     u32x4 RA0[kLoads], RA1[kLoads];
-    auto gloadA = [&](u32x4 *R, int kt) {
+    // NL: activation loads per thread (kLoads, or 1 for sparse tiles); AS / BB: LDS bytes of an
+    // activation stage / offset of the weight ring
+    auto gloadA = [&](u32x4 *R, int kt, auto nl_tag) {
+        constexpr int NL = decltype(nl_tag)::value;
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) R[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[i], kt * kRowBytes, 0);
+        for (int i = 0; i < NL; ++i) R[i] = __builtin_amdgcn_raw_buffer_load_b128(rsA, offA[i], kt * kRowBytes, 0);
     };
-    auto lwriteA = [&](const u32x4 *R, int astage, int i0, int n) {
-        unsigned char *base = lds + astage * kAStage + wofs;
+    auto lwriteA = [&](const u32x4 *R, int astage, int i0, int n, int AS) {
+        unsigned char *base = lds + astage * AS + wofs;
 #pragma unroll
         for (int i = i0; i < i0 + n; ++i) *(u32x4 *)(base + i * kLRows * kRowBytes) = R[i];
     };
-    auto dmaB = [&](int kt, int bstage, int i0 = 0, int n = kOpsB) {
-        unsigned char *dst = lds + kBBase + bstage * kBStage + wave * (kBN / kWaves) * kRowBytes;
+    auto dmaB = [&](int kt, int bstage, int i0, int n, int BB) {
+        unsigned char *dst = lds + BB + bstage * kBStage + wave * (kBN / kWaves) * kRowBytes;
 #pragma unroll
         for (int i = i0; i < i0 + n; ++i) dma16(rsB, offB[i], kt * kRowBytes, dst + i * 1024);
     };
@@ -281,15 +292,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int fr = lane & 31, fk = lane >> 5;
     const int nk = K / kBK;  // even: K is a multiple of 128
 
-    auto mainloop = [&](auto nb_tag) {
+    auto mainloop = [&](auto nb_tag, auto sp_tag) {
         constexpr int NB = decltype(nb_tag)::value;
+        constexpr bool kSp = decltype(sp_tag)::value;  // sparse tile: at most 64 live rows
         constexpr int NR = 2 + NB;  // fragment reads per K step
         constexpr int NM = 2 * NB;  // MFMAs per K step
+        constexpr int NL = kSp ? 1 : kLoads;            // activation loads per thread and stage
+        constexpr int AS = kSp ? kAStageSp : kAStage;
+        constexpr int BB = kSp ? kBBaseSp : kBBase;
+        constexpr int NBS = kSp ? kBStagesSp : kBStages;
+        constexpr int LA = kSp ? 3 : 2;                 // weight DMA lookahead in stages
+        using NLt = std::integral_constant<int, NL>;
         bf16x8 fw[2][2], fx[2][NB > 0 ? NB : 1];
         auto load = [&](int buf, int astage, int bstage, int ks) {
             if constexpr (NB > 0) {
-                const u32x4 *sa = (const u32x4 *)(lds + astage * kAStage);
-                const u32x4 *sb = (const u32x4 *)(lds + kBBase + bstage * kBStage);
+                const u32x4 *sa = (const u32x4 *)(lds + astage * AS);
+                const u32x4 *sb = (const u32x4 *)(lds + BB + bstage * kBStage);
                 const int kc = ks * 2 + fk;
 #pragma unroll
                 for (int a = 0; a < 2; ++a) {
@@ -311,53 +329,61 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[buf][a], fx[buf][b], acc[a][b], 0, 0, 0);
         };
 
-        // One stage kt: activations in LDS buffer kt & 1 (P), weights in ring slot bs = kt % 3;
+        // One stage kt: activations in LDS buffer kt & 1 (P), weights in ring slot bs = kt % NBS;
         // its step-0 fragments are already in fw/fx[0].  Issue order per stage (all VMEM, in
-        // order): weight DMA of kt+2 at the top, activation loads of kt+3 at step 2.  The weights
-        // of kt+1 (DMA issued one stage earlier) must have landed before the barrier; 24 younger
-        // VMEM ops (activations kt+2, weights kt+2, activations kt+3) may still be in flight.
+        // order): weight DMA of kt+LA at the top, activation loads of kt+3 at step 2.  The weights
+        // of kt+1 (DMA issued LA-1 stages earlier) must have landed before the barrier; the VMEM
+        // ops issued after them may still be in flight: dense tiles (LA 2) activations kt+2,
+        // weights kt+2, activations kt+3; sparse tiles (LA 3) activations kt+1, weights and
+        // activations kt+2, weights and activations kt+3, each where that stage exists.
         // kIssue: stages kt+2 (weights) and kt+3 (activations) exist; kNext: stage kt+1 exists.
         auto step = [&](auto p_tag, auto next_tag, auto issue_tag, int kt, int bs) {
             constexpr int P = decltype(p_tag)::value;
             constexpr bool kNext = decltype(next_tag)::value;
             constexpr bool kIssue = decltype(issue_tag)::value;
             u32x4 *Rn = P == 0 ? RA1 : RA0;  // holds the activations of stage kt+1
-            const int bs1 = bs + 1 == kBStages ? 0 : bs + 1;
-            const int bs2 = bs1 + 1 == kBStages ? 0 : bs1 + 1;
-            if constexpr (kIssue) {
-                dmaB(kt + 2, bs2, 0, kOpsB / 2);
+            const int bs1 = bs + 1 == NBS ? 0 : bs + 1;
+            const int bsl = (bs + LA) % NBS;  // slot of the stage the DMA requests
+            const bool issue_w = kIssue && (!kSp || kt + 3 < nk);
+            if (issue_w) {
+                dmaB(kt + LA, bsl, 0, kOpsB / 2, BB);
                 __builtin_amdgcn_sched_group_barrier(0x020, kOpsB / 2, 0);
             }
             // K steps 0 and 1: fragments of the next step under the MFMAs, and the activations
-            // of stage kt+1 into the free LDS buffer, half under each step
-            if constexpr (kNext) lwriteA(Rn, P ^ 1, 0, kLoads / 2);
+            // of stage kt+1 into the free LDS buffer, half under each step (sparse: one write)
+            if constexpr (kNext) lwriteA(Rn, P ^ 1, 0, kSp ? 1 : kLoads / 2, AS);
             load(1, P, bs, 1);
             mfmas(0);
             if constexpr (NB > 0) {
-                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
+                if constexpr (kNext) interleave_x_ds_mfma<0x200, kSp ? 1 : kLoads / 2, NR, NM>();
                 else interleave_ds_mfma<NR, NM>();
             }
-            if constexpr (kIssue) {
-                dmaB(kt + 2, bs2, kOpsB / 2, kOpsB / 2);
+            if (issue_w) {
+                dmaB(kt + LA, bsl, kOpsB / 2, kOpsB / 2, BB);
                 __builtin_amdgcn_sched_group_barrier(0x020, kOpsB / 2, 0);
             }
-            if constexpr (kNext) lwriteA(Rn, P ^ 1, kLoads / 2, kLoads / 2);
+            if constexpr (kNext && !kSp) lwriteA(Rn, P ^ 1, kLoads / 2, kLoads / 2, AS);
             load(0, P, bs, 2);
             mfmas(1);
             if constexpr (NB > 0) {
-                if constexpr (kNext) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
+                if constexpr (kNext && !kSp) interleave_x_ds_mfma<0x200, kLoads / 2, NR, NM>();
                 else interleave_ds_mfma<NR, NM>();
             }
             // K step 2: refill the register set with the activations of stage kt+3
             if constexpr (kIssue) {
-                if (kt + 3 < nk) gloadA(Rn, kt + 3);
+                if (kt + 3 < nk) gloadA(Rn, kt + 3, NLt{});
             }
             load(1, P, bs, 3);
             mfmas(0);
             if constexpr (NB > 0) interleave_ds_mfma<NR, NM>();
             // K step 3: publish stage kt+1 and load its first fragments under the last MFMAs
             if constexpr (kNext) {
-                if constexpr (kIssue) {
+                if constexpr (kSp) {
+                    constexpr int G = kOpsB + 1;  // weights + activations of one stage
+                    if (kt + 3 < nk) wait_vmcnt<1 + 2 * G>();
+                    else if (kt + 2 < nk) wait_vmcnt<1 + G>();
+                    else wait_vmcnt<1>();
+                } else if constexpr (kIssue) {
                     if (kt + 3 < nk) wait_vmcnt<2 * kLoads + kOpsB>();  // activations kt+2, kt+3; weights kt+2
                     else wait_vmcnt<kLoads + kOpsB>();                 // no activations kt+3 were issued
                 } else {
@@ -374,24 +400,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         using Y = std::true_type;
         using F = std::false_type;
 
-        // prologue: stage 0 (weights, activations), then stage 1, in issue order; activations
-        // of 0 written, activations of 2 in flight.  The barrier waits for stage 0 only: the
-        // weights of stage 1 land by the end of stage 0 like every later stage.
-        dmaB(0, 0);
+        // prologue: stage 0 (weights, activations), then stage 1 (sparse: and the weights of
+        // stage 2), in issue order; activations of 0 written, activations of 2 in flight.  The
+        // barrier waits for stage 0 only: the later stages land like every later stage.
+        dmaB(0, 0, 0, kOpsB, BB);
         asm volatile("" ::: "memory");  // keep the issue order: loads complete in it
         init_offA();
-        gloadA(RA0, 0);
+        gloadA(RA0, 0, NLt{});
         asm volatile("" ::: "memory");
-        dmaB(1, 1);
+        dmaB(1, 1, 0, kOpsB, BB);
         asm volatile("" ::: "memory");
-        gloadA(RA1, 1);
+        gloadA(RA1, 1, NLt{});
         asm volatile("" ::: "memory");
-        lwriteA(RA0, 0, 0, kLoads);
+        if constexpr (kSp) {
+            if (nk > 2) dmaB(2, 2, 0, kOpsB, BB);
+            asm volatile("" ::: "memory");
+        }
+        lwriteA(RA0, 0, 0, NL, AS);
         if (nk > 2) {
-            gloadA(RA0, 2);
-            wait_vmcnt<kOpsB + 2 * kLoads>();  // weights 1, activations 1 and 2 may be in flight
+            gloadA(RA0, 2, NLt{});
+            // dense: weights 1, activations 1 and 2 may be in flight; sparse: also weights 2
+            wait_vmcnt<(kSp ? 2 : 1) * kOpsB + 2 * NL>();
         } else {
-            wait_vmcnt<kOpsB + kLoads>();
+            wait_vmcnt<kOpsB + NL>();
         }
         lds_barrier();
         load(0, 0, 0, 0);
@@ -399,21 +430,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         int kt = 0;
         for (; kt + 2 < nk; kt += 2) {  // both stages of the pair issue (weights kt+2, kt+3 exist)
             step(T0{}, Y{}, Y{}, kt, bs);
-            bs = bs + 1 == kBStages ? 0 : bs + 1;
+            bs = bs + 1 == NBS ? 0 : bs + 1;
             step(T1{}, Y{}, Y{}, kt + 1, bs);
-            bs = bs + 1 == kBStages ? 0 : bs + 1;
+            bs = bs + 1 == NBS ? 0 : bs + 1;
         }
         // last pair: stage nk-2 has a next stage but nothing to issue; nk-1 is the last
         step(T0{}, Y{}, F{}, nk - 2, bs);
-        bs = bs + 1 == kBStages ? 0 : bs + 1;
+        bs = bs + 1 == NBS ? 0 : bs + 1;
         step(T1{}, F{}, F{}, nk - 1, bs);
     };
-    switch (nb_live) {
-        case 4: mainloop(std::integral_constant<int, 4>{}); break;
-        case 3: mainloop(std::integral_constant<int, 3>{}); break;
-        case 2: mainloop(std::integral_constant<int, 2>{}); break;
-        case 1: mainloop(std::integral_constant<int, 1>{}); break;
-        default: mainloop(std::integral_constant<int, 0>{}); break;
+    using Dense = std::false_type;
+    using Sparse = std::true_type;
+    if (rows <= kSpRows) {  // wm = 0 waves hold at most two live 32-row blocks, wm = 1 none
+        switch (nb_live) {
+            case 2: mainloop(std::integral_constant<int, 2>{}, Sparse{}); break;
+            case 1: mainloop(std::integral_constant<int, 1>{}, Sparse{}); break;
+            default: mainloop(std::integral_constant<int, 0>{}, Sparse{}); break;
+        }
+    } else {
+        switch (nb_live) {
+            case 4: mainloop(std::integral_constant<int, 4>{}, Dense{}); break;
+            case 3: mainloop(std::integral_constant<int, 3>{}, Dense{}); break;
+            case 2: mainloop(std::integral_constant<int, 2>{}, Dense{}); break;
+            case 1: mainloop(std::integral_constant<int, 1>{}, Dense{}); break;
+            default: mainloop(std::integral_constant<int, 0>{}, Dense{}); break;
+        }
     }
 
     // ---- epilogue: lane holds token row (lane & 31) of block b and weight rows
