@@ -154,7 +154,7 @@ def main():
                          "GEMMs' total rows and shapes, as a reference point for the MFMA fraction on this device")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
