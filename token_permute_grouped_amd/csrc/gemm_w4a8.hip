@@ -17,15 +17,19 @@
 // The GEMMs stream packed weights, which is what bounds them at small token counts.
 // Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows and
 // 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every token of the
-// tile.  Weights are never shared between waves, so each wave loads its rows straight
-// into registers in the MFMA operand layout (lane l: row l % 32, one contiguous
-// 32-code run per 64-wide K step) and dequantises them there.  K advances 256 per
-// chunk; weights are loaded three chunks ahead (four register sets).  Activations are
-// shared by the four waves: each chunk of the tile's token rows and its activation
-// scales are loaded into registers two chunks ahead and written to LDS one chunk
-// ahead (two buffers, swizzled).  Every load is an ordinary register load, so the
-// compiler's own waits are exact: no wait drains the weight prefetch, and the chunk
-// barriers carry no memory fence.
+// tile.  Weights are never shared between waves: each wave loads its rows with
+// line-coalesced loads (8 lanes per 128-byte line) three 256-wide K chunks ahead (four
+// register sets), transposes each chunk through its own LDS slot into the MFMA operand
+// layout (lane l: row l % 32, one contiguous 32-code run per 64-wide K step) and
+// dequantises it there.  Activations are shared by the four waves: each chunk of the
+// tile's token rows and its activation scales are loaded into registers two chunks
+// ahead and written to LDS one chunk ahead (two buffers, swizzled).  Every load is an
+// ordinary register load, so the compiler's own waits are exact: no wait drains the
+// weight prefetch, and the chunk barriers carry no memory fence.  In the forward the
+// first GEMM reads its rows straight from the token rows through row_src (the gather
+// folded into its loads).  With at most 32 tokens (and K a multiple of 1024) the
+// kernel is persistent: each workgroup walks several tiles and fetches the next one's
+// first chunks under the current one's last steps (w4a8_tiles, kLoop).
 // K is visited so that both halves of a 64-wide MFMA step lie in one 128-wide
 // activation-scale block; the partial sum of each block is added to the accumulator
 // times that block's activation scale (fp32), as the definition states.
