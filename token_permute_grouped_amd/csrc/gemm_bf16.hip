@@ -14,15 +14,19 @@
 // global memory; with one wave per SIMD (128 x 128 each) the same loop ran ~10%
 // slower.  Both operands are K-contiguous in HBM; K advances kBK = 64 per stage.
 //
-// Pipeline.  LDS holds two stages (128 KB).  Global loads go to registers first:
-// while the MFMAs of stage k run, the wave writes stage k+1 from its register set
-// into the free LDS buffer and refills the set with the loads of stage k+2, so a
-// load has about one stage of MFMAs to land.  The LDS writes of a stage (activation
-// stores and weight DMAs) are split over two K steps: a burst of them stalls the MFMA
-// issue.  Per stage there is one
-// barrier, taken before the last 16-wide K step so that the next stage's first
-// fragments load under that step's MFMAs and the MFMA issue does not drain.
-// Fragment reads of step s+1 are interleaved with the MFMAs of step s.
+// Pipeline.  LDS (160 KB) holds two activation stages of 32 KB and a ring of three
+// 32 KB weight stages.  Activations go global -> registers -> LDS: while the MFMAs of
+// stage k run, the wave writes stage k+1 from one of its two register sets into the
+// free LDS buffer and refills that set with the loads of stage k+3.  Weights go
+// straight to LDS by buffer-load DMA, requested two stages ahead.  The LDS writes of a
+// stage (activation stores and weight DMAs) are split over two K steps: a burst of
+// them stalls the MFMA issue.  Per stage there is one barrier, taken before the last
+// 16-wide K step so that the next stage's first fragments load under that step's
+// MFMAs and the MFMA issue does not drain.  Fragment reads of step s+1 are
+// interleaved with the MFMAs of step s.  Sparse tiles (at most 64 live rows) use a
+// second layout of the same LDS: 8 KB activation stages and a four-slot weight ring,
+// the weights requested three stages ahead (their arithmetic is small, the weight
+// stream is what they wait for).
 //
 // LDS layout.  A stage row is 64 bf16 = eight 16-byte chunks; chunk kc of row r sits
 // at slot kc ^ ((r & 7) ^ ((r >> 3) & 1)).  A fragment read (32 rows, one chunk)
@@ -31,7 +35,7 @@
 //
 // Operand order.  The weight fragment is the MFMA's first operand, so a lane's 16
 // accumulators of a block are 4 runs of 4 consecutive output columns of one token
-// row (8-byte bf16 stores).
+// row (8-byte bf16 writes into the epilogue's LDS staging of the output tile).
 //
 // SwiGLU fusion.  For GEMM1 an n-tile holds the weight rows of 128 output columns
 // c0..c0+127 ordered [gate 32 | up 32] x 4 (one pair per wave column), so gate and
