@@ -76,14 +76,17 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_file, kernel, launches_bytes_key="bytes_per_launch"):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the current source."""
+def measured_traffic(kernel_file, kernel, workload, seed, launches_bytes_key="bytes_per_launch"):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current source
+    and on this workload and seed (None otherwise)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh).get(kernel)
     if not rec or rec.get("source_sha") != source_hash([kernel_file]):
+        return None
+    if rec.get("workload") != workload or rec.get("seed") != seed:
         return None
     return rec.get(launches_bytes_key)
 
@@ -315,7 +318,8 @@ def main():
             "kernel": "grouped_gemm_bf16_kernel<true> (GEMM1 + SwiGLU)",
             "bound": "mfma", "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(g1 / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu"),
+            "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu",
+                                        cfg.name if args.tokens is None else None, args.seed),
             "algorithmic_per_launch": f"4*R*H*I = {gemm1_flops:.4g} flop (R={R} rows)",
         }
     else:

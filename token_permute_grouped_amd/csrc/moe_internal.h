@@ -104,13 +104,27 @@ hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s);
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN)
 // two floats -> two bf16 (round to nearest even) packed in one word, a in the low half: one
 // v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Streamed-out rows (written once, not read again by the kernel that writes them) are stored
+// through a buffer resource over the row with the sc1 cache-policy bit: a device-scope store,
+// written through the XCD's L2 rather than left there as a dirty line.  Measured on the row
+// gather and on the combine: equal or faster on every workload (the gather on a 101 MB output
+// 32 -> 18 us, the combine on the skewed layer 199 -> 190 us); the GEMM epilogues, whose
+// output tiles share the L2 with reused operands, measured slower with it and keep plain stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(void *row, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(row, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store16_through(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, const uint4 &v) {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int kSc1 = 16;  // cache-policy bits of a buffer store: sc0 = 1, nt = 2, sc1 = 16
+    __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){v.x, v.y, v.z, v.w}, r, byte_off, 0, kSc1);
 }
 
 }  // namespace tpg

@@ -5,7 +5,8 @@
 // token side: a wave reads a piece of x[t] once (16-byte loads, fully coalesced) and
 // writes it to each of the token's k destination rows, so HBM sees exactly T*H reads
 // and R*H writes, never a re-read of a token row.  On the W4A8 path the per-128 fp32
-// activation scales travel with their row.
+// activation scales travel with their row.  The destination rows are stored write-through
+// (device scope, see store16_through).
 #include "moe_internal.h"
 
 namespace tpg {
@@ -34,10 +35,10 @@ __global__ __launch_bounds__(256) void permute_kernel(const uint4 *__restrict__ 
         if (c0 + 64 * q < row_vec) v[q] = src[c0 + 64 * q];
     for (int j = 0; j < k; ++j) {
         if (rows[j] < 0) continue;
-        uint4 *dst = x_perm + (int64_t)rows[j] * row_vec;
+        const __amdgpu_buffer_rsrc_t dst = row_rsrc(x_perm + (int64_t)rows[j] * row_vec, row_vec * 16);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (c0 + 64 * q < row_vec) dst[c0 + 64 * q] = v[q];
+            if (c0 + 64 * q < row_vec) store16_through(dst, (c0 + 64 * q) * 16, v[q]);
     }
     if (blk == 0 && n_scale > 0) {
         for (int q = lane; q < n_scale; q += 64) {
