@@ -89,6 +89,28 @@ def test_route_ties_and_equal_logits():
     assert (w.cpu().numpy()[:8] == np.float32(1 / 8)).all()
 
 
+@pytest.mark.parametrize("E,k", [(200, 8), (256, 32), (3, 3), (130, 5), (64, 1)])
+def test_route_exact_order_on_ties_signed_zeros_and_denormals(E, k):
+    """selection is an exact comparison of the fp32 logits: ties (within and across lanes of a
+    wave) go to the lower id, -0 equals +0, subnormals keep their order"""
+    T = 120
+    rng = np.random.default_rng(E * 100 + k)
+    lg = rng.integers(-2, 3, size=(T, E)).astype(np.float32)          # many equal logits
+    lg[1::4] *= np.float32(1e-40)                                        # subnormals, +-0
+    sz = rng.random((T, E)) < 0.5
+    lg[2::4] = np.where(sz[2::4], np.float32(-0.0), np.float32(0.0))     # only signed zeros
+    lg[3::4] = np.where(sz[3::4], np.float32(-0.0), lg[3::4])            # zeros of both signs among ints
+    cfg = MoeConfig("ties_zero_denorm", T=T, H=128, I=128, E=E, k=k)
+    inp = {"cfg": cfg, "logits": lg, "x": np.zeros((T, cfg.H), np.uint16),
+           "w1": np.zeros((E, 2 * cfg.I, cfg.H), np.uint16), "w2": np.zeros((E, cfg.H, cfg.I), np.uint16)}
+    d = DeviceProblem(inp)
+    idx, w = d.route()
+    ref_idx, ref_w = oracle.route(lg, k)
+    assert (idx.cpu().numpy() == ref_idx).all()
+    assert np.abs(w.cpu().numpy().astype(np.float64) - ref_w).max() <= 2e-6
+    assert (idx.cpu().numpy()[2::4] == np.arange(k)).all()               # all-zero rows: ids 0..k-1
+
+
 # ----------------------------------------------------------------------------- permutation
 
 @pytest.mark.parametrize("name", _cases_all())

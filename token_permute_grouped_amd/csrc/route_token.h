@@ -8,73 +8,113 @@
 // logit.  The weight of slot j is exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k
 // chosen, which is the full softmax renormalised over the top k.
 //
-// Lane l holds experts l, l+64, l+128, l+192; each of the k rounds is a wave-wide argmax
-// (butterfly over 64 lanes); lane j keeps slot j.  If `ids` is not null, lane j < k also
-// stores the slot's expert id (or -1) at ids[j] (e.g. in LDS).
+// Lane l holds experts l, l+64, l+128, l+192.  Each of the k rounds is one wave-wide maximum
+// of a 32-bit key (the logit's bits mapped so that unsigned order is float order, -0 folded
+// onto +0) over DPP row operations, then a ballot of the lanes holding it; only equal logits in
+// several lanes take a second (minimum-id) reduction.  Every lane learns each round's winner,
+// so the normaliser is summed in slot order by every lane alike and lane j keeps slot j.  If
+// `ids` is not null, lane j < k also stores the slot's expert id (or -1) at ids[j] (e.g. in LDS).
 #pragma once
-
 #include "moe_internal.h"
 
 namespace tpg {
+namespace route_detail {
+
+// unsigned order of the key = numeric order of the (finite) float; -0 and +0 share a key; no
+// finite or infinite value maps to 0
+__device__ __forceinline__ uint32_t logit_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// DPP source of lane i: quad_perm / row_half_mirror / row_mirror stay within a row of 16 lanes;
+// row_bcast15 / row_bcast31 carry lane 15 / 31 into later rows (the rows row_mask enables).
+// Lanes with no source, and rows outside row_mask, keep `fill`.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp(uint32_t x, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, kCtrl, kRowMask, 0xf, false);
+}
+constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140,
+              kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// maximum of x over the 64 lanes, returned to every lane
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max(x, dpp<kQuadSwap1, 0xf>(x, 0u));
+    x = max(x, dpp<kQuadSwap2, 0xf>(x, 0u));
+    x = max(x, dpp<kRowHalfMirror, 0xf>(x, 0u));  // every lane: the maximum of its 8-lane half row
+    x = max(x, dpp<kRowMirror, 0xf>(x, 0u));      // every lane: the maximum of its 16-lane row
+    x = max(x, dpp<kRowBcast15, 0xa>(x, 0u));     // rows 1 and 3: rows 0-1 and 2-3
+    x = max(x, dpp<kRowBcast31, 0xc>(x, 0u));     // rows 2 and 3: rows 0-3 (lane 63)
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    x = min(x, dpp<kQuadSwap1, 0xf>(x, ~0u));
+    x = min(x, dpp<kQuadSwap2, 0xf>(x, ~0u));
+    x = min(x, dpp<kRowHalfMirror, 0xf>(x, ~0u));
+    x = min(x, dpp<kRowMirror, 0xf>(x, ~0u));
+    x = min(x, dpp<kRowBcast15, 0xa>(x, ~0u));
+    x = min(x, dpp<kRowBcast31, 0xc>(x, ~0u));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+}  // namespace route_detail
 
 __device__ __forceinline__ void route_token(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
                                             int64_t t, int E, int k, int lane, int32_t *__restrict__ topk_idx,
                                             float *__restrict__ topk_w, int32_t *ids) {
+    using namespace route_detail;
     const float *l = logits + t * E;
-    float v[4];
-    bool live[4];
+    uint32_t key[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        live[q] = e < E;
-        v[q] = live[q] ? l[e] : 0.0f;
+        key[q] = e < E ? logit_key(l[e]) : 0u;  // 0: no expert (or already taken)
     }
-
     int my_id = -1;
-    float my_logit = 0.0f, lmax = 0.0f;
+    float my_ex = 0.0f, lmax = 0.0f, z = 0.0f;
     for (int j = 0; j < k; ++j) {
-        // best remaining expert of this lane (ids grow with q, so strict '>' keeps the lower id)
-        float bv = 0.0f;
-        int bi = 0x7fffffff;
+        // this lane's best remaining expert: ids grow with q, so strict '>' keeps the lower id
+        uint32_t bk = 0u;
+        int bq = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (live[q] && (bi == 0x7fffffff || v[q] > bv)) {
-                bv = v[q];
-                bi = lane + 64 * q;
+            if (key[q] > bk) {
+                bk = key[q];
+                bq = q;
             }
-        // wave argmax: larger logit wins, equal logits -> lower id
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            const bool take = (oi != 0x7fffffff) && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
-            if (take) {
-                bv = ov;
-                bi = oi;
-            }
+        const uint32_t m = wave_max(bk);  // > 0: k <= E experts are live
+        const uint64_t holders = __ballot(bk == m);
+        int win;
+        if ((holders & (holders - 1)) == 0) {  // one lane holds the largest logit
+            const int wl = __builtin_ctzll(holders);
+            win = wl + 64 * __builtin_amdgcn_readlane(bq, wl);
+        } else {  // equal logits in several lanes: the lowest id among them
+            win = (int)wave_min(bk == m ? (uint32_t)(lane + 64 * bq) : ~0u);
         }
-        if ((bi & 63) == lane) {
+        if (lane == (win & 63)) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (bi == lane + 64 * q) live[q] = false;
+                if (q == (win >> 6)) key[q] = 0u;
         }
-        if (j == 0) lmax = bv;
+        const float lj = key_logit(m);
+        if (j == 0) lmax = lj;
+        // renormalised softmax weights: exp(l_j - l_max) summed over the chosen slots in order
+        const float ex = expf(lj - lmax);
+        z += ex;
         if (lane == j) {
-            my_id = bi;
-            my_logit = bv;
+            my_id = win;
+            my_ex = ex;
         }
     }
-
-    // renormalised softmax weights of the k chosen; every lane gets the same sum
-    float ex = lane < k ? expf(my_logit - lmax) : 0.0f;
-    float z = ex;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
     if (lane < k) {
         const int64_t s = t * k + lane;
         const bool dropped = slot_drop != nullptr && slot_drop[s] != 0;
         topk_idx[s] = dropped ? -1 : my_id;
-        topk_w[s] = ex / z;
+        topk_w[s] = my_ex / z;
         if (ids) ids[lane] = dropped ? -1 : my_id;
     }
 }
