@@ -93,7 +93,9 @@ int run_permute(const void *x, const float *x_scale, const int32_t *topk_idx, co
     int32_t *chunk_counts = (int32_t *)(ws + L.chunk_counts);
     auto mark = [&](int i) -> int { return ev ? hip_status(hipEventRecord((hipEvent_t)ev[i], s)) : MOE_OK; };
     int st = mark(0);
-    if (!st) st = hip_status(launch_tables(topk_idx, p.T, p.k, p.E, chunk_counts, offsets, row_src, slot_row, s));
+    if (!st)
+        st = hip_status(launch_tables(topk_idx, p.T, p.k, p.E, chunk_counts, offsets, row_src, slot_row, 0, 0, nullptr,
+                                      nullptr, s));
     if (!st) st = mark(1);
     if (!st)
         st = hip_status(launch_permute(x, is_w4a8(&p) ? x_scale : nullptr, slot_row, p.T, p.k, p.H,
@@ -165,8 +167,9 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         return st;
     }
     if ((st = mark(1))) return st;
-    if (!small &&
-        (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row, s))))
+    // the tables' scan launch also writes the GEMM tile list
+    if (!small && (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row,
+                                                 gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s))))
         return st;
     if ((st = mark(2))) return st;
     const bool fused = fused_gather(*p);
@@ -174,7 +177,6 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
                                                   x_perm, x_perm_scale, s))))
         return st;
     if ((st = mark(3))) return st;
-    if (!small && (st = hip_status(launch_build_tiles(offsets, p->E, gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s)))) return st;
     if ((st = mark(4))) return st;
     if (w4) {
         const uint8_t *a8 = fused ? (const uint8_t *)x : (const uint8_t *)x_perm;

@@ -53,7 +53,8 @@ hipError_t launch_route_topk(const float *logits, const uint8_t *slot_drop, int 
                              float *topk_w, hipStream_t s);
 
 hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *chunk_counts, int32_t *offsets,
-                         int32_t *row_src, int32_t *slot_row, hipStream_t s);
+                         int32_t *row_src, int32_t *slot_row, int bm, int by_expert, int32_t *tiles,
+                         int32_t *n_tiles, hipStream_t s);
 
 hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *slot_row, int T, int k, int H,
                           int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);

@@ -15,7 +15,7 @@
 // so the normaliser is summed in slot order by every lane alike and lane j keeps slot j.  If
 // `ids` is not null, lane j < k also stores the slot's expert id (or -1) at ids[j] (e.g. in LDS).
 #pragma once
-#include "moe_internal.h"
+#include "wave_ops.h"
 
 namespace tpg {
 namespace route_detail {
@@ -29,36 +29,6 @@ __device__ __forceinline__ uint32_t logit_key(float f) {
 }
 __device__ __forceinline__ float key_logit(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// DPP source of lane i: quad_perm / row_half_mirror / row_mirror stay within a row of 16 lanes;
-// row_bcast15 / row_bcast31 carry lane 15 / 31 into later rows (the rows row_mask enables).
-// Lanes with no source, and rows outside row_mask, keep `fill`.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp(uint32_t x, uint32_t fill) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, kCtrl, kRowMask, 0xf, false);
-}
-constexpr int kQuadSwap1 = 0xb1, kQuadSwap2 = 0x4e, kRowHalfMirror = 0x141, kRowMirror = 0x140,
-              kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-
-// maximum of x over the 64 lanes, returned to every lane
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-    x = max(x, dpp<kQuadSwap1, 0xf>(x, 0u));
-    x = max(x, dpp<kQuadSwap2, 0xf>(x, 0u));
-    x = max(x, dpp<kRowHalfMirror, 0xf>(x, 0u));  // every lane: the maximum of its 8-lane half row
-    x = max(x, dpp<kRowMirror, 0xf>(x, 0u));      // every lane: the maximum of its 16-lane row
-    x = max(x, dpp<kRowBcast15, 0xa>(x, 0u));     // rows 1 and 3: rows 0-1 and 2-3
-    x = max(x, dpp<kRowBcast31, 0xc>(x, 0u));     // rows 2 and 3: rows 0-3 (lane 63)
-    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-    x = min(x, dpp<kQuadSwap1, 0xf>(x, ~0u));
-    x = min(x, dpp<kQuadSwap2, 0xf>(x, ~0u));
-    x = min(x, dpp<kRowHalfMirror, 0xf>(x, ~0u));
-    x = min(x, dpp<kRowMirror, 0xf>(x, ~0u));
-    x = min(x, dpp<kRowBcast15, 0xa>(x, ~0u));
-    x = min(x, dpp<kRowBcast31, 0xc>(x, ~0u));
-    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 }  // namespace route_detail
@@ -86,14 +56,14 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, co
                 bk = key[q];
                 bq = q;
             }
-        const uint32_t m = wave_max(bk);  // > 0: k <= E experts are live
+        const uint32_t m = wave::max_u32(bk);  // > 0: k <= E experts are live
         const uint64_t holders = __ballot(bk == m);
         int win;
         if ((holders & (holders - 1)) == 0) {  // one lane holds the largest logit
             const int wl = __builtin_ctzll(holders);
             win = wl + 64 * __builtin_amdgcn_readlane(bq, wl);
         } else {  // equal logits in several lanes: the lowest id among them
-            win = (int)wave_min(bk == m ? (uint32_t)(lane + 64 * bq) : ~0u);
+            win = (int)wave::min_u32(bk == m ? (uint32_t)(lane + 64 * bq) : ~0u);
         }
         if (lane == (win & 63)) {
 #pragma unroll

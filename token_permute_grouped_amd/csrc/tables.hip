@@ -6,16 +6,22 @@
 //
 // Three launches, no atomics outside LDS and nothing order-dependent:
 //   1. chunk_hist  one workgroup per chunk of kChunk slots: LDS histogram -> chunk_counts[c][e]
-//   2. scan        one workgroup: per expert an exclusive prefix over chunks (in place),
-//                  then an exclusive prefix over experts -> offsets[E+1]
+//   2. scan        one workgroup of 1024 threads: the chunks are split into up to 16 parts per
+//                  expert, a thread sums one (expert, part) with all its loads in flight, then
+//                  per expert an exclusive prefix over parts and chunks (in place), an
+//                  exclusive prefix over experts -> offsets[E+1]; in the forward the same launch
+//                  also writes the GEMM tile list
 //   3. rank        one workgroup per chunk, one wave per quarter chunk: per-wave LDS bases,
 //                  then 64 slots at a time, a slot's rank among equal ids of lower lanes
 //                  comes from 9 ballots (one per bit of id+1) and a popcount.
-// The GEMM tile list (expert, m-tile) is built from offsets by build_tiles.
+// The GEMM tile list (expert, m-tile) is built from offsets by build_tile_list (in the scan
+// launch of the forward, or by build_tiles on its own).
 //
 // For up to kChunk slots the forward runs all of this (and the routing) in one workgroup
 // instead: frontend_small, with the expert ids kept in LDS between the steps.  At small
 // token counts the five launches it replaces cost more than their work.
+#include <algorithm>
+
 #include "route_token.h"
 
 namespace tpg {
@@ -44,39 +50,108 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t *__restri
     for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = h[e];
 }
 
-__global__ __launch_bounds__(256) void scan_kernel(int32_t *__restrict__ chunk_counts, int64_t nch, int E,
-                                                   int32_t *__restrict__ offsets) {
-    __shared__ int tot[256];
+// GEMM tile list from offsets (LDS or global, E+1 entries): tiles[2i] = expert, tiles[2i+1] =
+// first row of the tile within the expert (tiles of bm rows); n_tiles[0] = count, n_tiles[1] =
+// tiles before the partial section.  Default order: full tiles first (expert by expert), then each
+// expert's partial last tile.  by_expert: every expert's tiles together in row order (n_tiles[1] =
+// count).  Thread e < E handles expert e; every thread of the workgroup must call it (it holds a
+// barrier); ws is 8 ints of LDS (see block_incl_sum256).
+__device__ void build_tile_list(const int32_t *off, int E, int bm, int by_expert, int32_t *__restrict__ tiles,
+                                int32_t *__restrict__ n_tiles, int *ws) {
     const int e = threadIdx.x;
-    int run = 0;
+    int full = 0, part = 0;
     if (e < E) {
-        int32_t *col = chunk_counts + e;
-        int64_t c = 0;
-        for (; c + 4 <= nch; c += 4) {  // four independent loads in flight
-            const int v0 = col[(c + 0) * E], v1 = col[(c + 1) * E], v2 = col[(c + 2) * E], v3 = col[(c + 3) * E];
-            col[(c + 0) * E] = run;
-            col[(c + 1) * E] = run + v0;
-            col[(c + 2) * E] = run + v0 + v1;
-            col[(c + 3) * E] = run + v0 + v1 + v2;
-            run += v0 + v1 + v2 + v3;
+        const int cnt = off[e + 1] - off[e];
+        full = by_expert ? (cnt + bm - 1) / bm : cnt / bm;
+        part = !by_expert && (cnt % bm) ? 1 : 0;
+    }
+    int sf = full, sp = part, total_full, total_part;
+    block_incl_sum256(sf, sp, ws, &total_full, &total_part);
+    if (e < E) {
+        const int f0 = sf - full;
+        for (int m = 0; m < full; ++m) {
+            tiles[2 * (f0 + m)] = e;
+            tiles[2 * (f0 + m) + 1] = m * bm;
         }
-        for (; c < nch; ++c) {
-            const int v = col[c * E];
-            col[c * E] = run;
-            run += v;
+        if (part) {
+            const int pos = total_full + sp - 1;
+            tiles[2 * pos] = e;
+            tiles[2 * pos + 1] = full * bm;
         }
     }
-    tot[e] = e < E ? run : 0;
+    if (e == 0) {
+        n_tiles[0] = total_full + total_part;
+        n_tiles[1] = total_full;
+    }
+}
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 8;  // loads in flight per thread
+// parts the chunk column of one expert is split into: at most 16 (the per-expert walk over the
+// parts is serial), at least kScanBatch chunks each, and E * parts <= kScanThreads
+inline int scan_parts(int64_t nch, int E) {
+    const int64_t by_len = (nch + kScanBatch - 1) / kScanBatch;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({16, kScanThreads / E, by_len}));
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t *__restrict__ chunk_counts, int64_t nch, int E,
+                                                            int P, int32_t *__restrict__ offsets, int bm,
+                                                            int by_expert, int32_t *__restrict__ tiles,
+                                                            int32_t *__restrict__ n_tiles) {
+    __shared__ int part_base[kScanThreads];  // [part][E]: part sums, then exclusive bases
+    __shared__ int off[257], ws[8];
+    const int tid = threadIdx.x;
+    const int e = tid % E, part = tid / E;
+    const bool act = part < P;
+    const int64_t cpp = (nch + P - 1) / P;  // chunks per part
+    const int64_t c0 = act ? std::min<int64_t>(nch, part * cpp) : 0;
+    const int64_t c1 = act ? std::min<int64_t>(nch, c0 + cpp) : 0;
+    int32_t *col = chunk_counts + e;
+    int sum = 0;
+    for (int64_t c = c0; c < c1; c += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int q = 0; q < kScanBatch; ++q) v[q] = c + q < c1 ? col[(c + q) * E] : 0;
+#pragma unroll
+        for (int q = 0; q < kScanBatch; ++q) sum += v[q];
+    }
+    if (act) part_base[part * E + e] = sum;
     __syncthreads();
-    // inclusive Hillis-Steele scan over the 256 expert totals
-    for (int d = 1; d < 256; d <<= 1) {
-        const int add = e >= d ? tot[e - d] : 0;
-        __syncthreads();
-        tot[e] += add;
-        __syncthreads();
+    int etot = 0;  // expert tid's total
+    if (tid < E)
+        for (int pp = 0; pp < P; ++pp) {
+            const int v = part_base[pp * E + tid];
+            part_base[pp * E + tid] = etot;
+            etot += v;
+        }
+    // exclusive prefix over experts (the barrier inside also publishes the part bases)
+    int incl = etot, unused = 0, total, unused_total;
+    block_incl_sum256(incl, unused, ws, &total, &unused_total);
+    // exclusive prefix over chunks, in place: the part's base plus the running sum within it
+    if (act) {
+        int run = part_base[part * E + e];
+        for (int64_t c = c0; c < c1; c += kScanBatch) {
+            int v[kScanBatch];
+#pragma unroll
+            for (int q = 0; q < kScanBatch; ++q) v[q] = c + q < c1 ? col[(c + q) * E] : 0;
+#pragma unroll
+            for (int q = 0; q < kScanBatch; ++q) {
+                if (c + q < c1) col[(c + q) * E] = run;
+                run += v[q];
+            }
+        }
     }
-    if (e < E) offsets[e] = tot[e] - run;
-    if (e == E - 1) offsets[E] = tot[e];
+    if (tid < E) {
+        offsets[tid] = incl - etot;
+        off[tid] = incl - etot;
+    }
+    if (tid == 0) {
+        offsets[E] = total;
+        off[E] = total;
+    }
+    if (tiles == nullptr) return;  // uniform
+    __syncthreads();
+    build_tile_list(off, E, bm, by_expert, tiles, n_tiles, ws);
 }
 
 __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ idx, int64_t S, int E,
@@ -139,43 +214,11 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t *__restrict__ i
     }
 }
 
-// tiles[2i] = expert, tiles[2i+1] = first row of the tile within the expert (tiles of bm rows);
-// n_tiles[0] = count, n_tiles[1] = tiles before the partial section.  Default order: full
-// tiles first (expert by expert), then each expert's partial last tile.  by_expert: every
-// expert's tiles together in row order (n_tiles[1] = count).  One thread per expert.
 __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restrict__ offsets, int E, int bm,
                                                           int by_expert, int32_t *__restrict__ tiles,
                                                           int32_t *__restrict__ n_tiles) {
-    __shared__ int nf[256], np[256];
-    const int e = threadIdx.x;
-    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
-    const int full = by_expert ? (cnt + bm - 1) / bm : cnt / bm;
-    const int part = !by_expert && (cnt % bm) ? 1 : 0;
-    nf[e] = full;
-    np[e] = part;
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {  // inclusive scans of both counts
-        const int af = e >= d ? nf[e - d] : 0, ap = e >= d ? np[e - d] : 0;
-        __syncthreads();
-        nf[e] += af;
-        np[e] += ap;
-        __syncthreads();
-    }
-    const int total_full = nf[255];
-    const int f0 = nf[e] - full;
-    for (int m = 0; m < full; ++m) {
-        tiles[2 * (f0 + m)] = e;
-        tiles[2 * (f0 + m) + 1] = m * bm;
-    }
-    if (part) {
-        const int pos = total_full + np[e] - 1;
-        tiles[2 * pos] = e;
-        tiles[2 * pos + 1] = full * bm;
-    }
-    if (e == 255) {
-        n_tiles[0] = total_full + np[255];
-        n_tiles[1] = total_full;
-    }
+    __shared__ int ws[8];
+    build_tile_list(offsets, E, bm, by_expert, tiles, n_tiles, ws);
 }
 
 // Routing, tables and tile list of at most kChunk slots in one workgroup of 16 waves: the same
@@ -189,7 +232,7 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
     __shared__ int32_t sid[kChunk];          // expert id (or -1) of every slot
     __shared__ int cnt[kFrontWaves][256];    // per-wave counts, then per-wave bases
     __shared__ int off[257];
-    __shared__ int sa[256], sb[256];         // scan buffers
+    __shared__ int ws[8];                    // block prefix-sum scratch
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int S = T * k;
 
@@ -205,28 +248,21 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
 
     // per expert: exclusive bases over the waves and the total; exclusive scan over experts
     int tot = 0;
-    if (tid < 256) {
+    if (tid < 256)
         for (int ww = 0; ww < kFrontWaves; ++ww) {
             const int v = cnt[ww][tid];
             cnt[ww][tid] = tot;
             tot += v;
         }
-        sa[tid] = tot;
-    }
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        const int add = (tid < 256 && tid >= d) ? sa[tid - d] : 0;
-        __syncthreads();
-        if (tid < 256) sa[tid] += add;
-        __syncthreads();
-    }
+    int incl = tot, unused = 0, R_all, unused_total;
+    block_incl_sum256(incl, unused, ws, &R_all, &unused_total);
     if (tid < E) {
-        off[tid] = sa[tid] - tot;
-        offsets[tid] = sa[tid] - tot;
+        off[tid] = incl - tot;
+        offsets[tid] = incl - tot;
     }
-    if (tid == E - 1) {
-        off[E] = sa[tid];
-        offsets[E] = sa[tid];
+    if (tid == 0) {
+        off[E] = R_all;
+        offsets[E] = R_all;
     }
     __syncthreads();
 
@@ -249,43 +285,8 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
         if (tid >= R) row_src[tid] = -1;  // rows past the live count (r < R never lands here)
     }
 
-    // GEMM tile list (as build_tiles_kernel)
-    int full = 0, part = 0;
-    if (tid < 256) {
-        const int c = tid < E ? off[tid + 1] - off[tid] : 0;
-        full = by_expert ? (c + bm - 1) / bm : c / bm;
-        part = !by_expert && (c % bm) ? 1 : 0;
-        sa[tid] = full;
-        sb[tid] = part;
-    }
-    __syncthreads();
-    for (int d = 1; d < 256; d <<= 1) {
-        const int af = (tid < 256 && tid >= d) ? sa[tid - d] : 0;
-        const int ap = (tid < 256 && tid >= d) ? sb[tid - d] : 0;
-        __syncthreads();
-        if (tid < 256) {
-            sa[tid] += af;
-            sb[tid] += ap;
-        }
-        __syncthreads();
-    }
-    if (tid < 256) {
-        const int total_full = sa[255];
-        const int f0 = sa[tid] - full;
-        for (int m = 0; m < full; ++m) {
-            tiles[2 * (f0 + m)] = tid;
-            tiles[2 * (f0 + m) + 1] = m * bm;
-        }
-        if (part) {
-            const int pos = total_full + sb[tid] - 1;
-            tiles[2 * pos] = tid;
-            tiles[2 * pos + 1] = full * bm;
-        }
-        if (tid == 255) {
-            n_tiles[0] = total_full + sb[255];
-            n_tiles[1] = total_full;
-        }
-    }
+    // GEMM tile list
+    build_tile_list(off, E, bm, by_expert, tiles, n_tiles, ws);
 }
 
 hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
@@ -298,11 +299,13 @@ hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, 
 }
 
 hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *chunk_counts, int32_t *offsets,
-                         int32_t *row_src, int32_t *slot_row, hipStream_t s) {
+                         int32_t *row_src, int32_t *slot_row, int bm, int by_expert, int32_t *tiles,
+                         int32_t *n_tiles, hipStream_t s) {
     const int64_t S = (int64_t)T * k;
     const int64_t nch = (S + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(256), 0, s, topk_idx, S, E, chunk_counts);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(256), 0, s, chunk_counts, nch, E, offsets);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, chunk_counts, nch, E, scan_parts(nch, E),
+                       offsets, bm, by_expert, tiles, n_tiles);
     hipLaunchKernelGGL(rank_kernel, dim3(nch), dim3(256), 0, s, topk_idx, S, E, chunk_counts, offsets, row_src,
                        slot_row);
     return hipGetLastError();
