@@ -8,12 +8,14 @@
 // logit.  The weight of slot j is exp(l_j - l_max) / sum_i exp(l_i - l_max) over the k
 // chosen, which is the full softmax renormalised over the top k.
 //
-// Lane l holds experts l, l+64, l+128, l+192.  Each of the k rounds is one wave-wide maximum
-// of a 32-bit key (the logit's bits mapped so that unsigned order is float order, -0 folded
-// onto +0) over DPP row operations, then a ballot of the lanes holding it; only equal logits in
-// several lanes take a second (minimum-id) reduction.  Every lane learns each round's winner,
-// so the normaliser is summed in slot order by every lane alike and lane j keeps slot j.  If
-// `ids` is not null, lane j < k also stores the slot's expert id (or -1) at ids[j] (e.g. in LDS).
+// A token is routed by one row of 16 lanes (a DPP row), four tokens per wave64: lane i of the
+// row holds experts i, i+16, i+32, ...  Each of the k rounds is a row-wide maximum of a 32-bit
+// key (the logit's bits mapped so that unsigned order is float order, -0 folded onto +0) and a
+// row-wide minimum of the ids holding it (equal logits -> lower id), four DPP steps each
+// (quad_perm, row_half_mirror, row_mirror), so the rows never exchange data.  Every lane of the
+// row learns each round's winner, so the normaliser is summed in slot order identically in
+// every lane; lane i keeps slots i and i + 16 (k <= 32).  If `ids` is not null, the slots'
+// expert ids (or -1) are also stored at ids[j] (e.g. in LDS).
 #pragma once
 #include "wave_ops.h"
 
@@ -31,62 +33,102 @@ __device__ __forceinline__ float key_logit(uint32_t key) {
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
-}  // namespace route_detail
+// maximum / minimum over the 16 lanes of each row, returned to every lane of the row
+__device__ __forceinline__ uint32_t row_max(uint32_t x) {
+    using namespace wave;
+    x = max(x, dpp<kQuadSwap1, 0xf>(x, 0u));
+    x = max(x, dpp<kQuadSwap2, 0xf>(x, 0u));
+    x = max(x, dpp<kRowHalfMirror, 0xf>(x, 0u));
+    return max(x, dpp<kRowMirror, 0xf>(x, 0u));
+}
+__device__ __forceinline__ uint32_t row_min(uint32_t x) {
+    using namespace wave;
+    x = min(x, dpp<kQuadSwap1, 0xf>(x, ~0u));
+    x = min(x, dpp<kQuadSwap2, 0xf>(x, ~0u));
+    x = min(x, dpp<kRowHalfMirror, 0xf>(x, ~0u));
+    return min(x, dpp<kRowMirror, 0xf>(x, ~0u));
+}
 
-__device__ __forceinline__ void route_token(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
-                                            int64_t t, int E, int k, int lane, int32_t *__restrict__ topk_idx,
-                                            float *__restrict__ topk_w, int32_t *ids) {
-    using namespace route_detail;
+// V: experts per lane (16 V >= E).  t is a valid token for every row; only rows with `valid`
+// store.
+template <int V>
+__device__ __forceinline__ void route_row(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
+                                          int64_t t, bool valid, int E, int k, int i,
+                                          int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *ids) {
     const float *l = logits + t * E;
-    uint32_t key[4];
+    uint32_t key[V];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
+    for (int q = 0; q < V; ++q) {
+        const int e = i + 16 * q;
         key[q] = e < E ? logit_key(l[e]) : 0u;  // 0: no expert (or already taken)
     }
-    int my_id = -1;
-    float my_ex = 0.0f, lmax = 0.0f, z = 0.0f;
+    int id0 = -1, id1 = -1;
+    float ex0 = 0.0f, ex1 = 0.0f, lmax = 0.0f, z = 0.0f;
     for (int j = 0; j < k; ++j) {
         // this lane's best remaining expert: ids grow with q, so strict '>' keeps the lower id
         uint32_t bk = 0u;
         int bq = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < V; ++q)
             if (key[q] > bk) {
                 bk = key[q];
                 bq = q;
             }
-        const uint32_t m = wave::max_u32(bk);  // > 0: k <= E experts are live
-        const uint64_t holders = __ballot(bk == m);
-        int win;
-        if ((holders & (holders - 1)) == 0) {  // one lane holds the largest logit
-            const int wl = __builtin_ctzll(holders);
-            win = wl + 64 * __builtin_amdgcn_readlane(bq, wl);
-        } else {  // equal logits in several lanes: the lowest id among them
-            win = (int)wave::min_u32(bk == m ? (uint32_t)(lane + 64 * bq) : ~0u);
-        }
-        if (lane == (win & 63)) {
+        const uint32_t m = row_max(bk);  // > 0: k <= E experts are live
+        const int win = (int)row_min(bk == m ? (uint32_t)(i + 16 * bq) : ~0u);
+        if ((win & 15) == i) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (q == (win >> 6)) key[q] = 0u;
+            for (int q = 0; q < V; ++q)
+                if (q == (win >> 4)) key[q] = 0u;
         }
         const float lj = key_logit(m);
         if (j == 0) lmax = lj;
         // renormalised softmax weights: exp(l_j - l_max) summed over the chosen slots in order
         const float ex = expf(lj - lmax);
         z += ex;
-        if (lane == j) {
-            my_id = win;
-            my_ex = ex;
+        if (j == i) {
+            id0 = win;
+            ex0 = ex;
+        }
+        if (j == i + 16) {
+            id1 = win;
+            ex1 = ex;
         }
     }
-    if (lane < k) {
-        const int64_t s = t * k + lane;
-        const bool dropped = slot_drop != nullptr && slot_drop[s] != 0;
-        topk_idx[s] = dropped ? -1 : my_id;
-        topk_w[s] = my_ex / z;
-        if (ids) ids[lane] = dropped ? -1 : my_id;
+    if (!valid) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int j = i + 16 * h;
+        if (j < k) {
+            const int64_t s = t * k + j;
+            const bool dropped = slot_drop != nullptr && slot_drop[s] != 0;
+            const int id = dropped ? -1 : (h ? id1 : id0);
+            topk_idx[s] = id;
+            topk_w[s] = (h ? ex1 : ex0) / z;
+            if (ids) ids[j] = id;
+        }
     }
+}
+
+}  // namespace route_detail
+
+// Routes token t with the 16-lane row this lane belongs to (i = lane within the row).  All
+// 64 lanes of the wave must call it with the same E and k.
+__device__ __forceinline__ void route_token16(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
+                                              int64_t t, bool valid, int E, int k, int i,
+                                              int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                              int32_t *ids) {
+    using namespace route_detail;
+    if (E <= 16)
+        route_row<1>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    else if (E <= 32)
+        route_row<2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    else if (E <= 64)
+        route_row<4>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    else if (E <= 128)
+        route_row<8>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    else
+        route_row<16>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
 }
 
 }  // namespace tpg

@@ -236,8 +236,11 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int S = T * k;
 
-    // routing: one wave per token
-    for (int t = w; t < T; t += kFrontWaves) route_token(logits, slot_drop, t, E, k, lane, topk_idx, topk_w, sid + t * k);
+    // routing: one 16-lane row per token, four tokens per wave
+    for (int t0 = w * 4; t0 < T; t0 += kFrontWaves * 4) {
+        const int t = t0 + (lane >> 4);
+        route_token16(logits, slot_drop, t < T ? t : T - 1, t < T, E, k, lane & 15, topk_idx, topk_w, sid + t * k);
+    }
     for (int i = tid; i < kFrontWaves * 256; i += kChunk) (&cnt[0][0])[i] = 0;
     __syncthreads();
 
