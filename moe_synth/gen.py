@@ -1,4 +1,4 @@
-"""Seeded generator for the five MoE FFN forward workloads.
+"""Seeded generator for the MoE FFN forward workloads.
 
 Workloads (sizes and value distributions as the task's configurations give them):
 
@@ -10,6 +10,9 @@ Workloads (sizes and value distributions as the task's configurations give them)
                 with one fp32 scale per 128 columns, NVFP4 weights (e2m1 codes,
                 one e4m3 scale per 16 elements along K, one fp32 global scale per
                 expert and matrix); SwiGLU input clamped to +-10.
+* ``w4a8_mx``   as ``w4a8`` with MXFP4 weights: e2m1 codes, one e8m0 (power-of-two)
+                scale per 32 elements along K, one fp32 global scale per expert
+                and matrix.
 * ``ep_share``  T=32768, H=7168, I=2048, E=32, top-8, bf16; W1 gate/up rows
                 interleaved in blocks of 32; 10% of (token, slot) pairs dropped.
 
@@ -28,6 +31,7 @@ Layouts (all row-major, K contiguous):
   w1        bf16 bits uint16 [E][2I][H]        | w4a8: uint8 [E][2I][H/2] (low nibble = even k)
                                                    + e4m3 uint8 [E][2I][H/16] + f32 [E]
   w2        bf16 bits uint16 [E][H][I]         | w4a8: uint8 [E][H][I/2] + uint8 [E][H][I/16] + f32 [E]
+                                               | w4a8_mx: block scales e8m0 uint8 [E][2I][H/32], [E][H][I/32]
 W1 rows are [gate | up] (gate rows 0..I-1), or, with an interleave of 32, stored
 row 64q+r holds gate row 32q+r for r<32 and up row 32q+r-32 for r>=32.
 """
@@ -53,7 +57,7 @@ class MoeConfig:
     I: int
     E: int
     k: int
-    prec: str = "bf16"          # "bf16" or "w4a8"
+    prec: str = "bf16"          # "bf16", "w4a8" (NVFP4 weights) or "w4a8_mx" (MXFP4 weights)
     glu_interleave: int = 0     # 0 = [gate|up]; 32 = 32-row blocks gate,up,gate,up,...
     swiglu_clamp: float = 0.0   # 0 = none; c>0 clamps gate and up to [-c, c]
     zipf_s: float = 0.0         # >0: per-expert logit bias ln(rank^-s)
@@ -74,6 +78,8 @@ CONFIGS = {
     "skewed": MoeConfig("skewed", T=16384, H=4096, I=2048, E=128, k=8, zipf_s=1.2),
     "w4a8": MoeConfig("w4a8", T=256, H=7168, I=2048, E=32, k=8, prec="w4a8",
                       swiglu_clamp=10.0),
+    "w4a8_mx": MoeConfig("w4a8_mx", T=256, H=7168, I=2048, E=32, k=8, prec="w4a8_mx",
+                         swiglu_clamp=10.0),
     "ep_share": MoeConfig("ep_share", T=32768, H=7168, I=2048, E=32, k=8,
                           glu_interleave=32, drop_p=0.1),
 }
@@ -204,6 +210,33 @@ def _quantise_nvfp4(w: np.ndarray):
     return packed, bs_code, gs
 
 
+def _quantise_mxfp4(w: np.ndarray):
+    """One expert's matrix fp32 [N][K] -> (packed e2m1 [N][K/2], e8m0 scales [N][K/32], fp32 global).
+
+    The global scale is a power of two, gs = 2^(floor(log2 amax) - 8), so that a block holding the
+    matrix's largest value gets block exponent 6.  Block exponent (OCP MX: floor(log2) of the
+    block's amax minus e2m1's largest exponent, 2) eb = floor(log2(amax_32 / gs)) - 2, kept within
+    -5..6 (the scale range the FlashInfer follow-up #6517 asks for); scale code eb + 127; code =
+    e2m1(w / (2^eb gs)), round to nearest even, saturating at +-6.
+    """
+    N, K = w.shape
+    amax = float(np.abs(w).max())
+    gs = np.float32(2.0 ** (np.floor(np.log2(amax)) - 8)) if amax > 0 else np.float32(1.0)
+    packed = np.empty((N, K // 2), dtype=np.uint8)
+    bs_code = np.empty((N, K // 32), dtype=np.uint8)
+    for r0 in range(0, N, 256):  # row blocks keep the temporaries small
+        blk = w[r0:r0 + 256].reshape(-1, K // 32, 32)
+        amax32 = np.abs(blk).max(axis=2).astype(np.float64)
+        with np.errstate(divide="ignore"):
+            eb = np.floor(np.log2(amax32 / float(gs))) - 2
+        eb = np.clip(np.where(amax32 > 0, eb, -5), -5, 6).astype(np.int32)
+        scale = (np.ldexp(np.float32(1.0), eb) * gs).astype(np.float32)
+        codes = _e2m1_codes((blk / scale[:, :, None]).astype(np.float32)).reshape(-1, K)
+        packed[r0:r0 + 256] = codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))
+        bs_code[r0:r0 + 256] = (eb + 127).astype(np.uint8)
+    return packed, bs_code, gs
+
+
 # ----------------------------------------------------------------------------
 # the generator
 # ----------------------------------------------------------------------------
@@ -272,20 +305,23 @@ def generate(cfg: MoeConfig, seed: int = 0, T: int | None = None, threads: int |
             list(ex.map(job, range(E)))
         out["w1"], out["w2"] = w1, w2
     else:
+        mx = cfg.prec == "w4a8_mx"
+        bk = 32 if mx else 16  # K values per block scale
+        quant = _quantise_mxfp4 if mx else _quantise_nvfp4
         w1 = np.empty((E, 2 * I, H // 2), dtype=np.uint8)
-        w1b = np.empty((E, 2 * I, H // 16), dtype=np.uint8)
+        w1b = np.empty((E, 2 * I, H // bk), dtype=np.uint8)
         w1g = np.empty(E, dtype=np.float32)
         w2 = np.empty((E, H, I // 2), dtype=np.uint8)
-        w2b = np.empty((E, H, I // 16), dtype=np.uint8)
+        w2b = np.empty((E, H, I // bk), dtype=np.uint8)
         w2g = np.empty(E, dtype=np.float32)
 
         def job(e):
             a = (_normal(ch1[e], 2 * I * H) * sd1).reshape(2 * I, H)
             if perm is not None:
                 a = a[perm]
-            w1[e], w1b[e], w1g[e] = _quantise_nvfp4(a)
+            w1[e], w1b[e], w1g[e] = quant(a)
             b = (_normal(ch2[e], H * I) * sd2).reshape(H, I)
-            w2[e], w2b[e], w2g[e] = _quantise_nvfp4(b)
+            w2[e], w2b[e], w2g[e] = quant(b)
 
         with ThreadPoolExecutor(_threads(threads)) as ex:
             list(ex.map(job, range(E)))

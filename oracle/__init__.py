@@ -43,6 +43,8 @@ def _load():
     lib.orc_e4m3_value.restype = f64
     lib.orc_e2m1_value.argtypes = [ctypes.c_uint8]
     lib.orc_e2m1_value.restype = f64
+    lib.orc_e8m0_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e8m0_value.restype = f64
     lib.orc_e4m3_encode.argtypes = [f64]
     lib.orc_e4m3_encode.restype = ctypes.c_uint8
     lib.orc_fp4_to_fp8.argtypes = [ctypes.c_uint8, ctypes.c_uint8]
@@ -52,7 +54,7 @@ def _load():
     lib.orc_permute_rows.argtypes = [i64, i32, i32, P, P, P]
     lib.orc_combine_bf16.argtypes = [i32, i32, i32, P, P, P, P]
     lib.orc_ffn_rows_bf16.argtypes = [i64, P, P, i32, i32, i32, f64, P, P, P, P]
-    lib.orc_ffn_rows_w4a8.argtypes = [i64, P, P, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P]
+    lib.orc_ffn_rows_w4a8.argtypes = [i64, P, P, i32, i32, i32, f64, P, P, P, P, P, P, P, P, i32, P]
     lib.orc_moe_forward.argtypes = [i32, P, i32, i32, i32, i32, i32, i32, i32, f64,
                                     P, P, P, P, P, P, P, P, P, P, P]
     lib.orc_max_threads.restype = i32
@@ -79,6 +81,10 @@ def e4m3_value(code: int) -> float:
 
 def e2m1_value(code: int) -> float:
     return _load().orc_e2m1_value(int(code))
+
+
+def e8m0_value(code: int) -> float:
+    return _load().orc_e8m0_value(int(code))
 
 
 def e4m3_encode(v: float) -> int:
@@ -169,7 +175,8 @@ def ffn_rows(inp: dict, tokens, experts):
                               keep(inp["x"], np.uint8), keep(inp["x_scale"], np.float32),
                               keep(inp["w1"], np.uint8), keep(inp["w1_bscale"], np.uint8),
                               keep(inp["w1_gscale"], np.float32), keep(inp["w2"], np.uint8),
-                              keep(inp["w2_bscale"], np.uint8), keep(inp["w2_gscale"], np.float32), _p(y))
+                              keep(inp["w2_bscale"], np.uint8), keep(inp["w2_gscale"], np.float32),
+                              1 if cfg.prec == "w4a8_mx" else 0, _p(y))
     return y
 
 
@@ -181,10 +188,11 @@ def moe_forward(inp: dict, tokens=None):
     keep = _Keep()
     tok = _c(tokens, np.int32)
     out = np.empty((tok.size, cfg.H), np.float64)
-    w4 = cfg.prec == "w4a8"
+    w4 = cfg.prec != "bf16"
     xdt = np.uint8 if w4 else np.uint16
+    prec = {"bf16": 0, "w4a8": 1, "w4a8_mx": 2}[cfg.prec]
     _load().orc_moe_forward(
-        tok.size, _p(tok), cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, 1 if w4 else 0, cfg.glu_interleave,
+        tok.size, _p(tok), cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, prec, cfg.glu_interleave,
         cfg.swiglu_clamp, keep(inp["logits"], np.float32), keep(inp.get("slot_drop"), np.uint8),
         keep(inp["x"], xdt), keep(inp.get("x_scale"), np.float32),
         keep(inp["w1"], xdt), keep(inp.get("w1_bscale"), np.uint8),

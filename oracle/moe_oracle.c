@@ -17,9 +17,11 @@
  *            kernel description (dispatch, both FFN GEMMs with NVFP4 weights and
  *            FP8 activations, SwiGLU, top-k combine; NVFP4 -> FP8 dequant) and
  *            its Usage section (-1 masks a route; FP32 routing weights; FP32
- *            input scales per 128 channels; E4M3 weight scale per 16 values).
+ *            input scales per 128 channels; E4M3 weight scale per 16 values
+ *            for NVFP4 weights, E8M0 per 32 values for MXFP4 weights).
  *  [FI6517]  its follow-up #6517, point 4 (weight preparation: low-nibble-first
- *            packing, NVFP4 scales bounded by 6*scale <= 448, per-expert global
+ *            packing, NVFP4 scales bounded by 6*scale <= 448, MXFP4 scales kept
+ *            within 2^-5..2^6 for groups with nonzero codes, per-expert global
  *            scales) and the split family's note that the second GEMM's
  *            activation scales are per 128 like the first's.
  *  [MG3971]  Megatron-LM PR #3971 "Support GEMM + Swiglu fused MLP" -- the
@@ -51,6 +53,14 @@
  *    GEMM result.
  *  - W4A8 SwiGLU output: re-quantised per (row, 128 columns) with
  *    s = amax/448 (s = 1 if that is 0), q = e4m3(h / s), in float32.
+ *  - MXFP4 weights (precision 2): the weight's value is its e2m1 value times
+ *    2^(E8M0 code - 127) (the OCP MX scale format: a power of two, bias 127,
+ *    code 255 NaN), exactly, with no rounding to FP8; the per-expert global
+ *    scale multiplies the GEMM result, and activations, SwiGLU, h re-quantised
+ *    to FP8 and the second GEMM are as for NVFP4.  The pages' kernel decodes
+ *    MXFP4 to FP8 first, which is exact for the scales they require
+ *    (2^-5..2^6 for groups with nonzero codes [FI6517]), so on those inputs
+ *    both readings give the same value.
  */
 #include <math.h>
 #include <stdint.h>
@@ -94,6 +104,12 @@ double orc_e2m1_value(uint8_t c)
     int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
     double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
     return s ? -v : v;
+}
+
+/* OCP E8M0 (the MX scale): 2^(c - 127); code 255 is NaN. */
+double orc_e8m0_value(uint8_t c)
+{
+    return c == 255 ? NAN : ldexp(1.0, (int)c - 127);
 }
 
 /* Nearest E4M3FN code to v, ties to the even code, saturating at +-448; a NaN
@@ -289,21 +305,25 @@ static void ffn_bf16(int H, int I, int il, double clamp, const uint16_t *xrow, c
     }
 }
 
-/* dequantised NVFP4 weight at (row, col) of a [N][K] matrix: e4m3(fp8 dequant) * global */
+/* weight at (row, col) of a packed [N][K] matrix, before its global scale.  NVFP4 (mx = 0):
+ * the FP8 dequant of e2m1 * e4m3 block scale (one per 16 along K), through lut.  MXFP4
+ * (mx = 1): e2m1 * 2^(e8m0 block scale - 127) (one per 32 along K), exactly. */
 static double w4_value(const uint8_t *packed, const uint8_t *bscale, int K, long row, int col,
-                       const double *lut)
+                       const double *lut, int mx)
 {
     uint8_t byte = packed[row * (K / 2) + col / 2];
     uint8_t code = (col % 2 == 0) ? (byte & 15) : (byte >> 4); /* low nibble = even element [FI6517] */
-    uint8_t sc = bscale[row * (K / 16) + col / 16];
-    return lut[code * 256 + sc];
+    if (mx)
+        return orc_e2m1_value(code) * orc_e8m0_value(bscale[row * (K / 32) + col / 32]);
+    return lut[code * 256 + bscale[row * (K / 16) + col / 16]];
 }
 
 /* W4A8 expert [FI6343]: FP8 activations with per-128 scales x NVFP4 weights
- * dequantised to FP8, clamped SwiGLU, h re-quantised to FP8 per 128, second GEMM. */
+ * dequantised to FP8 (or MXFP4 weights, mx = 1), clamped SwiGLU, h re-quantised to
+ * FP8 per 128, second GEMM. */
 static void ffn_w4a8(int H, int I, int il, double clamp, const uint8_t *x8, const float *xs, const uint8_t *w1e,
                      const uint8_t *w1b, double w1g, const uint8_t *w2e, const uint8_t *w2b, double w2g,
-                     const double *lut, double *xd, double *h, double *y)
+                     const double *lut, int mx, double *xd, double *h, double *y)
 {
     float hf[128];
     for (int c = 0; c < H; c++)
@@ -312,8 +332,8 @@ static void ffn_w4a8(int H, int I, int il, double clamp, const uint8_t *x8, cons
         long rg = w1_row(I, il, n, 0), ru = w1_row(I, il, n, 1);
         double g = 0.0, u = 0.0;
         for (int c = 0; c < H; c++) {
-            g += xd[c] * w4_value(w1e, w1b, H, rg, c, lut);
-            u += xd[c] * w4_value(w1e, w1b, H, ru, c, lut);
+            g += xd[c] * w4_value(w1e, w1b, H, rg, c, lut, mx);
+            u += xd[c] * w4_value(w1e, w1b, H, ru, c, lut, mx);
         }
         h[n] = swiglu(g * w1g, u * w1g, clamp);
     }
@@ -336,7 +356,7 @@ static void ffn_w4a8(int H, int I, int il, double clamp, const uint8_t *x8, cons
     for (int c = 0; c < H; c++) {
         double acc = 0.0;
         for (int n = 0; n < I; n++)
-            acc += h[n] * w4_value(w2e, w2b, I, c, n, lut);
+            acc += h[n] * w4_value(w2e, w2b, I, c, n, lut, mx);
         y[c] = acc * w2g;
     }
 }
@@ -371,11 +391,13 @@ void orc_ffn_rows_bf16(long n, const int32_t *token, const int32_t *expert, int 
     }
 }
 
+/* mx = 0: NVFP4 weights (block scales [E][N][K/16]); mx = 1: MXFP4 ([E][N][K/32]) */
 void orc_ffn_rows_w4a8(long n, const int32_t *token, const int32_t *expert, int H, int I, int il, double clamp,
                        const uint8_t *x8, const float *xs, const uint8_t *w1, const uint8_t *w1b,
-                       const float *w1g, const uint8_t *w2, const uint8_t *w2b, const float *w2g, double *y)
+                       const float *w1g, const uint8_t *w2, const uint8_t *w2b, const float *w2g, int mx, double *y)
 {
     double *lut = fp4_fp8_lut();
+    const int bk = mx ? 32 : 16; /* K values per block scale */
 #pragma omp parallel
     {
         double *h = (double *)malloc(sizeof(double) * I), *xd = (double *)malloc(sizeof(double) * H);
@@ -383,8 +405,8 @@ void orc_ffn_rows_w4a8(long n, const int32_t *token, const int32_t *expert, int 
         for (long i = 0; i < n; i++) {
             size_t e = (size_t)expert[i], t = (size_t)token[i];
             ffn_w4a8(H, I, il, clamp, x8 + t * H, xs + t * (H / 128), w1 + e * 2 * I * (H / 2),
-                     w1b + e * 2 * I * (H / 16), w1g[e], w2 + e * H * (I / 2), w2b + e * H * (I / 16), w2g[e], lut,
-                     xd, h, y + (size_t)i * H);
+                     w1b + e * 2 * I * (H / bk), w1g[e], w2 + e * H * (I / 2), w2b + e * H * (I / bk), w2g[e], lut,
+                     mx, xd, h, y + (size_t)i * H);
         }
         free(h);
         free(xd);
@@ -402,7 +424,8 @@ void orc_moe_forward(int n_tok, const int32_t *tokens, int T, int H, int I, int 
                      const void *w1, const void *w1_bscale, const float *w1_gscale, const void *w2,
                      const void *w2_bscale, const float *w2_gscale, double *out)
 {
-    double *lut = prec == 1 ? fp4_fp8_lut() : NULL;
+    double *lut = prec != 0 ? fp4_fp8_lut() : NULL;
+    const int mx = prec == 2, bk = mx ? 32 : 16; /* K values per weight block scale */
     (void)T;
 #pragma omp parallel
     {
@@ -427,9 +450,9 @@ void orc_moe_forward(int n_tok, const int32_t *tokens, int T, int H, int I, int 
                              (const uint16_t *)w2 + e * H * I, h, y);
                 else
                     ffn_w4a8(H, I, il, clamp, (const uint8_t *)x + t * H, x_scale + t * (H / 128),
-                             (const uint8_t *)w1 + e * 2 * I * (H / 2), (const uint8_t *)w1_bscale + e * 2 * I * (H / 16),
+                             (const uint8_t *)w1 + e * 2 * I * (H / 2), (const uint8_t *)w1_bscale + e * 2 * I * (H / bk),
                              w1_gscale[e], (const uint8_t *)w2 + e * H * (I / 2),
-                             (const uint8_t *)w2_bscale + e * H * (I / 16), w2_gscale[e], lut, xd, h, y);
+                             (const uint8_t *)w2_bscale + e * H * (I / bk), w2_gscale[e], lut, mx, xd, h, y);
                 for (int c = 0; c < H; c++)
                     o[c] += w[j] * y[c];
             }

@@ -7,6 +7,7 @@ a closed form, or an invariant of the method.  The inputs are random and
 asymmetric, so a dropped term, a wrong sign or index, or a transposed operand in
 the oracle fails at least one of them.
 """
+import dataclasses
 import itertools
 
 import numpy as np
@@ -385,6 +386,88 @@ def test_w4a8_generator_respects_the_decoder_range():
     xs = inp["x_scale"]
     xq = torch.from_numpy(inp["x"]).view(torch.float8_e4m3fn).to(torch.float32).numpy()
     assert np.abs(xq).max() <= 448 and xs.shape == (4, 2)
+
+
+# ----------------------------------------------------------------------------- MXFP4 weights
+
+def test_e8m0_is_a_power_of_two_with_bias_127():
+    # OCP MX scale format: exponent only, bias 127, code 0xFF is NaN
+    assert oracle.e8m0_value(127) == 1.0 and oracle.e8m0_value(128) == 2.0 and oracle.e8m0_value(126) == 0.5
+    assert oracle.e8m0_value(0) == 2.0 ** -127 and oracle.e8m0_value(254) == 2.0 ** 127
+    assert np.isnan(oracle.e8m0_value(255))
+
+
+def test_mxfp4_values_in_the_required_scale_range_are_exact_in_fp8():
+    # FlashInfer #6517 keeps MXFP4 scales within 2^-5..2^6 so that an FP8 decode neither saturates
+    # nor flushes: there every exact MX value (the oracle's reading) is an e4m3 value
+    for sc in range(122, 134):
+        for c in range(16):
+            v = oracle.e2m1_value(c) * oracle.e8m0_value(sc)
+            assert oracle.e4m3_value(oracle.e4m3_encode(v)) == v
+    assert oracle.e4m3_value(oracle.e4m3_encode(6 * 2.0 ** 7)) == 448.0  # one step above: saturates
+
+
+def _mx_as_nvfp4(inp):
+    """The same weights with each e8m0 block scale (one per 32 along K) written as the two equal
+    e4m3 scales of its 16-wide halves: inside 2^-5..2^6 every e2m1 * scale product is an e4m3
+    value, so the NVFP4 FP8 dequant reproduces the MX values exactly."""
+    out = dict(inp)
+    for key in ("w1_bscale", "w2_bscale"):
+        v = np.ldexp(np.float32(1.0), inp[key].astype(np.int32) - 127).astype(np.float32)
+        out[key] = torch.from_numpy(np.repeat(v, 2, axis=-1)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    out["cfg"] = dataclasses.replace(inp["cfg"], prec="w4a8")
+    return out
+
+
+def test_mxfp4_ffn_and_forward_equal_nvfp4_with_equal_block_scales():
+    cfg = MoeConfig("t", T=6, H=256, I=256, E=3, k=2, prec="w4a8_mx", swiglu_clamp=10.0)
+    inp = generate(cfg, seed=21)
+    assert inp["w1_bscale"].shape == (3, 512, 8) and inp["w2_bscale"].shape == (3, 256, 8)
+    rng = np.random.default_rng(5)  # scales varying block to block: a wrong block index changes values
+    for key in ("w1_bscale", "w2_bscale"):
+        inp[key] = rng.integers(122, 134, size=inp[key].shape).astype(np.uint8)
+    nv = _mx_as_nvfp4(inp)
+    tok = np.array([0, 1, 2, 3, 4, 5, 0, 3], np.int32)
+    ex = np.array([0, 1, 2, 0, 1, 2, 2, 1], np.int32)
+    assert np.array_equal(oracle.ffn_rows(inp, tok, ex), oracle.ffn_rows(nv, tok, ex))
+    assert np.array_equal(oracle.moe_forward(inp), oracle.moe_forward(nv))
+
+
+def test_mxfp4_ffn_equals_dense_computation_on_exact_weights():
+    cfg = MoeConfig("t", T=5, H=256, I=256, E=2, k=2, prec="w4a8_mx", swiglu_clamp=10.0)
+    inp = generate(cfg, seed=22)
+    tok = np.array([0, 1, 2, 3, 4], np.int32)
+    ex = np.array([0, 1, 1, 0, 1], np.int32)
+    y = oracle.ffn_rows(inp, tok, ex)
+    xq = torch.from_numpy(inp["x"]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xd = xq * np.repeat(inp["x_scale"].astype(np.float64), 128, axis=1)
+
+    def dense(packed, bscale, gscale):
+        codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(packed.shape[0], -1)
+        mag = E2M1_VALUES[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+        return mag * np.ldexp(1.0, np.repeat(bscale.astype(np.int64) - 127, 32, axis=1)) * np.float64(gscale)
+
+    for i, (t, e) in enumerate(zip(tok, ex)):
+        w1 = dense(inp["w1"][e], inp["w1_bscale"][e], inp["w1_gscale"][e])
+        w2 = dense(inp["w2"][e], inp["w2_bscale"][e], inp["w2_gscale"][e])
+        g = np.clip(xd[t] @ w1[: cfg.I].T, -10, 10)
+        u = np.clip(xd[t] @ w1[cfg.I:].T, -10, 10)
+        h = (g * scipy.special.expit(g) * u).astype(np.float32).reshape(-1, 128)
+        s = (np.abs(h).max(axis=1) / np.float32(448)).astype(np.float32)
+        s[s == 0] = 1
+        hq = _torch_fp8_round((h / s[:, None]).astype(np.float32)) * s[:, None].astype(np.float64)
+        np.testing.assert_allclose(y[i], hq.reshape(-1) @ w2.T, rtol=1e-9, atol=1e-12)
+
+
+def test_mxfp4_generator_keeps_scales_in_the_required_range():
+    # FlashInfer #6517: MXFP4 block scales within 2^-5..2^6; the rest in a power-of-two global scale
+    cfg = MoeConfig("t", T=4, H=512, I=256, E=2, k=1, prec="w4a8_mx")
+    inp = generate(cfg, seed=23)
+    for key in ("w1_bscale", "w2_bscale"):
+        assert (inp[key] >= 122).all() and (inp[key] <= 133).all() and (inp[key] == 133).any()
+    for key in ("w1_gscale", "w2_gscale"):
+        m, _ = np.frexp(inp[key])
+        assert (m == 0.5).all()  # powers of two
 
 
 # ----------------------------------------------------------------------------- generator
