@@ -196,9 +196,10 @@ def main():
             a = a.view(np.int16)
         return torch.from_numpy(a).to(dev)
 
-    w4 = cfg.prec == "w4a8"
-    p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.MOE_PREC_W4A8 if w4 else tpg.MOE_PREC_BF16,
-                        cfg.glu_interleave, cfg.swiglu_clamp)
+    w4 = cfg.prec != "bf16"
+    mx = cfg.prec == "w4a8_mx"
+    p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.PRECISIONS[cfg.prec], cfg.glu_interleave,
+                         cfg.swiglu_clamp)
     d = {k: dt(inp.get(k)) for k in ("logits", "slot_drop", "x", "x_scale", "w1", "w1_bscale", "w1_gscale", "w2",
                                       "w2_bscale", "w2_gscale")}
     wts = tpg.make_weights(d["w1"], d["w2"], d["w1_bscale"], d["w1_gscale"], d["w2_bscale"], d["w2_gscale"])
@@ -324,13 +325,14 @@ def main():
         }
     else:
         # the W4A8 expert FFN streams the packed weights of every expert that has a row:
-        # W1 codes 2I*H/2 + scales 2I*H/16, W2 codes H*I/2 + scales H*I/16 bytes per expert,
+        # W1 codes 2I*H/2 + scales 2I*H/16 (MXFP4: /32), W2 codes H*I/2 + scales H*I/16 (/32) per expert,
         # plus activations in (R*H fp8 + scales), h round trip and y out; the weights dominate
         ids = np.argsort(-inp["logits"], axis=1, kind="stable")[:, :k]
         if inp.get("slot_drop") is not None:
             ids = np.where(inp["slot_drop"] == 1, -1, ids)
         n_exp = len(np.unique(ids[ids >= 0]))
-        w_bytes = n_exp * (2 * I * H // 2 + 2 * I * H // 16 + H * I // 2 + H * I // 16)
+        sb = 32 if mx else 16  # K values per weight block scale
+        w_bytes = n_exp * (2 * I * H // 2 + 2 * I * H // sb + H * I // 2 + H * I // sb)
         act_bytes = R * H + R * (H // 128) * 4 + R * I * (4 + 4 + 1) + R * (I // 128) * 4 + R * H * 2
         ffn_bytes = w_bytes + act_bytes
         a = gbs(ffn_bytes, stage_ms["gemm1_swiglu"])
@@ -353,7 +355,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8xfp4" if w4 else "bf16",
+        "dtype": ("fp8xmxfp4" if mx else "fp8xfp4") if w4 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} H={H} I={I} E={cfg.E} top-{k}"
                                + (f", Zipf s={cfg.zipf_s} expert bias" if cfg.zipf_s else "")

@@ -65,7 +65,13 @@ enum {
      * E4M3) and multiplied on FP8 matrix cores; h is re-quantised to FP8 per
      * (row, 128 columns) with s = amax/448 (the split family's note that the
      * second GEMM's activation scales are per 128 like the first's).  out bf16. */
-    MOE_PREC_W4A8 = 1
+    MOE_PREC_W4A8 = 1,
+    /* The same with MXFP4 weights (the Usage section's "E8M0 per 32 values"): E2M1
+     * codes packed as above, one E8M0 scale (2^(code - 127)) per 32 values along K,
+     * and one fp32 global scale per expert and matrix.  The codes and their scales
+     * go to the FP4 matrix cores as they are: each product e2m1 * 2^s * fp8 is exact
+     * (no FP8 rounding of the weight, so no scale-range limit). */
+    MOE_PREC_W4A8_MX = 2
 };
 
 /* Selects which call moe_workspace_bytes() sizes the workspace for. */
@@ -73,12 +79,12 @@ enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
 
 typedef struct moe_problem {
     int32_t T;              /* tokens, >= 0 */
-    int32_t H;              /* hidden size, multiple of 128 (W4A8: of 256), 128..65536 */
-    int32_t I;              /* per-expert intermediate size, multiple of 128 (W4A8: of 256);
+    int32_t H;              /* hidden size, multiple of 128 (W4A8, W4A8_MX: of 256), 128..65536 */
+    int32_t I;              /* per-expert intermediate size, multiple of 128 (W4A8, W4A8_MX: of 256);
                                one expert matrix (2*I*H bf16) must be below 2 GB */
     int32_t E;              /* experts, 1..256 */
     int32_t k;              /* experts per token, 1..min(E, 32); T*k < 2^31 */
-    int32_t prec;           /* MOE_PREC_BF16 or MOE_PREC_W4A8 */
+    int32_t prec;           /* MOE_PREC_BF16, MOE_PREC_W4A8 or MOE_PREC_W4A8_MX */
     /* Megatron-LM "Support GEMM + Swiglu fused MLP", option
      * moe_mlp_glu_interleave_size: 0 = W1 rows are [gate (I rows) | up (I rows)]
      * (the fused fc1 layout in Megatron-LM PR #5984's log); 32 = stored row
@@ -92,7 +98,8 @@ typedef struct moe_problem {
 
 /* Expert weights (device pointers, borrowed).  bf16: only w1 and w2 are used.
  * w4a8: w1 uint8 [E][2I][H/2], w1_bscale uint8 [E][2I][H/16], w1_gscale fp32 [E];
- *       w2 uint8 [E][H][I/2],  w2_bscale uint8 [E][H][I/16],  w2_gscale fp32 [E]. */
+ *       w2 uint8 [E][H][I/2],  w2_bscale uint8 [E][H][I/16],  w2_gscale fp32 [E].
+ * w4a8_mx: the same with w1_bscale uint8 [E][2I][H/32], w2_bscale uint8 [E][H][I/32]. */
 typedef struct moe_weights {
     const void *w1;
     const void *w1_bscale;

@@ -39,9 +39,8 @@ class DeviceProblem:
     def __init__(self, inp: dict):
         self.inp = inp
         cfg = self.cfg = inp["cfg"]
-        self.w4 = cfg.prec == "w4a8"
-        self.p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k,
-                                  tpg.MOE_PREC_W4A8 if self.w4 else tpg.MOE_PREC_BF16,
+        self.w4 = cfg.prec != "bf16"
+        self.p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.PRECISIONS[cfg.prec],
                                   cfg.glu_interleave, cfg.swiglu_clamp)
         self.logits = to_dev(inp["logits"])
         self.drop = to_dev(inp.get("slot_drop"))

@@ -49,6 +49,7 @@ def _p(**kw):
     (dict(glu_interleave=16), tpg.MOE_ERR_UNSUPPORTED), (dict(swiglu_clamp=-1.0), tpg.MOE_ERR_UNSUPPORTED),
     (dict(swiglu_clamp=float("nan")), tpg.MOE_ERR_UNSUPPORTED),
     (dict(prec=1, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=1, I=384), tpg.MOE_ERR_SHAPE),
+    (dict(prec=2, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=2, I=384), tpg.MOE_ERR_SHAPE), (dict(prec=3), tpg.MOE_ERR_UNSUPPORTED),
     (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE),
 ])
 def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
@@ -84,11 +85,12 @@ def test_null_pointers_are_rejected():
     assert lib.moe_permute_timed(FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None, ev) == NULL
     assert lib.moe_permute_timed(FAKE, None, FAKE, p, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None,
                                  None) == NULL
-    # W4A8 needs the scale arrays too
-    p4 = ctypes.byref(_p(prec=tpg.MOE_PREC_W4A8, H=256))
-    assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p4, FAKE, FAKE, 1 << 40, None) == NULL
-    assert lib.moe_forward(FAKE, None, FAKE, None, ctypes.byref(tpg.Weights(*[FAKE] * 6)), p4, FAKE, FAKE,
-                           1 << 40, None) == NULL
+    # W4A8 (NVFP4 or MXFP4 weights) needs the scale arrays too
+    for prec in (tpg.MOE_PREC_W4A8, tpg.MOE_PREC_W4A8_MX):
+        p4 = ctypes.byref(_p(prec=prec, H=256))
+        assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p4, FAKE, FAKE, 1 << 40, None) == NULL
+        assert lib.moe_forward(FAKE, None, FAKE, None, ctypes.byref(tpg.Weights(*[FAKE] * 6)), p4, FAKE, FAKE,
+                               1 << 40, None) == NULL
 
 
 def test_small_workspace_is_rejected():
@@ -136,6 +138,10 @@ def test_workspace_sizes():
     S4 = 256 * 8
     n4 = tpg.moe_workspace_bytes(w4, tpg.MOE_WS_FORWARD)
     assert S4 * (7168 * 2 + 2048 * 5) <= n4 < S4 * (7168 * 2 + 2048 * 5 + 7168)
+    # MXFP4 weights change only the weight scales: the same workspace for every call
+    mx = _p(T=256, H=7168, I=2048, E=32, k=8, prec=tpg.MOE_PREC_W4A8_MX, swiglu_clamp=10.0)
+    for which in (tpg.MOE_WS_PERMUTE, tpg.MOE_WS_GROUPED_FFN, tpg.MOE_WS_FORWARD):
+        assert tpg.moe_workspace_bytes(mx, which) == tpg.moe_workspace_bytes(w4, which) > 0
     assert tpg.moe_workspace_bytes(big, tpg.MOE_WS_PERMUTE) < tpg.moe_workspace_bytes(big, tpg.MOE_WS_GROUPED_FFN) < n
     assert tpg.moe_workspace_bytes(big, 99) == 0
 

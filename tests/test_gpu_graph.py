@@ -25,6 +25,8 @@ CASES = [
     MoeConfig("graph_w4a8", T=64, H=512, I=256, E=8, k=2, prec="w4a8", swiglu_clamp=10.0),
     # K a multiple of 1024 and T <= 32: the persistent W4A8 GEMMs
     MoeConfig("graph_w4a8_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8", swiglu_clamp=10.0),
+    MoeConfig("graph_w4a8_mx_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
+    MoeConfig("graph_w4a8_mx", T=64, H=512, I=256, E=8, k=2, prec="w4a8_mx", swiglu_clamp=10.0),
 ]
 
 

@@ -15,7 +15,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpg_moe.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
-MOE_PREC_BF16, MOE_PREC_W4A8 = 0, 1
+MOE_PREC_BF16, MOE_PREC_W4A8, MOE_PREC_W4A8_MX = 0, 1, 2
+# precision of a synthetic workload's `prec` name
+PRECISIONS = {"bf16": MOE_PREC_BF16, "w4a8": MOE_PREC_W4A8, "w4a8_mx": MOE_PREC_W4A8_MX}
 MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 
 # every symbol include/moe.h declares

@@ -1,6 +1,8 @@
 // W4A8 expert FFN: FP8 E4M3 activations (one fp32 scale per 128 columns) times
 // NVFP4 weights dequantised to FP8 in-kernel, on FP8 matrix cores
-// (v_mfma_f32_32x32x64_f8f6f4 with unit block scales).
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales), or times MXFP4 weights
+// (kMX: E2M1 codes with one E8M0 scale per 32 along K) fed to the FP4 matrix cores as
+// they are, the E8M0 byte as the instruction's weight block scale.
 //
 // Sources: FlashInfer "[SM90] Add W4A8 MegaMoE support" -- the fused kernel's
 // NVFP4 -> FP8 dequant, the clamped SwiGLU, and its Usage section (E2M1 codes, one
@@ -44,7 +46,11 @@
 // row l % 32 and the 32 consecutive K bytes starting at 32 * (l / 32); the output
 // layout is that of the 32 x 32 bf16 MFMA.  The weight fragment is the first
 // operand, so a lane's accumulators are runs of 4 consecutive output columns of
-// one token row.
+// one token row.  With an FP4 first operand (measured with one wave and chosen
+// operands): lane l holds 32 codes (16 bytes, low nibble first) of K 32 (l / 32)
+// .. +31, its scale byte scales exactly those, and the FP8 second operand then pairs
+// its bytes 0-15 with K 16 (l / 32) .. +15 and bytes 16-31 with K 32 + 16 (l / 32)
+// .. +15, so the MXFP4 path reads its activation granules in that order.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -172,7 +178,7 @@ __device__ __forceinline__ W4Tile w4a8_tile_of(int v, int nb_n, const int32_t *_
 // chunks instead, so the pipeline runs on across tiles and only the first tile pays for a
 // prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at the same
 // register set and buffer phase).
-template <bool kSwiGLU, int NTB, bool kLoop>
+template <bool kSwiGLU, bool kMX, int NTB, bool kLoop>
 __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, const int32_t *__restrict__ offsets,
                                            const int32_t *__restrict__ tiles, int n_mt, unsigned char *act,
                                            float *xsl, unsigned char *wlds, const u32x2 *lut) {
@@ -183,6 +189,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     const int nb_n = g.N / kBN;
     const int sg = tid & 15, sr = tid >> 4;
     const int srow = min(tid, kBM - 1);
+    constexpr int kSB = kMX ? 32 : 16;  // K values per weight block scale
     const bool gather = g.row_src != nullptr;
 
     // ---- addressing of one tile.  Weights: each wave streams its own 32 rows, in chunks of
@@ -207,7 +214,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
         const int64_t nw = kLoop ? (int64_t)g.E * g.N : g.N;
         r.W = __builtin_amdgcn_make_buffer_rsrc((void *)(g.Wq + w0 * (K / 2)), (short)0, (int)(nw * (K / 2)),
                                                 0x00020000);
-        r.Ws = __builtin_amdgcn_make_buffer_rsrc((void *)(g.Wbs + w0 * (K / 16)), (short)0, (int)(nw * (K / 16)),
+        r.Ws = __builtin_amdgcn_make_buffer_rsrc((void *)(g.Wbs + w0 * (K / kSB)), (short)0, (int)(nw * (K / kSB)),
                                                  0x00020000);
         const bool whole = gather || kLoop;  // rows addressed from the start of the array
         const int64_t a0 = whole ? 0 : t.row_begin;
@@ -233,7 +240,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             a.woff[i] = (uint32_t)((er + weight_row((lane >> 3) + 8 * i)) * (K / 2) + (lane & 7) * 16);
-        a.wsoff = (uint32_t)((er + weight_row(lane >> 1)) * (K / 16) + (lane & 1) * 8);
+        a.wsoff = (uint32_t)((er + weight_row(lane >> 1)) * (K / kSB) + (lane & 1) * (kKC / kSB / 2));
 #pragma unroll
         for (int i = 0; i < NTB * 2 + 1; ++i) a.src[i] = 0;
         if (gather) {
@@ -261,14 +268,20 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     auto load_w = [&](WChunk &w, const Addr &a, int c) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], c * (kKC / 2), 0);
-        w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * (kKC / 16), 0);
+        if constexpr (kMX)
+            w.s = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs.Ws, a.wsoff, c * (kKC / kSB), 0), 0u};
+        else
+            w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * (kKC / kSB), 0);
     };
     unsigned char *const wl = wlds + wave * (2 * kWSlot);  // this wave's two staging slots
     auto store_w = [&](const WChunk &w, int slot) {
         unsigned char *d = wl + slot * kWSlot;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(u32x4 *)(d + ((lane >> 3) + 8 * i) * kWRow + (lane & 7) * 16) = w.c[i];
-        *(u32x2 *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 8) = w.s;
+        if constexpr (kMX)
+            *(uint32_t *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 4) = w.s.x;
+        else
+            *(u32x2 *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 8) = w.s;
     };
     u32x4 ar[NTB * 2];
     u32x2 ars;
@@ -306,26 +319,42 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) part[tb][v] = 0.f;
-            const uint32_t sq = *(const uint32_t *)(wsr + 8 * q);
+            // block scales of this lane's K runs: NVFP4 e4m3 bytes 8q + 4h + 2t, +1 (one per 16 K),
+            // MXFP4 e8m0 byte 4q + 2h + t (one per 32 K)
+            const uint32_t sq = kMX ? *(const uint32_t *)(wsr - 4 * half + 4 * q) >> (16 * half)
+                                    : *(const uint32_t *)(wsr + 8 * q);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {  // two 64-wide MFMA steps per 128-wide block
                 const u32x4 cw = *(const u32x4 *)(wr + 64 * q + 16 * t);
-                const uint32_t sc = sq >> (16 * t);
-                const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
-                const u32x2 d0 = dequant8(cw.x, t0), d1 = dequant8(cw.y, t0);
-                const u32x2 d2 = dequant8(cw.z, t1), d3 = dequant8(cw.w, t1);
-                const i32x8 wa = {(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y,
-                                  (int)d2.x, (int)d2.y, (int)d3.x, (int)d3.y};
-                const int gk = 8 * q + 4 * half + 2 * t;  // granule of this lane's 32 K bytes
+                i32x8 wa;
+                int wscale = 127;  // e8m0 1.0: the NVFP4 weights are dequantised to fp8 here
+                if constexpr (kMX) {  // the e2m1 codes are the MFMA's fp4 operand as they are
+                    wa = i32x8{(int)cw.x, (int)cw.y, (int)cw.z, (int)cw.w, 0, 0, 0, 0};
+                    wscale = (int)((sq >> (8 * t)) & 0xffu);
+                } else {
+                    const uint32_t sc = sq >> (16 * t);
+                    const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
+                    const u32x2 d0 = dequant8(cw.x, t0), d1 = dequant8(cw.y, t0);
+                    const u32x2 d2 = dequant8(cw.z, t1), d3 = dequant8(cw.w, t1);
+                    wa = i32x8{(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y, (int)d2.x, (int)d2.y, (int)d3.x, (int)d3.y};
+                }
+                // activation granules (16 K each) of this lane's 32 fp8 bytes.  Both operands fp8: one
+                // contiguous run, the same K as the weight run.  Weights fp4: the instruction pairs
+                // the weight run of lane half h (K 32h..32h+31 of the step) with activation bytes
+                // 0-15 of half 0 and of half 1, so a lane of half h holds granules h and h + 2 of
+                // the step's weight K (measured on the device with one wave and chosen operands)
+                const int gk_lo = kMX ? 8 * q + 2 * t + half : 8 * q + 4 * half + 2 * t;
+                const int gk_hi = kMX ? gk_lo + 4 : gk_lo + 1;
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     const int r = tb * 32 + (lane & 31);
-                    const u32x4 lo = *(const u32x4 *)(ab + r * kKC + aslot(r, gk) * 16);
-                    const u32x4 hi = *(const u32x4 *)(ab + r * kKC + aslot(r, gk + 1) * 16);
+                    const u32x4 lo = *(const u32x4 *)(ab + r * kKC + aslot(r, gk_lo) * 16);
+                    const u32x4 hi = *(const u32x4 *)(ab + r * kKC + aslot(r, gk_hi) * 16);
                     const i32x8 xb = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    part[tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, part[tb], 0, 0, 0, 127, 0,
-                                                                               127);
+                    // operand formats: weights fp4 e2m1 (4) or fp8 e4m3 (0), activations fp8 e4m3
+                    part[tb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wa, xb, part[tb], kMX ? 4 : 0, 0, 0,
+                                                                               wscale, 0, 127);
                 }
             }
 #pragma unroll
@@ -472,10 +501,10 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     __shared__ u32x2 lut[256];                                                                         \
     __shared__ float xsl[2 * kBM * 2]; /* activation scales of the staged chunks [buf][row][block] */ \
     __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot]; /* 2 slots per wave */ \
-    lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after the first barrier of a tile */
+    if constexpr (!kMX) lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after a tile's first barrier */
 
 // one tile per workgroup; its token-block count from its own rows
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
@@ -484,18 +513,18 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
     const W4Tile t = w4a8_tile_of(blockIdx.x, g.N / kBN, offsets, tiles, n_mt);
     if (!t.valid) return;
     if (t.rows > 32)
-        w4a8_tiles<kSwiGLU, 2, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 2, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
     else
-        w4a8_tiles<kSwiGLU, 1, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
 }
 
 // persistent (at most 32 rows per tile): workgroup b takes virtual blocks b, b + gridDim.x, ...
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kernel(
     W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    w4a8_tiles<kSwiGLU, 1, true>(g, blockIdx.x, gridDim.x, offsets, tiles, n_tiles[0], act, xsl, wlds, lut);
+    w4a8_tiles<kSwiGLU, kMX, 1, true>(g, blockIdx.x, gridDim.x, offsets, tiles, n_tiles[0], act, xsl, wlds, lut);
 }
 #undef TPG_W4A8_LDS
 
@@ -566,15 +595,23 @@ W4Launch w4_launch(int64_t max_tiles, int N, int K, int E, int a_rows, int T) {
     return {std::min<int64_t>(blocks, 2 * (int64_t)n_cu), true};
 }
 
-template <bool kSwiGLU>
-void launch_w4a8_gemm(const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
-                      const int32_t *n_tiles, hipStream_t s) {
+template <bool kSwiGLU, bool kMX>
+void launch_w4a8_gemm_as(const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
+                         const int32_t *n_tiles, hipStream_t s) {
     if (l.persistent)
-        hipLaunchKernelGGL(grouped_gemm_w4a8_persistent_kernel<kSwiGLU>, dim3(l.grid), dim3(kThreads), 0, s, g,
+        hipLaunchKernelGGL((grouped_gemm_w4a8_persistent_kernel<kSwiGLU, kMX>), dim3(l.grid), dim3(kThreads), 0, s, g,
                            offsets, tiles, n_tiles);
     else
-        hipLaunchKernelGGL(grouped_gemm_w4a8_kernel<kSwiGLU>, dim3(l.grid), dim3(kThreads), 0, s, g, offsets, tiles,
-                           n_tiles);
+        hipLaunchKernelGGL((grouped_gemm_w4a8_kernel<kSwiGLU, kMX>), dim3(l.grid), dim3(kThreads), 0, s, g, offsets,
+                           tiles, n_tiles);
+}
+template <bool kSwiGLU>
+void launch_w4a8_gemm(bool mx, const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
+                      const int32_t *n_tiles, hipStream_t s) {
+    if (mx)
+        launch_w4a8_gemm_as<kSwiGLU, true>(l, g, offsets, tiles, n_tiles, s);
+    else
+        launch_w4a8_gemm_as<kSwiGLU, false>(l, g, offsets, tiles, n_tiles, s);
 }
 }  // namespace
 
@@ -590,7 +627,8 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     W4Args g1{x_perm, x_perm_scale, row_src, p.k, row_src ? p.T : S, (const uint8_t *)w.w1,
               (const uint8_t *)w.w1_bscale, w.w1_gscale, H, 2 * I, I, p.glu_interleave, p.E, p.swiglu_clamp, h32,
               nullptr, 0};
-    launch_w4a8_gemm<true>(l1, g1, offsets, tiles, n_tiles, s);
+    const bool mx = p.prec == MOE_PREC_W4A8_MX;
+    launch_w4a8_gemm<true>(mx, l1, g1, offsets, tiles, n_tiles, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t items = n_slots(p) * (I / 128);
@@ -599,7 +637,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     if (err != hipSuccess) return err;
     W4Args g2{h8, hs, nullptr, 1, S, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale,
               w.w2_gscale, I, H, I, 0, p.E, 0.0f, nullptr, y_perm, H};
-    launch_w4a8_gemm<false>(l2, g2, offsets, tiles, n_tiles, s);
+    launch_w4a8_gemm<false>(mx, l2, g2, offsets, tiles, n_tiles, s);
     return hipGetLastError();
 }
 

@@ -21,9 +21,10 @@ int check_problem(const moe_problem *p) {
     if ((int64_t)p->T * p->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     // one expert matrix must stay below 2 GB (32-bit byte offsets inside a matrix)
     if ((int64_t)p->H * p->I * 4 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
-    if (p->prec != MOE_PREC_BF16 && p->prec != MOE_PREC_W4A8) return MOE_ERR_UNSUPPORTED;
+    if (p->prec != MOE_PREC_BF16 && p->prec != MOE_PREC_W4A8 && p->prec != MOE_PREC_W4A8_MX)
+        return MOE_ERR_UNSUPPORTED;
     // W4A8 stages K 256 at a time: H and I multiples of 256
-    if (p->prec == MOE_PREC_W4A8 && (p->H % 256 != 0 || p->I % 256 != 0)) return MOE_ERR_SHAPE;
+    if (p->prec != MOE_PREC_BF16 && (p->H % 256 != 0 || p->I % 256 != 0)) return MOE_ERR_SHAPE;
     if (p->glu_interleave != 0 && p->glu_interleave != 32) return MOE_ERR_UNSUPPORTED;
     if (!(p->swiglu_clamp >= 0.0f) || p->swiglu_clamp > 3.0e38f) return MOE_ERR_UNSUPPORTED;  // also rejects NaN
     return MOE_OK;
@@ -35,7 +36,8 @@ int hip_status(hipError_t e) {
     return MOE_ERR_HIP;
 }
 
-bool is_w4a8(const moe_problem *p) { return p->prec == MOE_PREC_W4A8; }
+// fp8 activations with fp4 weights (NVFP4 or MXFP4)
+bool is_w4a8(const moe_problem *p) { return p->prec == MOE_PREC_W4A8 || p->prec == MOE_PREC_W4A8_MX; }
 
 int check_weights(const moe_weights *w, const moe_problem *p) {
     if (!w || !w->w1 || !w->w2) return MOE_ERR_NULL;

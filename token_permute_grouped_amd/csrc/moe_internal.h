@@ -42,7 +42,7 @@ constexpr int kGemmBMW4A8 = 64;
 
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
-inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_W4A8 ? kGemmBMW4A8 : kGemmBM; }
+inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? kGemmBM : kGemmBMW4A8; }
 // upper bound of sum_e ceil(count_e / bm) over any routing
 inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + gemm_bm(p) - 1) / gemm_bm(p) + p.E; }
 
