@@ -9,7 +9,10 @@ GEMM1 + SwiGLU, GEMM2, combine, with every input already resident in HBM.
 Timing: W untimed warm-up steps, then K moe_forward steps bracketed by device
 synchronisation and HIP events on the library's stream (ms_per_step, value).  Then K
 single forwards, each after a 512 MB write that flushes the caches (median:
-cold_cache_ms_per_step).  The
+cold_cache_ms_per_step).  Then one forward captured in a HIP graph and replayed K times
+(median graph_ms_per_step), and K times after a flush each (graph_cold_ms_per_step: the
+FlashInfer MegaMoE Performance section's method, one MoE call per graph, cold cache
+before each call).  The
 per-stage durations come from K further steps through moe_forward_timed (same
 kernels plus a HIP event at every stage boundary), measured live in the same run.
 On bf16 data the forward folds the row gather into GEMM1; the permute kernel's own
@@ -250,9 +253,38 @@ def main():
         cold.append(hip.ms(c0, c1))
         hip.destroy(c0)
         hip.destroy(c1)
-    del flush
     cold_ms = float(np.median(cold))
     log(f"cold caches: median {cold_ms:.4f} ms per forward over {args.steps}")
+
+    # one forward per HIP graph: captured once (torch's graph capture on its own stream; the
+    # library enqueues on torch's current stream, allocates nothing and records no memset),
+    # replayed K times warm and K times each after the 512 MB flush
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_runs = {False: [], True: []}
+    for flushed in (False, True):
+        for i in range(args.steps):
+            if flushed:
+                flush.fill_(i & 0xFF)
+            c0, c1 = hip.create(), hip.create()
+            hip.record(c0, stream)
+            graph.replay()
+            hip.record(c1, stream)
+            torch.cuda.synchronize()
+            graph_runs[flushed].append(hip.ms(c0, c1))
+            hip.destroy(c0)
+            hip.destroy(c1)
+    del graph, flush
+    graph_ms, graph_cold_ms = float(np.median(graph_runs[False])), float(np.median(graph_runs[True]))
+    log(f"graph replay: median {graph_ms:.4f} ms warm, {graph_cold_ms:.4f} ms with the caches flushed")
 
     # stage breakdown: K more steps through moe_forward_timed (same kernels plus a HIP event at
     # every stage boundary; each event adds a few microseconds, visible only at small T)
@@ -373,13 +405,16 @@ def main():
         "gather_hbm_frac": round(gbs(gather_bytes, permute_gather_ms) / PEAK_HBM_GBS, 4),
         "gather_after_forward_ms": round(permute_gather_after_fwd_ms, 4),
         "gather_after_forward_hbm_frac": round(gbs(gather_bytes, permute_gather_after_fwd_ms) / PEAK_HBM_GBS, 4),
-        "gather_in_forward": "separate kernel" if w4 else "folded into GEMM1 (x read through row_src)",
+        "gather_in_forward": ("folded into GEMM1 (x read through row_src)" if T * H * act_b < 2 ** 31
+                              else "separate kernel"),
         "permute_tables_ms": round(permute_tables_ms, 4),
         "combine_gbs": round(gbs(combine_bytes, stage_ms["combine"]), 1),
         "combine_hbm_frac": round(gbs(combine_bytes, stage_ms["combine"]) / PEAK_HBM_GBS, 4),
         "stage_ms": {k_: round(v, 4) for k_, v in stage_ms.items()},
         "wall_ms_per_step": round(wall_ms, 4),
         "cold_cache_ms_per_step": round(cold_ms, 4),  # median, caches flushed before each forward
+        "graph_ms_per_step": round(graph_ms, 4),  # median replay of one captured forward
+        "graph_cold_ms_per_step": round(graph_cold_ms, 4),  # the same, caches flushed before each
         "roofline": roofline,
         "cpu_baseline": None,
     }
