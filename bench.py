@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="skewed")
     ap.add_argument("--tokens", type=int, default=None, help="token count override (e.g. the W4A8 sweep points)")
+    ap.add_argument("--w4-layout", choices=("tiled", "rows"), default="tiled",
+                    help="W4A8 weight storage: tiled (prepared once by moe_w4a8_tile_weights) or row-major")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -205,7 +207,15 @@ def main():
                          cfg.swiglu_clamp)
     d = {k: dt(inp.get(k)) for k in ("logits", "slot_drop", "x", "x_scale", "w1", "w1_bscale", "w1_gscale", "w2",
                                       "w2_bscale", "w2_gscale")}
-    wts = tpg.make_weights(d["w1"], d["w2"], d["w1_bscale"], d["w1_gscale"], d["w2_bscale"], d["w2_gscale"])
+    layout = tpg.MOE_W4_LAYOUT_ROWS
+    if w4 and args.w4_layout == "tiled":
+        # the weights prepared once, as a deployment would at load time (moe_w4a8_tile_weights)
+        for m, (n, kk) in (("w1", (2 * cfg.I, cfg.H)), ("w2", (cfg.H, cfg.I))):
+            ct, st = torch.empty_like(d[m]), torch.empty_like(d[m + "_bscale"])
+            tpg.moe_w4a8_tile_weights(d[m], d[m + "_bscale"], ct, st, cfg.E, n, kk, p.prec)
+            d[m], d[m + "_bscale"] = ct, st
+        layout = tpg.MOE_W4_LAYOUT_TILED
+    wts = tpg.make_weights(d["w1"], d["w2"], d["w1_bscale"], d["w1_gscale"], d["w2_bscale"], d["w2_gscale"], layout)
     ws = torch.empty(tpg.moe_workspace_bytes(p, tpg.MOE_WS_FORWARD), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
     torch.cuda.synchronize()
@@ -415,6 +425,7 @@ def main():
         "cold_cache_ms_per_step": round(cold_ms, 4),  # median, caches flushed before each forward
         "graph_ms_per_step": round(graph_ms, 4),  # median replay of one captured forward
         "graph_cold_ms_per_step": round(graph_cold_ms, 4),  # the same, caches flushed before each
+        "weight_layout": (args.w4_layout if w4 else "rows"),
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -99,7 +99,14 @@ typedef struct moe_problem {
 /* Expert weights (device pointers, borrowed).  bf16: only w1 and w2 are used.
  * w4a8: w1 uint8 [E][2I][H/2], w1_bscale uint8 [E][2I][H/16], w1_gscale fp32 [E];
  *       w2 uint8 [E][H][I/2],  w2_bscale uint8 [E][H][I/16],  w2_gscale fp32 [E].
- * w4a8_mx: the same with w1_bscale uint8 [E][2I][H/32], w2_bscale uint8 [E][H][I/32]. */
+ * w4a8_mx: the same with w1_bscale uint8 [E][2I][H/32], w2_bscale uint8 [E][H][I/32].
+ * w4_layout (W4A8 and W4A8_MX only) says how the codes and block scales of each
+ * matrix are stored: MOE_W4_LAYOUT_ROWS, the row-major arrays above, or
+ * MOE_W4_LAYOUT_TILED, the same bytes regrouped by moe_w4a8_tile_weights so that
+ * the GEMMs stream every 32-row, 256-wide piece as one contiguous run (the
+ * FlashInfer Usage section likewise prepares weights once with a transform
+ * function).  Both give bitwise the same results. */
+enum { MOE_W4_LAYOUT_ROWS = 0, MOE_W4_LAYOUT_TILED = 1 };
 typedef struct moe_weights {
     const void *w1;
     const void *w1_bscale;
@@ -107,6 +114,7 @@ typedef struct moe_weights {
     const void *w2;
     const void *w2_bscale;
     const float *w2_gscale;
+    int32_t w4_layout;
 } moe_weights;
 
 /* Host only.  Bytes of device workspace the given call needs for this problem
@@ -208,6 +216,19 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
  * block scale, outside the defined domain, gives the NaN code with the product's
  * sign. */
 int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
+
+/* W4A8 weight preparation: one matrix stack of E experts with N rows and K columns
+ * (N a multiple of 32, K of 256), row-major codes uint8 [E][N][K/2] and block scales
+ * uint8 [E][N][K/bs] (bs = 16 for MOE_PREC_W4A8, 32 for MOE_PREC_W4A8_MX), rewritten
+ * into MOE_W4_LAYOUT_TILED: for every expert e, 32-row block b, 256-wide K piece c and
+ * row r < 32,
+ *   codes_tiled [e][b][c][r][0..127]    = codes [e][32 b + r][128 c .. 128 c + 127]
+ *   bscale_tiled[e][b][c][r][0..256/bs) = bscale[e][32 b + r][(256/bs) c ..]
+ * (the same array sizes).  Device pointers; the outputs must not overlap the inputs;
+ * enqueued on `stream`.  Call it once per matrix (W1: N = 2I, K = H; W2: N = H, K =
+ * I) when the weights are loaded. */
+int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled,
+                          int32_t E, int32_t N, int32_t K, int32_t prec, void *stream);
 
 #ifdef __cplusplus
 }

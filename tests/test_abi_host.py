@@ -123,6 +123,31 @@ def test_zero_tokens_returns_ok_without_touching_anything():
     assert lib.moe_forward(None, None, None, None, w, p, None, None, 0, None) == tpg.MOE_OK
 
 
+def test_w4a8_tile_weights_argument_checks():
+    lib = tpg.load()
+    A, B, C, D = 1 << 20, 2 << 20, 3 << 20, 4 << 20  # disjoint fake device ranges (never touched)
+    ok_shape = (2, 64, 512)
+    assert lib.moe_w4a8_tile_weights(None, B, C, D, *ok_shape, tpg.MOE_PREC_W4A8, None) == tpg.MOE_ERR_NULL
+    assert lib.moe_w4a8_tile_weights(A, B, C, None, *ok_shape, tpg.MOE_PREC_W4A8, None) == tpg.MOE_ERR_NULL
+    assert lib.moe_w4a8_tile_weights(A, B, C, D, *ok_shape, tpg.MOE_PREC_BF16, None) == tpg.MOE_ERR_UNSUPPORTED
+    for E, N, K in ((0, 64, 512), (2, 48, 512), (2, 64, 384), (2, 64, 128)):
+        assert lib.moe_w4a8_tile_weights(A, B, C, D, E, N, K, tpg.MOE_PREC_W4A8_MX, None) == tpg.MOE_ERR_SHAPE
+    # outputs overlapping the inputs (2 * 64 * 256 = 32 KB of codes from A)
+    assert lib.moe_w4a8_tile_weights(A, B, A + 4096, D, *ok_shape, tpg.MOE_PREC_W4A8, None) == tpg.MOE_ERR_UNSUPPORTED
+    assert lib.moe_w4a8_tile_weights(A, B, C, B, *ok_shape, tpg.MOE_PREC_W4A8, None) == tpg.MOE_ERR_UNSUPPORTED
+
+
+def test_unknown_weight_layout_is_rejected():
+    lib = tpg.load()
+    for prec in (tpg.MOE_PREC_W4A8, tpg.MOE_PREC_W4A8_MX):
+        p = ctypes.byref(_p(prec=prec, H=256))
+        w = tpg.Weights(*[FAKE] * 6, 7)
+        assert lib.moe_forward(FAKE, None, FAKE, FAKE, ctypes.byref(w), p, FAKE, FAKE, 1 << 40,
+                               None) == tpg.MOE_ERR_UNSUPPORTED
+        assert lib.moe_grouped_ffn(FAKE, FAKE, FAKE, ctypes.byref(w), p, FAKE, FAKE, 1 << 40,
+                                   None) == tpg.MOE_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes():
     big = _p(T=32768, H=7168, I=2048, E=32, k=8, glu_interleave=32)
     n = tpg.moe_workspace_bytes(big, tpg.MOE_WS_FORWARD)

@@ -1,0 +1,101 @@
+"""GPU checks of the tiled W4A8 weight layout (MOE_W4_LAYOUT_TILED).
+
+moe_w4a8_tile_weights must regroup the bytes exactly as include/moe.h defines (compared
+with a numpy regrouping of the same arrays, bit for bit), and a forward or grouped FFN on
+tiled weights must give bitwise the output of the same call on row-major weights (the
+GEMMs see the same values in the same order; only their addresses change).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import token_permute_grouped_amd as tpg
+from moe_synth import CONFIGS, MoeConfig, generate
+from tests._gpu import DEV, DeviceProblem, bf16_host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def tile_host(codes: np.ndarray, bscale: np.ndarray, bs: int):
+    """the layout's definition: [e][b][c][r][bytes] from row-major [e][32 b + r][bytes of piece c]"""
+    E, N, Kh = codes.shape
+    nc = Kh // 128
+    c = codes.reshape(E, N // 32, 32, nc, 128).transpose(0, 1, 3, 2, 4)
+    s = bscale.reshape(E, N // 32, 32, nc, 256 // bs).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(c).reshape(codes.shape), np.ascontiguousarray(s).reshape(bscale.shape)
+
+
+def tile_device(codes: torch.Tensor, bscale: torch.Tensor, prec: int):
+    E, N, Kh = codes.shape
+    ct, st = torch.empty_like(codes), torch.empty_like(bscale)
+    tpg.moe_w4a8_tile_weights(codes, bscale, ct, st, E, N, 2 * Kh, prec)
+    return ct, st
+
+
+@pytest.mark.parametrize("prec,shape", [("w4a8", (3, 64, 512)), ("w4a8_mx", (3, 64, 512)),
+                                        ("w4a8", (2, 96, 1280)), ("w4a8_mx", (1, 32, 256)),
+                                        ("w4a8_mx", (5, 160, 768))])
+def test_tile_weights_regroups_bytes_exactly(prec, shape):
+    E, N, K = shape
+    bs = 32 if prec == "w4a8_mx" else 16
+    rng = np.random.default_rng(N + K)
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    bscale = rng.integers(0, 256, size=(E, N, K // bs), dtype=np.uint8)
+    ct, st = tile_device(to_dev(codes), to_dev(bscale), tpg.PRECISIONS[prec])
+    want_c, want_s = tile_host(codes, bscale, bs)
+    assert np.array_equal(ct.cpu().numpy(), want_c)
+    assert np.array_equal(st.cpu().numpy(), want_s)
+
+
+CASES = {
+    "nv_tiny": MoeConfig("nv_tiny", T=64, H=256, I=256, E=8, k=2, prec="w4a8", swiglu_clamp=10.0),
+    "mx_interleaved_drop": MoeConfig("mx_interleaved_drop", T=100, H=512, I=512, E=6, k=3, prec="w4a8_mx",
+                                     glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    "nv_ragged": MoeConfig("nv_ragged", T=300, H=768, I=768, E=5, k=2, prec="w4a8"),
+    # persistent GEMMs (T <= 32, K a multiple of 1024), several tiles per workgroup
+    "nv_persistent": MoeConfig("nv_persistent", T=32, H=1024, I=1024, E=64, k=8, prec="w4a8",
+                               glu_interleave=32, swiglu_clamp=10.0),
+    "mx_persistent": MoeConfig("mx_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8_mx",
+                               swiglu_clamp=10.0),
+}
+
+
+def _tiled_problem(inp):
+    """a DeviceProblem whose weights are the tiled copies of inp's"""
+    cfg = inp["cfg"]
+    d = DeviceProblem(inp)
+    prec = tpg.PRECISIONS[cfg.prec]
+    w = dict(d.w)
+    w["w1"], w["w1_bscale"] = tile_device(d.w["w1"], d.w["w1_bscale"], prec)
+    w["w2"], w["w2_bscale"] = tile_device(d.w["w2"], d.w["w2_bscale"], prec)
+    d.w_tiled = w
+    d.weights = tpg.make_weights(w["w1"], w["w2"], w["w1_bscale"], w["w1_gscale"], w["w2_bscale"], w["w2_gscale"],
+                                 tpg.MOE_W4_LAYOUT_TILED)
+    return d
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_and_grouped_ffn_on_tiled_weights_equal_row_major(name):
+    cfg = CASES[name]
+    print(f"[gpu w4 layout] {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec}", flush=True)
+    inp = generate(cfg, seed=0)
+    rows, tiled = DeviceProblem(inp), _tiled_problem(inp)
+    assert (bf16_host(rows.forward()) == bf16_host(tiled.forward())).all()
+    idx, _ = rows.route()
+    offsets, _, _, x_perm, x_perm_scale = rows.permute(idx)
+    y_rows = bf16_host(rows.grouped_ffn(x_perm, x_perm_scale, offsets))
+    y_tiled = bf16_host(tiled.grouped_ffn(x_perm, x_perm_scale, offsets))
+    R = int(offsets[-1].item())
+    assert (y_rows[:R] == y_tiled[:R]).all()
+
+
+@pytest.mark.parametrize("wl,T", [("w4a8", 1), ("w4a8", 256), ("w4a8_mx", 16), ("w4a8_mx", 256)])
+def test_full_layer_forward_on_tiled_weights_equals_row_major(wl, T):
+    print(f"[gpu w4 layout] {wl} layer T={T}", flush=True)
+    inp = generate(CONFIGS[wl], seed=0, T=T)
+    rows, tiled = DeviceProblem(inp), _tiled_problem(inp)
+    a, b = bf16_host(rows.forward()), bf16_host(tiled.forward())
+    torch.cuda.synchronize()
+    assert (a == b).all()

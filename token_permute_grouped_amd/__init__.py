@@ -18,12 +18,14 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE
 MOE_PREC_BF16, MOE_PREC_W4A8, MOE_PREC_W4A8_MX = 0, 1, 2
 # precision of a synthetic workload's `prec` name
 PRECISIONS = {"bf16": MOE_PREC_BF16, "w4a8": MOE_PREC_W4A8, "w4a8_mx": MOE_PREC_W4A8_MX}
+MOE_W4_LAYOUT_ROWS, MOE_W4_LAYOUT_TILED = 0, 1
 MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_workspace_bytes", "moe_status_str", "moe_last_hip_error", "moe_route_topk", "moe_permute",
     "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_w4a8_dequant_table",
+    "moe_w4a8_tile_weights",
 )
 MOE_N_STAGE_EVENTS = 8
 MOE_N_PERMUTE_EVENTS = 3
@@ -45,7 +47,8 @@ class Problem(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w1_bscale", ctypes.c_void_p), ("w1_gscale", ctypes.c_void_p),
-                ("w2", ctypes.c_void_p), ("w2_bscale", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p)]
+                ("w2", ctypes.c_void_p), ("w2_bscale", ctypes.c_void_p), ("w2_gscale", ctypes.c_void_p),
+                ("w4_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -79,8 +82,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P]
     lib.moe_forward_timed.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P, ctypes.POINTER(ctypes.c_void_p)]
     lib.moe_w4a8_dequant_table.argtypes = [P, P]
+    lib.moe_w4a8_tile_weights.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
     for name in ("moe_route_topk", "moe_permute", "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward",
-                 "moe_forward_timed", "moe_w4a8_dequant_table"):
+                 "moe_forward_timed", "moe_w4a8_dequant_table", "moe_w4a8_tile_weights"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -120,8 +124,10 @@ def make_problem(T, H, I, E, k, prec=MOE_PREC_BF16, glu_interleave=0, swiglu_cla
     return Problem(T, H, I, E, k, prec, glu_interleave, swiglu_clamp)
 
 
-def make_weights(w1, w2, w1_bscale=None, w1_gscale=None, w2_bscale=None, w2_gscale=None) -> Weights:
-    return Weights(_ptr(w1), _ptr(w1_bscale), _ptr(w1_gscale), _ptr(w2), _ptr(w2_bscale), _ptr(w2_gscale))
+def make_weights(w1, w2, w1_bscale=None, w1_gscale=None, w2_bscale=None, w2_gscale=None,
+                 w4_layout=MOE_W4_LAYOUT_ROWS) -> Weights:
+    return Weights(_ptr(w1), _ptr(w1_bscale), _ptr(w1_gscale), _ptr(w2), _ptr(w2_bscale), _ptr(w2_gscale),
+                   w4_layout)
 
 
 def moe_workspace_bytes(problem: Problem, which: int = MOE_WS_FORWARD) -> int:
@@ -186,6 +192,12 @@ def moe_forward_timed(logits, slot_drop, x, x_scale, weights: Weights, problem: 
     _check("moe_forward_timed", load().moe_forward_timed(_ptr(logits), _ptr(slot_drop), _ptr(x), _ptr(x_scale),
                                                          ctypes.byref(weights), ctypes.byref(problem), _ptr(out),
                                                          _ptr(ws), ws_bytes, _stream(stream), ev))
+
+
+def moe_w4a8_tile_weights(codes, bscale, codes_tiled, bscale_tiled, E, N, K, prec, stream=None):
+    """row-major W4A8 codes [E][N][K/2] and block scales -> MOE_W4_LAYOUT_TILED (see include/moe.h)"""
+    _check("moe_w4a8_tile_weights", load().moe_w4a8_tile_weights(_ptr(codes), _ptr(bscale), _ptr(codes_tiled),
+                                                                 _ptr(bscale_tiled), E, N, K, prec, _stream(stream)))
 
 
 def moe_w4a8_dequant_table(out8, stream=None):

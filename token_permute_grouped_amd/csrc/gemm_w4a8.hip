@@ -120,7 +120,12 @@ struct W4Args {
     const int32_t *row_src;  // NULL, or [S]: row r reads token row row_src[r] / gather_k
     int gather_k, a_rows;    // rows of A8 / As: T with row_src, else S
     const uint8_t *Wq;   // [E][N][K/2] e2m1 codes, low nibble = even k
-    const uint8_t *Wbs;  // [E][N][K/16] e4m3 block scales
+    const uint8_t *Wbs;  // [E][N][K/16] e4m3 block scales (MXFP4: [E][N][K/32] e8m0)
+    // Bytes between consecutive rows of a 32-row block and between consecutive 256-wide K
+    // pieces of one row, for the codes (w_) and the block scales (s_): row-major storage
+    // (pitch K/2, step 128) or the tiled layout (pitch 128, step 4096: a block's piece is one
+    // contiguous 4 KB run).  A 32-row block occupies the same bytes in both.
+    int w_pitch, w_step, s_pitch, s_step;
     const float *Wgs;    // [E] global scales
     int K, N, I, il, E;
     float clamp;
@@ -237,10 +242,12 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
             return t.nt * kBN + wave * 32 + rl;
         };
         const int er = kLoop ? t.e * g.N : 0;  // expert's first row within the descriptor
+        // a wave's 32 weight rows are one 32-row block of the matrix (weight_row(r) = weight_row(0) + r)
+        const int blk = er + weight_row(0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            a.woff[i] = (uint32_t)((er + weight_row((lane >> 3) + 8 * i)) * (K / 2) + (lane & 7) * 16);
-        a.wsoff = (uint32_t)((er + weight_row(lane >> 1)) * (K / kSB) + (lane & 1) * (kKC / kSB / 2));
+            a.woff[i] = (uint32_t)(blk * (K / 2) + ((lane >> 3) + 8 * i) * g.w_pitch + (lane & 7) * 16);
+        a.wsoff = (uint32_t)(blk * (K / kSB) + (lane >> 1) * g.s_pitch + (lane & 1) * (kKC / kSB / 2));
 #pragma unroll
         for (int i = 0; i < NTB * 2 + 1; ++i) a.src[i] = 0;
         if (gather) {
@@ -267,11 +274,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     Rs rs;
     auto load_w = [&](WChunk &w, const Addr &a, int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], c * (kKC / 2), 0);
+        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], c * g.w_step, 0);
         if constexpr (kMX)
-            w.s = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs.Ws, a.wsoff, c * (kKC / kSB), 0), 0u};
+            w.s = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs.Ws, a.wsoff, c * g.s_step, 0), 0u};
         else
-            w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * (kKC / kSB), 0);
+            w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * g.s_step, 0);
     };
     unsigned char *const wl = wlds + wave * (2 * kWSlot);  // this wave's two staging slots
     auto store_w = [&](const WChunk &w, int slot) {
@@ -615,6 +622,18 @@ void launch_w4a8_gemm(bool mx, const W4Launch &l, const W4Args &g, const int32_t
 }
 }  // namespace
 
+namespace {
+// code and scale strides of one matrix stack with K columns in the given layout (see W4Args)
+void set_layout(W4Args &g, int K, bool mx, int layout) {
+    const int sb = mx ? 32 : 16;  // K values per block scale
+    const bool tiled = layout == MOE_W4_LAYOUT_TILED;
+    g.w_pitch = tiled ? kKC / 2 : K / 2;
+    g.w_step = tiled ? 32 * (kKC / 2) : kKC / 2;
+    g.s_pitch = tiled ? kKC / sb : K / sb;
+    g.s_step = tiled ? 32 * (kKC / sb) : kKC / sb;
+}
+}  // namespace
+
 hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
                                    const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
                                    int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
@@ -622,12 +641,26 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     const int H = p.H, I = p.I;
     if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
     const int S = (int)n_slots(p);
+    const bool mx = p.prec == MOE_PREC_W4A8_MX;
     const W4Launch l1 = w4_launch(max_tiles, 2 * I, H, p.E, row_src ? p.T : S, p.T),
                    l2 = w4_launch(max_tiles, H, I, p.E, S, p.T);
-    W4Args g1{x_perm, x_perm_scale, row_src, p.k, row_src ? p.T : S, (const uint8_t *)w.w1,
-              (const uint8_t *)w.w1_bscale, w.w1_gscale, H, 2 * I, I, p.glu_interleave, p.E, p.swiglu_clamp, h32,
-              nullptr, 0};
-    const bool mx = p.prec == MOE_PREC_W4A8_MX;
+    W4Args g1{};
+    g1.A8 = x_perm;
+    g1.As = x_perm_scale;
+    g1.row_src = row_src;
+    g1.gather_k = p.k;
+    g1.a_rows = row_src ? p.T : S;
+    g1.Wq = (const uint8_t *)w.w1;
+    g1.Wbs = (const uint8_t *)w.w1_bscale;
+    g1.Wgs = w.w1_gscale;
+    g1.K = H;
+    g1.N = 2 * I;
+    g1.I = I;
+    g1.il = p.glu_interleave;
+    g1.E = p.E;
+    g1.clamp = p.swiglu_clamp;
+    g1.Hout = h32;
+    set_layout(g1, H, mx, w.w4_layout);
     launch_w4a8_gemm<true>(mx, l1, g1, offsets, tiles, n_tiles, s);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -635,9 +668,56 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    W4Args g2{h8, hs, nullptr, 1, S, (const uint8_t *)w.w2, (const uint8_t *)w.w2_bscale,
-              w.w2_gscale, I, H, I, 0, p.E, 0.0f, nullptr, y_perm, H};
+    W4Args g2{};
+    g2.A8 = h8;
+    g2.As = hs;
+    g2.gather_k = 1;
+    g2.a_rows = S;
+    g2.Wq = (const uint8_t *)w.w2;
+    g2.Wbs = (const uint8_t *)w.w2_bscale;
+    g2.Wgs = w.w2_gscale;
+    g2.K = I;
+    g2.N = H;
+    g2.I = I;
+    g2.E = p.E;
+    g2.Yout = y_perm;
+    g2.ldy = H;
+    set_layout(g2, I, mx, w.w4_layout);
     launch_w4a8_gemm<false>(mx, l2, g2, offsets, tiles, n_tiles, s);
+    return hipGetLastError();
+}
+
+// MOE_W4_LAYOUT_TILED from row-major codes and block scales: one thread per destination unit
+// (16 code bytes, or 8 scale bytes); destination unit d of a 32-row block's 256-wide piece c
+// holds row r, bytes 16 j (8 j) of that row's piece
+__global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                           int64_t units, int unit_bytes, int piece_units,
+                                                           int row_bytes, int n_pieces) {
+    const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (d >= units) return;
+    const int j = (int)(d % piece_units);
+    const int r = (int)((d / piece_units) % 32);
+    const int64_t c = (d / (piece_units * 32)) % n_pieces;
+    const int64_t blk = d / ((int64_t)piece_units * 32 * n_pieces);  // expert * (N / 32) + block
+    const int64_t from = (blk * 32 + r) * row_bytes + c * (piece_units * unit_bytes) + j * unit_bytes;
+    if (unit_bytes == 16)
+        *(uint4 *)(dst + d * 16) = *(const uint4 *)(src + from);
+    else
+        *(uint2 *)(dst + d * 8) = *(const uint2 *)(src + from);
+}
+
+hipError_t launch_tile_weights(const uint8_t *codes, const uint8_t *bscale, uint8_t *codes_tiled,
+                               uint8_t *bscale_tiled, int E, int N, int K, bool mx, hipStream_t s) {
+    const int sb = mx ? 32 : 16, n_pieces = K / kKC;
+    const int64_t rows = (int64_t)E * N;
+    const int64_t cu = rows * (K / 2) / 16;      // 16-byte code units
+    const int64_t su = rows * (K / sb) / 8;      // 8-byte scale units
+    hipLaunchKernelGGL(tile_weights_kernel, dim3((cu + 255) / 256), dim3(256), 0, s, codes, codes_tiled, cu, 16,
+                       (kKC / 2) / 16, K / 2, n_pieces);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(tile_weights_kernel, dim3((su + 255) / 256), dim3(256), 0, s, bscale, bscale_tiled, su, 8,
+                       (kKC / sb) / 8, K / sb, n_pieces);
     return hipGetLastError();
 }
 

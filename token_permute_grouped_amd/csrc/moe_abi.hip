@@ -42,6 +42,8 @@ bool is_w4a8(const moe_problem *p) { return p->prec == MOE_PREC_W4A8 || p->prec 
 int check_weights(const moe_weights *w, const moe_problem *p) {
     if (!w || !w->w1 || !w->w2) return MOE_ERR_NULL;
     if (is_w4a8(p) && (!w->w1_bscale || !w->w1_gscale || !w->w2_bscale || !w->w2_gscale)) return MOE_ERR_NULL;
+    if (is_w4a8(p) && w->w4_layout != MOE_W4_LAYOUT_ROWS && w->w4_layout != MOE_W4_LAYOUT_TILED)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -322,6 +324,24 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
 int moe_w4a8_dequant_table(uint8_t *out8, void *stream) {
     if (!out8) return MOE_ERR_NULL;
     return hip_status(launch_w4a8_dequant_table(out8, (hipStream_t)stream));
+}
+
+int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled, int32_t E,
+                          int32_t N, int32_t K, int32_t prec, void *stream) {
+    if (!codes || !bscale || !codes_tiled || !bscale_tiled) return MOE_ERR_NULL;
+    if (prec != MOE_PREC_W4A8 && prec != MOE_PREC_W4A8_MX) return MOE_ERR_UNSUPPORTED;
+    if (E < 1 || N < 32 || N % 32 != 0 || K < 256 || K % 256 != 0) return MOE_ERR_SHAPE;
+    const bool mx = prec == MOE_PREC_W4A8_MX;
+    const uint64_t nc = (uint64_t)E * N * (K / 2), ns = (uint64_t)E * N * (K / (mx ? 32 : 16));
+    auto overlap = [](const void *a, uint64_t na, const void *b, uint64_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + nb && y < x + na;
+    };
+    if (overlap(codes, nc, codes_tiled, nc) || overlap(bscale, ns, bscale_tiled, ns) ||
+        overlap(codes, nc, bscale_tiled, ns) || overlap(bscale, ns, codes_tiled, nc))
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_tile_weights((const uint8_t *)codes, (const uint8_t *)bscale, (uint8_t *)codes_tiled,
+                                          (uint8_t *)bscale_tiled, E, N, K, mx, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -102,6 +102,9 @@ hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const
 
 hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s);
 
+hipError_t launch_tile_weights(const uint8_t *codes, const uint8_t *bscale, uint8_t *codes_tiled,
+                               uint8_t *bscale_tiled, int E, int N, int K, bool mx, hipStream_t s);
+
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
