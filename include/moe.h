@@ -198,7 +198,7 @@ int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, co
  * (for W4A8 the two GEMMs run between marks 4 and 5 and mark 6 follows at once;
  * where the gather is folded into GEMM1, mark 3 follows mark 2 at once; the tile
  * list is written by the tables' launches, so mark 4 follows mark 3 at once; for
- * at most 1024 slots and 32 tokens one launch routes and builds the tables and the
+ * at most 1024 slots and 256 tokens one launch routes and builds the tables and the
  * tile list, between marks 0 and 1).
  * For measurement; the marks add no work to the kernels. */
 #define MOE_N_STAGE_EVENTS 8

@@ -222,9 +222,12 @@ def test_forward_matches_oracle(name):
     MoeConfig("front_drop", T=30, H=256, I=256, E=16, k=4, glu_interleave=32, drop_p=0.1),
     MoeConfig("front_e256", T=32, H=128, I=128, E=256, k=32),             # exactly 1024 slots
     MoeConfig("front_one", T=1, H=256, I=384, E=4, k=4),
+    MoeConfig("front_t128", T=128, H=256, I=256, E=32, k=8, drop_p=0.05),   # 1024 slots, two routing passes
+    MoeConfig("front_t256", T=256, H=128, I=128, E=64, k=4),             # 256 tokens: four passes
+    MoeConfig("front_t100_odd", T=100, H=128, I=256, E=12, k=3),         # last pass partly empty
 ], ids=lambda c: c.name)
 def test_forward_small_front_end_matches_separate_steps(cfg):
-    """up to 1024 slots and 32 tokens the forward routes, builds the tables and the tile
+    """up to 1024 slots and 256 tokens the forward routes, builds the tables and the tile
     list in one launch; it must give exactly what the separate entry points give"""
     inp = generate(cfg, seed=2)
     d = DeviceProblem(inp)
