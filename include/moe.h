@@ -26,8 +26,11 @@
  *  - Argument checks run on the host before anything is enqueued and read no
  *    device memory; a failed check enqueues nothing.  T == 0 is valid and
  *    enqueues nothing.  Device-side preconditions (not checked): logits finite;
- *    tables consistent with one another.  Expert ids outside [0, E) are treated
- *    as -1 (dropped) by every kernel that reads them.
+ *    tables consistent with one another; every array holds at least the bytes its
+ *    description gives for the problem's precision and weight layout (the library
+ *    sees pointers only: a bf16 problem over fp8 / fp4 buffers reads past them).
+ *    Expert ids outside [0, E) are treated as -1 (dropped) by every kernel that
+ *    reads them.
  *  - Return value: a moe_status; MOE_ERR_HIP means a launch failed, and
  *    moe_last_hip_error() gives its hipError_t code.
  *  - The library is stateless; calls on different streams may run concurrently
