@@ -234,6 +234,81 @@ def test_permute_then_combine_with_identity_experts_returns_x(name, T):
     assert (out[~keep] == 0).all()
 
 
+def _fingerprint_combine_case(seed, T=48, k=4, E=8, H=24, p_drop=0.2):
+    """Routing with dropped slots, tables from Python's stable sort, distinct random integer rows
+    per slot (|y| < 128, exact in bf16), and weights (1 + m/8) 2^-12j per slot j (m < 8): term j of
+    a token's sum is an integer below 2^11 in magnitude times 2^(-3-12j), so the terms sit in
+    disjoint 12-bit bands, the fp64 sum is exact (47 bits for k = 4) and records which row was
+    paired with which slot's weight; any other pairing changes it."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < p_drop] = -1
+    idx[0] = -1                                              # a token with every slot dropped
+    _, _, row_src, slot_row = _tables_brute(idx, E)
+    R = int((idx >= 0).sum())
+    y = rng.integers(-127, 128, (max(R, 1), H)).astype(np.float32)
+    y_bits = bf16_bits_from_f32(y)
+    assert (bf16_bits_to_f32(y_bits) == y).all()
+    m = rng.integers(0, 8, (T, k))
+    w = (np.ldexp(1.0 + m / 8.0, -12 * np.arange(k)[None, :])).astype(np.float32)
+    return idx, row_src, slot_row, y_bits, y.astype(np.float64), w
+
+
+def _combine_by_definition(idx, row_src, y, w):
+    """out[t] = sum over the token's valid slots j of w[t, j] times the row that holds slot t*k+j,
+    in Python fractions (exact); the row of a slot is found by scanning row_src."""
+    from fractions import Fraction
+    T, k = idx.shape
+    where = {int(s): r for r, s in enumerate(row_src) if s >= 0}
+    out = np.zeros((T, y.shape[1]))
+    for t in range(T):
+        for c in range(y.shape[1]):
+            acc = Fraction(0)
+            for j in range(k):
+                if idx[t, j] >= 0:
+                    acc += Fraction(float(w[t, j])) * Fraction(float(y[where[t * k + j], c]))
+            out[t, c] = float(acc)                           # exact: the bands never overlap
+    return out
+
+
+def test_combine_pairs_each_weight_with_its_own_slot_row():
+    idx, row_src, slot_row, y_bits, y, w = _fingerprint_combine_case(seed=31)
+    T, k = idx.shape
+    want = _combine_by_definition(idx, row_src, y, w)
+    got = oracle.combine_bf16(y_bits, slot_row, w, T, k)
+    assert np.array_equal(got, want)
+    assert (got[0] == 0).all()                               # all slots dropped: 0
+    # the same pin rejects the outputs of a combine that mispairs: weights of slots 0 and 1 swapped
+    # within each token, or each slot read from its neighbour's row
+    w_swapped = w.copy()
+    w_swapped[:, [0, 1]] = w[:, [1, 0]]
+    assert not np.array_equal(oracle.combine_bf16(y_bits, slot_row, w_swapped, T, k), want)
+    sr = slot_row.reshape(T, k)
+    sr_rot = np.where((sr >= 0).all(axis=1, keepdims=True), np.roll(sr, 1, axis=1), sr).reshape(-1)
+    assert (sr_rot != slot_row).any()
+    assert not np.array_equal(oracle.combine_bf16(y_bits, sr_rot, w, T, k), want)
+
+
+def test_combine_equals_a_scatter_matrix_product():
+    """General values: out = C Y with C[t, r] = w[t, j] where row r holds slot (t, j) (numpy fp64
+    matmul on the brute-force tables)"""
+    rng = np.random.default_rng(32)
+    T, k, E, H = 64, 6, 16, 40
+    idx = rng.integers(0, E, (T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.15] = -1
+    _, _, row_src, slot_row = _tables_brute(idx, E)
+    R = int((idx >= 0).sum())
+    y_bits = bf16_bits_from_f32(rng.standard_normal((R, H)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    C = np.zeros((T, R))
+    for r in range(R):
+        s = int(row_src[r])
+        C[s // k, r] = w[s // k, s % k]
+    want = C @ bf16_bits_to_f32(y_bits).astype(np.float64)
+    got = oracle.combine_bf16(y_bits, slot_row, w, T, k)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
 # ----------------------------------------------------------------------------- expert FFN
 
 def _dense_mlp(x, w1_logical, w2, I, clamp=0.0):
@@ -457,6 +532,65 @@ def test_mxfp4_ffn_equals_dense_computation_on_exact_weights():
         s[s == 0] = 1
         hq = _torch_fp8_round((h / s[:, None]).astype(np.float32)) * s[:, None].astype(np.float64)
         np.testing.assert_allclose(y[i], hq.reshape(-1) @ w2.T, rtol=1e-9, atol=1e-12)
+
+
+def _w4_dense(packed, bscale, gscale, mx):
+    """one expert matrix, dequantised in numpy/torch: NVFP4 through torch's fp8 cast of the exact
+    e2m1 * e4m3 product, MXFP4 exactly (e2m1 * 2^(e8m0 - 127)); times the global scale"""
+    if not mx:
+        return _dequant_nvfp4(packed, bscale, gscale)
+    codes = np.stack([packed & 15, packed >> 4], axis=-1).reshape(packed.shape[0], -1)
+    mag = E2M1_VALUES[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    return mag * np.ldexp(1.0, np.repeat(bscale.astype(np.int64) - 127, 32, axis=1)) * np.float64(gscale)
+
+
+def _w4a8_forward_dense(inp, swap01=False):
+    """The W4A8 forward token by token: scipy softmax over the logits, the k largest (stable
+    argsort), renormalised over them, dropped slots skipped; each expert as dense numpy matrices
+    (W1 rows de-interleaved), h re-quantised per 128 with torch's fp8 cast.  swap01 pairs the
+    weights of slots 0 and 1 the wrong way round (to show the comparison would see it)."""
+    cfg = inp["cfg"]
+    mx = cfg.prec == "w4a8_mx"
+    xq = torch.from_numpy(inp["x"]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xd = xq * np.repeat(inp["x_scale"].astype(np.float64), 128, axis=1)
+    w1 = [deinterleave_rows(_w4_dense(inp["w1"][e], inp["w1_bscale"][e], inp["w1_gscale"][e], mx), cfg.I,
+                            cfg.glu_interleave) for e in range(cfg.E)]
+    w2 = [_w4_dense(inp["w2"][e], inp["w2_bscale"][e], inp["w2_gscale"][e], mx) for e in range(cfg.E)]
+    out = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        p = scipy.special.softmax(inp["logits"][t].astype(np.float64))
+        sel = np.argsort(-p, kind="stable")[: cfg.k]
+        w = p[sel] / p[sel].sum()
+        if swap01:
+            w[[0, 1]] = w[[1, 0]]
+        for j, e in enumerate(sel):
+            if inp["slot_drop"] is not None and inp["slot_drop"][t, j]:
+                continue
+            c = cfg.swiglu_clamp
+            g, u = xd[t] @ w1[e][: cfg.I].T, xd[t] @ w1[e][cfg.I:].T
+            if c:
+                g, u = np.clip(g, -c, c), np.clip(u, -c, c)
+            h = (g * scipy.special.expit(g) * u).astype(np.float32).reshape(-1, 128)
+            s = (np.abs(h).max(axis=1) / np.float32(448)).astype(np.float32)
+            s[s == 0] = 1
+            hq = _torch_fp8_round((h / s[:, None]).astype(np.float32)) * s[:, None].astype(np.float64)
+            out[t] += w[j] * (hq.reshape(-1) @ w2[e].T)
+    return out
+
+
+@pytest.mark.parametrize("prec", ["w4a8", "w4a8_mx"])
+def test_w4a8_forward_equals_routed_weighted_dense_computation(prec):
+    """the W4A8 / MXFP4 branch of the oracle's forward (routing, expert choice, weights, dropped
+    slots, interleaved W1, clamp, h re-quantisation, combine) against the dense numpy computation"""
+    cfg = MoeConfig("t", T=12, H=256, I=256, E=5, k=3, prec=prec, glu_interleave=32, swiglu_clamp=10.0,
+                    drop_p=0.25)
+    inp = generate(cfg, seed=41)
+    assert inp["slot_drop"].any() and not inp["slot_drop"].all()
+    got = oracle.moe_forward(inp)
+    want = _w4a8_forward_dense(inp)
+    np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12)
+    # a mispaired combine (weights of slots 0 and 1 exchanged) is far outside that tolerance
+    assert np.abs(_w4a8_forward_dense(inp, swap01=True) - got).max() > 1e-3 * np.abs(got).max()
 
 
 def test_mxfp4_generator_keeps_scales_in_the_required_range():
