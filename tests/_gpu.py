@@ -33,6 +33,32 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max() / (m if m > 0 else 1.0))
 
 
+def whole_tiles(offsets: np.ndarray, bm: int) -> np.ndarray:
+    """every row of two whole m-tiles of bm rows: an interior tile of the largest expert and the
+    first tile of the expert of median (non-zero) size"""
+    counts = np.diff(offsets)
+    big = int(np.argmax(counts))
+    m = (int(counts[big]) // bm) // 2                      # an interior full tile where there is one
+    a0 = int(offsets[big]) + m * bm
+    rows = [np.arange(a0, min(a0 + bm, int(offsets[big + 1])))]
+    live = np.nonzero(counts)[0]
+    med = int(live[np.argsort(counts[live], kind="stable")[live.size // 2]])
+    if med != big:
+        rows.append(np.arange(int(offsets[med]), min(int(offsets[med]) + bm, int(offsets[med + 1]))))
+    return np.concatenate(rows).astype(np.int64)
+
+
+def assert_all_rows_written(dev_bits, n_rows: int, ref_absmax: float, what: str):
+    """no element of the first n_rows rows still holds the 0xFFFF fill (a bf16 NaN), and the largest
+    magnitude stays within 4x of the sampled reference's (a skipped GEMM1 tile would leave the
+    workspace fill in h and blow the row up)"""
+    live = dev_bits[:n_rows]
+    n_canary = int((live == -1).sum())
+    assert n_canary == 0, f"{what}: {n_canary} elements never written"
+    amax = float((live.to(torch.int32) << 16).view(torch.float32).abs().max())
+    assert np.isfinite(amax) and amax <= 4.0 * ref_absmax, (what, amax, ref_absmax)
+
+
 class DeviceProblem:
     """One workload resident on the GPU, plus the output and workspace buffers of each call."""
 

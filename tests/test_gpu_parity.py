@@ -6,8 +6,11 @@ bit-exact copies; bf16 outputs max|err| / max|ref| <= 2e-2 against the fp64
 oracle; routing weights within 2e-6 of the fp64 values.  Full-size workloads are
 checked in full where the oracle is cheap (routing, tables, permutation) and on
 sampled rows / tokens where it is not (expert FFN, forward); the sample always
-holds the first and last row of every non-empty expert, so every ragged tile tail
-is covered.
+holds the first and last row of every non-empty expert (every ragged tile tail)
+and two whole 256-row m-tiles (an interior one of the largest expert, the first of
+the median expert).  Every output buffer starts filled with 0xFFFF: at every size
+each live row must have left that fill, with no magnitude far above the sampled
+reference's, and rows past the live count must still hold it.
 """
 from __future__ import annotations
 
@@ -20,7 +23,8 @@ import torch
 import oracle
 import token_permute_grouped_amd as tpg
 from moe_synth import CONFIGS, MoeConfig, bf16_bits_from_f32, deinterleave_rows, generate
-from tests._gpu import DEV, DeviceProblem, bf16_f64, bf16_host, rel_err, to_dev
+from tests._gpu import DEV, DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, \
+    whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -178,15 +182,15 @@ def test_grouped_ffn_rows(name):
     rs = row_src.cpu().numpy()
     R = int(off[-1])
     small = name in SMALL_CASES
-    rows = np.arange(R) if small else _sample_rows(off, extra=32, seed=1)
+    rows = np.arange(R) if small else np.union1d(_sample_rows(off, extra=32, seed=1), whole_tiles(off, 256))
     expert = np.searchsorted(off, rows, side="right") - 1
     ref = oracle.ffn_rows(inp, rs[rows] // cfg.k, expert)
     got = bf16_f64(bf16_host(y)[rows])
     err = rel_err(got, ref)
     print(f"[gpu parity] {name}: grouped FFN on {rows.size} rows, max|err|/max|ref| = {err:.3e}")
     assert err <= BF16_BAR
-    if small:
-        assert (bf16_host(y)[R:] == 0xFFFF).all()   # rows past R not written
+    assert_all_rows_written(y, R, float(np.abs(ref).max()), f"{name} y_perm")
+    assert (bf16_host(y)[R:] == 0xFFFF).all()   # rows past R not written
 
 
 def test_interleave_32_equals_plain_layout():
@@ -215,6 +219,7 @@ def test_forward_matches_oracle(name):
     err = rel_err(bf16_f64(out[tokens]), ref)
     print(f"[gpu parity] {name}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}")
     assert err <= BF16_BAR
+    assert_all_rows_written(to_dev(out), cfg.T, float(np.abs(ref).max()), f"{name} forward out")
 
 
 @pytest.mark.parametrize("cfg", [

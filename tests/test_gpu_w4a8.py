@@ -20,7 +20,8 @@ import oracle
 import token_permute_grouped_amd as tpg
 from moe_synth import CONFIGS, MoeConfig, generate
 from moe_synth.gen import w4a8_sweep_tokens
-from tests._gpu import DEV, DeviceProblem, bf16_f64, bf16_host, rel_err
+from tests._gpu import DEV, DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, \
+    whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +133,7 @@ def test_forward_token_sweep(T):
     err = rel_err(bf16_f64(out[tokens]), ref)
     print(f"[gpu w4a8] sweep T={T}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}")
     assert err <= W4A8_BAR
+    assert_all_rows_written(to_dev(out), T, float(np.abs(ref).max()), f"w4a8 T={T} forward out")
 
 
 @pytest.mark.parametrize("case", list(SMALL) + ["T1", "T16", "T256"])
@@ -161,12 +163,15 @@ def test_grouped_ffn_full_layer_sampled_rows():
     for e in range(cfg.E):
         if off[e + 1] > off[e]:
             rows += [off[e], off[e + 1] - 1]
-    rows = np.unique(np.array(rows, dtype=np.int64))
+    rows = np.union1d(np.array(rows, dtype=np.int64), whole_tiles(off, 64))  # + two whole 64-row m-tiles
     expert = np.searchsorted(off, rows, side="right") - 1
     ref = oracle.ffn_rows(inp, row_src.cpu().numpy()[rows] // cfg.k, expert)
     err = rel_err(bf16_f64(bf16_host(y)[rows]), ref)
     print(f"[gpu w4a8] full layer: grouped FFN on {rows.size} rows, max|err|/max|ref| = {err:.3e}")
     assert err <= W4A8_BAR
+    R = int(off[-1])
+    assert_all_rows_written(y, R, float(np.abs(ref).max()), "w4a8 T=256 y_perm")
+    assert (bf16_host(y)[R:] == 0xFFFF).all()
 
 
 def test_forward_deterministic_and_workspace_reuse():

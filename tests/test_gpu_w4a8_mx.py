@@ -16,7 +16,7 @@ import pytest
 import oracle
 from moe_synth import CONFIGS, MoeConfig, generate
 from moe_synth.gen import w4a8_sweep_tokens
-from tests._gpu import DeviceProblem, bf16_f64, bf16_host, rel_err
+from tests._gpu import DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -67,6 +67,7 @@ def _ffn_rows_err(inp, d, rows_of=None):
     expert = np.searchsorted(off, rows, side="right") - 1
     ref = oracle.ffn_rows(inp, row_src.cpu().numpy()[rows] // cfg.k, expert)
     got = bf16_host(y)
+    assert_all_rows_written(y, R, float(np.abs(ref).max()), f"{cfg.name} y_perm")
     return rel_err(bf16_f64(got[rows]), ref), got, R
 
 
@@ -93,9 +94,11 @@ def test_forward_token_sweep(T):
     out = bf16_host(d.forward())
     tokens = np.arange(T) if T <= 16 else np.unique(
         np.concatenate([np.random.default_rng(T).integers(0, T, 6), [0, T - 1]]))
-    err = rel_err(bf16_f64(out[tokens]), oracle.moe_forward(inp, tokens))
+    ref = oracle.moe_forward(inp, tokens)
+    err = rel_err(bf16_f64(out[tokens]), ref)
     print(f"[gpu w4a8_mx] sweep T={T}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}")
     assert err <= W4A8_BAR
+    assert_all_rows_written(to_dev(out), T, float(np.abs(ref).max()), f"w4a8_mx T={T} forward out")
 
 
 @pytest.mark.parametrize("case", list(SMALL) + ["T1", "T16", "T256"])
@@ -118,11 +121,12 @@ def test_grouped_ffn_full_layer_sampled_rows():
         for e in range(inp["cfg"].E):
             if off[e + 1] > off[e]:
                 rows += [off[e], off[e + 1] - 1]
-        return np.unique(np.array(rows, dtype=np.int64))
+        return np.union1d(np.array(rows, dtype=np.int64), whole_tiles(off, 64))  # + two whole 64-row m-tiles
 
-    err, _, _ = _ffn_rows_err(inp, d, first_last)
-    print(f"[gpu w4a8_mx] full layer: grouped FFN on the first and last row of every expert, "
-          f"max|err|/max|ref| = {err:.3e}")
+    err, got, R = _ffn_rows_err(inp, d, first_last)
+    print(f"[gpu w4a8_mx] full layer: grouped FFN on the first and last row of every expert and two whole "
+          f"m-tiles, max|err|/max|ref| = {err:.3e}")
+    assert (got[R:] == 0xFFFF).all()
     assert err <= W4A8_BAR
 
 
