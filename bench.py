@@ -216,7 +216,7 @@ def main():
             d[m], d[m + "_bscale"] = ct, st
         layout = tpg.MOE_W4_LAYOUT_TILED
     wts = tpg.make_weights(d["w1"], d["w2"], d["w1_bscale"], d["w1_gscale"], d["w2_bscale"], d["w2_gscale"], layout)
-    ws = torch.empty(tpg.moe_workspace_bytes(p, tpg.MOE_WS_FORWARD), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tpg.moe_workspace_bytes(p), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device=dev)
     torch.cuda.synchronize()
     log(f"inputs resident on {torch.cuda.get_device_name(0)}; workspace {ws.numel() / 2**30:.2f} GiB")
@@ -321,7 +321,7 @@ def main():
     srow = torch.empty(S, dtype=torch.int32, device=dev)
     x_perm = torch.empty((S, cfg.H), dtype=torch.uint8 if w4 else torch.int16, device=dev)
     x_perm_scale = torch.empty((S, cfg.H // 128), dtype=torch.float32, device=dev) if w4 else None
-    pws = torch.empty(max(1, tpg.moe_workspace_bytes(p, tpg.MOE_WS_PERMUTE)), dtype=torch.uint8, device=dev)
+    pws = torch.empty(max(1, tpg.moe_call_workspace_bytes(p, tpg.MOE_WS_PERMUTE)), dtype=torch.uint8, device=dev)
     def permute_run(after_forward):
         pev = [[hip.create() for _ in range(tpg.MOE_N_PERMUTE_EVENTS)] for _ in range(args.steps + 2)]
         for i in range(args.steps + 2):  # the first two are warm-up

@@ -17,10 +17,13 @@
  * Conventions shared by every entry point
  *  - Pointers are DEVICE pointers unless a parameter says otherwise; the problem
  *    and weight descriptors themselves are host structs.
- *  - `stream` is a hipStream_t (NULL = the null stream).  Every call enqueues its
- *    kernels on that stream and returns; none synchronises, allocates device
- *    memory, or keeps a pointer after it returns.  Buffers must stay alive until
- *    the stream has executed the work.  Weights are borrowed, never copied.
+ *  - `stream` is a hipStream_t (NULL = the null stream); the header declares the
+ *    handle type itself (an opaque pointer, the same typedef as HIP's), so a caller
+ *    needs no HIP header.  Every call enqueues its kernels on that stream and
+ *    returns; none synchronises, allocates device memory, or keeps a pointer after
+ *    it returns.  Buffers must stay alive until the stream has executed the work.
+ *    Weights are borrowed, never copied (the FlashInfer Usage section: buffers are
+ *    allocated by the caller before graph capture).
  *  - All arrays are row-major with the last index contiguous.  bf16 is passed as
  *    raw 16-bit patterns, fp8 as OCP E4M3FN bytes, fp4 as OCP E2M1 nibbles.
  *  - Argument checks run on the host before anything is enqueued and read no
@@ -45,6 +48,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* HIP's stream handle (hip_runtime_api.h declares the same typedef). */
+typedef struct ihipStream_t *hipStream_t;
 
 typedef enum moe_status {
     MOE_OK = 0,
@@ -77,7 +83,7 @@ enum {
     MOE_PREC_W4A8_MX = 2
 };
 
-/* Selects which call moe_workspace_bytes() sizes the workspace for. */
+/* Selects which call moe_call_workspace_bytes() sizes the workspace for. */
 enum { MOE_WS_PERMUTE = 0, MOE_WS_GROUPED_FFN = 1, MOE_WS_FORWARD = 2 };
 
 typedef struct moe_problem {
@@ -86,7 +92,7 @@ typedef struct moe_problem {
     int32_t I;              /* per-expert intermediate size, multiple of 128 (W4A8, W4A8_MX: of 256);
                                one expert matrix (2*I*H bf16) must be below 2 GB */
     int32_t E;              /* experts, 1..256 */
-    int32_t k;              /* experts per token, 1..min(E, 32); T*k < 2^31 */
+    int32_t k;              /* experts per token, 1..E; T*k < 2^31 */
     int32_t prec;           /* MOE_PREC_BF16, MOE_PREC_W4A8 or MOE_PREC_W4A8_MX */
     /* Megatron-LM "Support GEMM + Swiglu fused MLP", option
      * moe_mlp_glu_interleave_size: 0 = W1 rows are [gate (I rows) | up (I rows)]
@@ -120,12 +126,19 @@ typedef struct moe_weights {
     int32_t w4_layout;
 } moe_weights;
 
-/* Host only.  Bytes of device workspace the given call needs for this problem
- * (MOE_WS_*); 0 if the problem is invalid.  The size depends only on the problem,
- * never on the routing, so one allocation made before graph capture serves every
- * call of that shape.  Workspace contents need not be initialised and are not
- * preserved between calls. */
-size_t moe_workspace_bytes(const moe_problem *p, int which);
+/* Host only.  Bytes of device workspace that serve every entry point for this
+ * problem (the largest plan: moe_forward's); 0 if the problem is invalid.  The
+ * size depends only on the problem, never on the routing, so one allocation made
+ * before graph capture serves every call of that shape (the FlashInfer pull request
+ * "[SM90] Add W4A8 MegaMoE support" sizes its workspace for the largest plan, and
+ * its Usage section has the caller allocate it before capture).  Workspace
+ * contents need not be initialised and are not preserved between calls. */
+size_t moe_workspace_bytes(const moe_problem *p);
+
+/* Host only.  The smaller workspace one step entry point needs (MOE_WS_PERMUTE for
+ * moe_permute, MOE_WS_GROUPED_FFN for moe_grouped_ffn, MOE_WS_FORWARD as
+ * moe_workspace_bytes); 0 if the problem or `which` is invalid. */
+size_t moe_call_workspace_bytes(const moe_problem *p, int which);
 
 /* Host only.  Static English text for a moe_status value. */
 const char *moe_status_str(int status);
@@ -141,7 +154,7 @@ int moe_last_hip_error(void);
  * restricted to the k chosen and renormalised to sum to 1; a dropped slot keeps
  * its weight and is skipped by the combine). */
 int moe_route_topk(const float *logits, const uint8_t *slot_drop, const moe_problem *p, int32_t *topk_idx,
-                   float *topk_w, void *stream);
+                   float *topk_w, hipStream_t stream);
 
 /* Permute.  From topk_idx int32 [T][k] builds the tables
  *   offsets int32 [E+1]  exclusive prefix of the expert counts (offsets[E] = R,
@@ -155,7 +168,7 @@ int moe_route_topk(const float *logits, const uint8_t *slot_drop, const moe_prob
  * function of topk_idx (bit-exact, deterministic). */
 int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
                 int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, void *ws,
-                size_t ws_bytes, void *stream);
+                size_t ws_bytes, hipStream_t stream);
 
 /* moe_permute with timing marks: identical work, plus hipEventRecord of
  * stage_events[i] (MOE_N_PERMUTE_EVENTS hipEvent_t handles, created by the
@@ -165,24 +178,31 @@ int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, co
 #define MOE_N_PERMUTE_EVENTS 3
 int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
                       int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale,
-                      void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
+                      void *ws, size_t ws_bytes, hipStream_t stream, void *const *stage_events);
 
-/* Grouped expert FFN.  For every expert e and row r in [offsets[e], offsets[e+1]):
+/* Grouped expert FFN: the two expert GEMMs with the SwiGLU between them (the
+ * FlashInfer fused kernel's two FFN GEMMs and clamped SwiGLU; the GEMM + SwiGLU
+ * fused MLP of Megatron-LM "Support GEMM + Swiglu fused MLP", whose
+ * moe_mlp_glu_interleave_size option glu_interleave follows).
+ * For every expert e and row r in [offsets[e], offsets[e+1]):
  * y_perm[r] = (silu(g) * u) W2_e^T with [g | u] = x_perm[r] W1_e^T (clamped if
  * swiglu_clamp > 0).  x_perm as produced by moe_permute; y_perm bf16 [T*k][H];
  * rows >= offsets[E] are not written.  Needs ws of at least
- * moe_workspace_bytes(p, MOE_WS_GROUPED_FFN) bytes (holds h and the tile list). */
+ * moe_call_workspace_bytes(p, MOE_WS_GROUPED_FFN) bytes (holds h and the tile list). */
 int moe_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t *offsets, const moe_weights *w,
-                    const moe_problem *p, void *y_perm, void *ws, size_t ws_bytes, void *stream);
+                    const moe_problem *p, void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Unpermute and combine: out[t] = bf16( sum_{j=0..k-1, slot_row[t*k+j] >= 0}
+/* Unpermute and combine: the top-k reduction that ends the FlashInfer fused MoE
+ * (-1 routes skipped), with the unpermute folded in as Megatron-LM "add permute
+ * fusion into hybrid ep" folds it into the combine:
+ * out[t] = bf16( sum_{j=0..k-1, slot_row[t*k+j] >= 0}
  * topk_w[t][j] * y_perm[slot_row[t*k+j]] ), accumulated in fp32 in ascending j
  * with no atomics (deterministic).  A token whose slots are all dropped gets 0. */
 int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const float *topk_w, const moe_problem *p,
-                          void *out, void *stream);
+                          void *out, hipStream_t stream);
 
 /* The whole forward: route, permute, grouped FFN, combine, on one stream, with
- * every intermediate in ws (at least moe_workspace_bytes(p, MOE_WS_FORWARD)).
+ * every intermediate in ws (at least moe_workspace_bytes(p)).
  * Whenever the byte offsets into x fit 31 bits (T*H*2 < 2^31 for bf16, T*H < 2^31
  * for W4A8) the row gather is folded into GEMM1, which reads row r of the
  * expert-major order (and, for W4A8, its activation scales) straight from
@@ -191,7 +211,7 @@ int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const flo
  * the workspace holds none.  The result is bitwise the same as moe_permute +
  * moe_grouped_ffn + moe_unpermute_combine. */
 int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
-                const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream);
+                const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* moe_forward with timing marks: identical work, plus hipEventRecord of
  * stage_events[i] (MOE_N_STAGE_EVENTS hipEvent_t handles, created by the caller)
@@ -206,7 +226,7 @@ int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, co
  * For measurement; the marks add no work to the kernels. */
 #define MOE_N_STAGE_EVENTS 8
 int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
-                      const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
+                      const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream,
                       void *const *stage_events);
 
 /* Diagnostic: the W4A8 dequant of every (e2m1 code, e4m3 block scale s) pair at
@@ -218,7 +238,7 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
  * so out8[p][c][s] is the e4m3 code of code (c + p) mod 16 times scale s.  A NaN
  * block scale, outside the defined domain, gives the NaN code with the product's
  * sign. */
-int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
+int moe_w4a8_dequant_table(uint8_t *out8, hipStream_t stream);
 
 /* W4A8 weight preparation: one matrix stack of E experts with N rows and K columns
  * (N a multiple of 32, K of 256), row-major codes uint8 [E][N][K/2] and block scales
@@ -231,7 +251,7 @@ int moe_w4a8_dequant_table(uint8_t *out8, void *stream);
  * enqueued on `stream`.  Call it once per matrix (W1: N = 2I, K = H; W2: N = H, K =
  * I) when the weights are loaded. */
 int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled,
-                          int32_t E, int32_t N, int32_t K, int32_t prec, void *stream);
+                          int32_t E, int32_t N, int32_t K, int32_t prec, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -78,7 +78,7 @@ class DeviceProblem:
         self.S = cfg.T * cfg.k
 
     def workspace(self, which, fill=None):
-        n = tpg.moe_workspace_bytes(self.p, which)
+        n = tpg.moe_call_workspace_bytes(self.p, which)
         ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
         if fill is not None:
             ws.fill_(fill)

@@ -44,7 +44,8 @@ def _p(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-1), tpg.MOE_ERR_SHAPE), (dict(H=100), tpg.MOE_ERR_SHAPE), (dict(H=0), tpg.MOE_ERR_SHAPE),
     (dict(I=64), tpg.MOE_ERR_SHAPE), (dict(E=0), tpg.MOE_ERR_SHAPE), (dict(E=257, k=2), tpg.MOE_ERR_SHAPE),
-    (dict(k=0), tpg.MOE_ERR_SHAPE), (dict(k=9, E=8), tpg.MOE_ERR_SHAPE), (dict(k=33, E=64), tpg.MOE_ERR_SHAPE),
+    (dict(k=0), tpg.MOE_ERR_SHAPE), (dict(k=9, E=8), tpg.MOE_ERR_SHAPE), (dict(k=65, E=64), tpg.MOE_ERR_SHAPE),
+    (dict(k=257, E=256), tpg.MOE_ERR_SHAPE),
     (dict(T=2 ** 28, k=8), tpg.MOE_ERR_SHAPE), (dict(prec=7), tpg.MOE_ERR_UNSUPPORTED),
     (dict(glu_interleave=16), tpg.MOE_ERR_UNSUPPORTED), (dict(swiglu_clamp=-1.0), tpg.MOE_ERR_UNSUPPORTED),
     (dict(swiglu_clamp=float("nan")), tpg.MOE_ERR_UNSUPPORTED),
@@ -64,7 +65,8 @@ def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     assert lib.moe_grouped_ffn(FAKE, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
     assert lib.moe_unpermute_combine(FAKE, FAKE, FAKE, p, FAKE, None) == status
     assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
-    assert lib.moe_workspace_bytes(p, tpg.MOE_WS_FORWARD) == 0
+    assert lib.moe_workspace_bytes(p) == 0
+    assert lib.moe_call_workspace_bytes(p, tpg.MOE_WS_PERMUTE) == 0
 
 
 def test_null_pointers_are_rejected():
@@ -107,7 +109,7 @@ def test_small_workspace_is_rejected():
         (tpg.MOE_WS_GROUPED_FFN, lambda n: lib.moe_grouped_ffn(FAKE, None, FAKE, w, p, FAKE, FAKE, n, None)),
         (tpg.MOE_WS_FORWARD, lambda n: lib.moe_forward(FAKE, None, FAKE, None, w, p, FAKE, FAKE, n, None)),
     ]:
-        need = tpg.moe_workspace_bytes(pr, which)
+        need = tpg.moe_call_workspace_bytes(pr, which)
         assert need > 0
         assert call(need - 1) == tpg.MOE_ERR_WORKSPACE
 
@@ -148,27 +150,39 @@ def test_unknown_weight_layout_is_rejected():
                                    None) == tpg.MOE_ERR_UNSUPPORTED
 
 
+def test_k_up_to_e_is_accepted():
+    """1 <= k <= E <= 256: a problem with k above 32 passes the host checks (here it stops at the
+    first NULL pointer) and gets a workspace"""
+    lib = tpg.load()
+    for E, k in ((64, 64), (256, 33), (256, 256)):
+        pr = _p(E=E, k=k)
+        assert tpg.moe_workspace_bytes(pr) > 0
+        assert lib.moe_route_topk(None, None, ctypes.byref(pr), FAKE, FAKE, None) == tpg.MOE_ERR_NULL
+
+
 def test_workspace_sizes():
     big = _p(T=32768, H=7168, I=2048, E=32, k=8, glu_interleave=32)
-    n = tpg.moe_workspace_bytes(big, tpg.MOE_WS_FORWARD)
+    n = tpg.moe_workspace_bytes(big)
+    assert n == tpg.moe_call_workspace_bytes(big, tpg.MOE_WS_FORWARD)
     S = 32768 * 8
     # the bf16 forward gathers inside GEMM1 (T*H*2 < 2^31): it holds y_perm (bf16 [S][H]) and
     # h (bf16 [S][I]) but no x_perm; sized by shape only
     assert S * (7168 * 2 + 2048 * 2) <= n < S * (7168 * 2 * 2 + 2048 * 2)
     # too many token rows for 31-bit offsets into x: the forward runs the separate gather
     unfused = _p(T=131072, H=8192, I=1024, E=8, k=2)
-    assert tpg.moe_workspace_bytes(unfused, tpg.MOE_WS_FORWARD) >= 131072 * 2 * (8192 * 2 * 2 + 1024 * 2)
+    assert tpg.moe_workspace_bytes(unfused) >= 131072 * 2 * (8192 * 2 * 2 + 1024 * 2)
     # W4A8 gathers inside GEMM1 too: y_perm (bf16) and h (fp32, fp8 and scales) but no fp8 x_perm
     w4 = _p(T=256, H=7168, I=2048, E=32, k=8, prec=tpg.MOE_PREC_W4A8, swiglu_clamp=10.0)
     S4 = 256 * 8
-    n4 = tpg.moe_workspace_bytes(w4, tpg.MOE_WS_FORWARD)
+    n4 = tpg.moe_workspace_bytes(w4)
     assert S4 * (7168 * 2 + 2048 * 5) <= n4 < S4 * (7168 * 2 + 2048 * 5 + 7168)
     # MXFP4 weights change only the weight scales: the same workspace for every call
     mx = _p(T=256, H=7168, I=2048, E=32, k=8, prec=tpg.MOE_PREC_W4A8_MX, swiglu_clamp=10.0)
     for which in (tpg.MOE_WS_PERMUTE, tpg.MOE_WS_GROUPED_FFN, tpg.MOE_WS_FORWARD):
-        assert tpg.moe_workspace_bytes(mx, which) == tpg.moe_workspace_bytes(w4, which) > 0
-    assert tpg.moe_workspace_bytes(big, tpg.MOE_WS_PERMUTE) < tpg.moe_workspace_bytes(big, tpg.MOE_WS_GROUPED_FFN) < n
-    assert tpg.moe_workspace_bytes(big, 99) == 0
+        assert tpg.moe_call_workspace_bytes(mx, which) == tpg.moe_call_workspace_bytes(w4, which) > 0
+    assert (tpg.moe_call_workspace_bytes(big, tpg.MOE_WS_PERMUTE)
+            < tpg.moe_call_workspace_bytes(big, tpg.MOE_WS_GROUPED_FFN) < n)
+    assert tpg.moe_call_workspace_bytes(big, 99) == 0
 
 
 def test_status_strings():

@@ -38,6 +38,7 @@ SMALL_CASES = {
                                   drop_p=0.1),
     "clamped": MoeConfig("clamped", T=150, H=384, I=256, E=8, k=3, swiglu_clamp=1.0),
     "ragged_tiles": MoeConfig("ragged_tiles", T=700, H=256, I=640, E=5, k=2),
+    "wide_k": MoeConfig("wide_k", T=40, H=128, I=128, E=128, k=64),          # k above 32: 16 slots per lane
 }
 FULL = ["mid", "skewed", "ep_share"]
 
@@ -93,7 +94,7 @@ def test_route_ties_and_equal_logits():
     assert (w.cpu().numpy()[:8] == np.float32(1 / 8)).all()
 
 
-@pytest.mark.parametrize("E,k", [(200, 8), (256, 32), (3, 3), (130, 5), (64, 1)])
+@pytest.mark.parametrize("E,k", [(200, 8), (256, 32), (3, 3), (130, 5), (64, 1), (256, 200), (48, 48)])
 def test_route_exact_order_on_ties_signed_zeros_and_denormals(E, k):
     """selection is an exact comparison of the fp32 logits: ties (within and across lanes of a
     wave) go to the lower id, -0 equals +0, subnormals keep their order"""
@@ -230,6 +231,7 @@ def test_forward_matches_oracle(name):
     MoeConfig("front_t128", T=128, H=256, I=256, E=32, k=8, drop_p=0.05),   # 1024 slots, two routing passes
     MoeConfig("front_t256", T=256, H=128, I=128, E=64, k=4),             # 256 tokens: four passes
     MoeConfig("front_t100_odd", T=100, H=128, I=256, E=12, k=3),         # last pass partly empty
+    MoeConfig("front_wide_k", T=8, H=128, I=128, E=256, k=100, drop_p=0.1),  # k above 32 in the front end
 ], ids=lambda c: c.name)
 def test_forward_small_front_end_matches_separate_steps(cfg):
     """up to 1024 slots and 256 tokens the forward routes, builds the tables and the tile

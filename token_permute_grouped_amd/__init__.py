@@ -23,7 +23,7 @@ MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = (
-    "moe_workspace_bytes", "moe_status_str", "moe_last_hip_error", "moe_route_topk", "moe_permute",
+    "moe_workspace_bytes", "moe_call_workspace_bytes", "moe_status_str", "moe_last_hip_error", "moe_route_topk", "moe_permute",
     "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_w4a8_dequant_table",
     "moe_w4a8_tile_weights",
 )
@@ -69,8 +69,10 @@ def load() -> ctypes.CDLL:
     P, I32, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     PP = ctypes.POINTER(Problem)
     PW = ctypes.POINTER(Weights)
-    lib.moe_workspace_bytes.argtypes = [PP, I32]
+    lib.moe_workspace_bytes.argtypes = [PP]
     lib.moe_workspace_bytes.restype = SZ
+    lib.moe_call_workspace_bytes.argtypes = [PP, I32]
+    lib.moe_call_workspace_bytes.restype = SZ
     lib.moe_status_str.argtypes = [I32]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_last_hip_error.restype = I32
@@ -130,8 +132,14 @@ def make_weights(w1, w2, w1_bscale=None, w1_gscale=None, w2_bscale=None, w2_gsca
                    w4_layout)
 
 
-def moe_workspace_bytes(problem: Problem, which: int = MOE_WS_FORWARD) -> int:
-    return int(load().moe_workspace_bytes(ctypes.byref(problem), which))
+def moe_workspace_bytes(problem: Problem) -> int:
+    """bytes of workspace that serve every entry point (moe_forward's plan)"""
+    return int(load().moe_workspace_bytes(ctypes.byref(problem)))
+
+
+def moe_call_workspace_bytes(problem: Problem, which: int) -> int:
+    """the smaller workspace of one step entry point (MOE_WS_PERMUTE / MOE_WS_GROUPED_FFN)"""
+    return int(load().moe_call_workspace_bytes(ctypes.byref(problem), which))
 
 
 def moe_route_topk(logits, slot_drop, problem: Problem, topk_idx, topk_w, stream=None):

@@ -15,7 +15,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int check_problem(const moe_problem *p) {
     if (!p) return MOE_ERR_NULL;
-    if (p->T < 0 || p->E < 1 || p->E > 256 || p->k < 1 || p->k > 32 || p->k > p->E) return MOE_ERR_SHAPE;
+    if (p->T < 0 || p->E < 1 || p->E > 256 || p->k < 1 || p->k > p->E) return MOE_ERR_SHAPE;
     if (p->H < 128 || p->H > 65536 || p->H % 128 != 0) return MOE_ERR_SHAPE;
     if (p->I < 128 || p->I > 65536 || p->I % 128 != 0) return MOE_ERR_SHAPE;
     if ((int64_t)p->T * p->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
@@ -130,7 +130,7 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
 }
 
 int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
-                 const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
+                 const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream,
                  void *const *ev) {
     int st = check_problem(p);
     if (st) return st;
@@ -138,10 +138,10 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
     if (!logits || !x || !out || !ws) return MOE_ERR_NULL;
     if ((st = check_weights(w, p))) return st;
     if (is_w4a8(p) && !x_scale) return MOE_ERR_NULL;
-    if (ws_bytes < moe_workspace_bytes(p, MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < moe_workspace_bytes(p)) return MOE_ERR_WORKSPACE;
     const WsLayout L = ws_layout(*p);
     char *b = (char *)ws;
-    hipStream_t s = (hipStream_t)stream;
+    hipStream_t s = stream;
     int32_t *topk_idx = (int32_t *)(b + L.topk_idx);
     float *topk_w = (float *)(b + L.topk_w);
     int32_t *offsets = (int32_t *)(b + L.offsets);
@@ -223,7 +223,12 @@ using namespace tpg;
 
 extern "C" {
 
-size_t moe_workspace_bytes(const moe_problem *p, int which) {
+size_t moe_workspace_bytes(const moe_problem *p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return ws_layout(*p).forward_end;
+}
+
+size_t moe_call_workspace_bytes(const moe_problem *p, int which) {
     if (check_problem(p) != MOE_OK) return 0;
     const WsLayout L = ws_layout(*p);
     switch (which) {
@@ -249,30 +254,30 @@ const char *moe_status_str(int status) {
 int moe_last_hip_error(void) { return g_last_hip_error; }
 
 int moe_route_topk(const float *logits, const uint8_t *slot_drop, const moe_problem *p, int32_t *topk_idx,
-                   float *topk_w, void *stream) {
+                   float *topk_w, hipStream_t stream) {
     int st = check_problem(p);
     if (st) return st;
     if (p->T == 0) return MOE_OK;
     if (!logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
-    return hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, (hipStream_t)stream));
+    return hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, stream));
 }
 
 int moe_permute(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p, int32_t *offsets,
                 int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale, void *ws, size_t ws_bytes,
-                void *stream) {
+                hipStream_t stream) {
     int st = check_problem(p);
     if (st) return st;
     if (p->T == 0) return MOE_OK;
     if (!x || !topk_idx || !offsets || !row_src || !slot_row || !x_perm || !ws) return MOE_ERR_NULL;
     if (is_w4a8(p) && (!x_scale || !x_perm_scale)) return MOE_ERR_NULL;
-    if (ws_bytes < moe_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < moe_call_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
     return run_permute(x, x_scale, topk_idx, *p, offsets, row_src, slot_row, x_perm, x_perm_scale, (char *)ws,
-                       (hipStream_t)stream);
+                       stream);
 }
 
 int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_idx, const moe_problem *p,
                       int32_t *offsets, int32_t *row_src, int32_t *slot_row, void *x_perm, float *x_perm_scale,
-                      void *ws, size_t ws_bytes, void *stream, void *const *stage_events) {
+                      void *ws, size_t ws_bytes, hipStream_t stream, void *const *stage_events) {
     if (!stage_events) return MOE_ERR_NULL;
     for (int i = 0; i < MOE_N_PERMUTE_EVENTS; ++i)
         if (!stage_events[i]) return MOE_ERR_NULL;
@@ -281,40 +286,40 @@ int moe_permute_timed(const void *x, const float *x_scale, const int32_t *topk_i
     if (p->T == 0) return MOE_OK;
     if (!x || !topk_idx || !offsets || !row_src || !slot_row || !x_perm || !ws) return MOE_ERR_NULL;
     if (is_w4a8(p) && (!x_scale || !x_perm_scale)) return MOE_ERR_NULL;
-    if (ws_bytes < moe_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < moe_call_workspace_bytes(p, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
     return run_permute(x, x_scale, topk_idx, *p, offsets, row_src, slot_row, x_perm, x_perm_scale, (char *)ws,
-                       (hipStream_t)stream, stage_events);
+                       stream, stage_events);
 }
 
 int moe_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t *offsets, const moe_weights *w,
-                    const moe_problem *p, void *y_perm, void *ws, size_t ws_bytes, void *stream) {
+                    const moe_problem *p, void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream) {
     int st = check_problem(p);
     if (st) return st;
     if (p->T == 0) return MOE_OK;
     if (!x_perm || !offsets || !y_perm || !ws) return MOE_ERR_NULL;
     if ((st = check_weights(w, p))) return st;
     if (is_w4a8(p) && !x_perm_scale) return MOE_ERR_NULL;
-    if (ws_bytes < moe_workspace_bytes(p, MOE_WS_GROUPED_FFN)) return MOE_ERR_WORKSPACE;
-    return run_grouped_ffn(x_perm, x_perm_scale, offsets, *w, *p, y_perm, (char *)ws, (hipStream_t)stream);
+    if (ws_bytes < moe_call_workspace_bytes(p, MOE_WS_GROUPED_FFN)) return MOE_ERR_WORKSPACE;
+    return run_grouped_ffn(x_perm, x_perm_scale, offsets, *w, *p, y_perm, (char *)ws, stream);
 }
 
 int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const float *topk_w, const moe_problem *p,
-                          void *out, void *stream) {
+                          void *out, hipStream_t stream) {
     int st = check_problem(p);
     if (st) return st;
     if (p->T == 0) return MOE_OK;
     if (!y_perm || !slot_row || !topk_w || !out) return MOE_ERR_NULL;
     return hip_status(launch_combine((const uint16_t *)y_perm, slot_row, topk_w, p->T, p->k, p->H, (uint16_t *)out,
-                                     (hipStream_t)stream));
+                                     stream));
 }
 
 int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
-                const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream) {
+                const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
     return forward_impl(logits, slot_drop, x, x_scale, w, p, out, ws, ws_bytes, stream, nullptr);
 }
 
 int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
-                      const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, void *stream,
+                      const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream,
                       void *const *stage_events) {
     if (!stage_events) return MOE_ERR_NULL;
     for (int i = 0; i < MOE_N_STAGE_EVENTS; ++i)
@@ -322,13 +327,13 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
     return forward_impl(logits, slot_drop, x, x_scale, w, p, out, ws, ws_bytes, stream, stage_events);
 }
 
-int moe_w4a8_dequant_table(uint8_t *out8, void *stream) {
+int moe_w4a8_dequant_table(uint8_t *out8, hipStream_t stream) {
     if (!out8) return MOE_ERR_NULL;
-    return hip_status(launch_w4a8_dequant_table(out8, (hipStream_t)stream));
+    return hip_status(launch_w4a8_dequant_table(out8, stream));
 }
 
 int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled, int32_t E,
-                          int32_t N, int32_t K, int32_t prec, void *stream) {
+                          int32_t N, int32_t K, int32_t prec, hipStream_t stream) {
     if (!codes || !bscale || !codes_tiled || !bscale_tiled) return MOE_ERR_NULL;
     if (prec != MOE_PREC_W4A8 && prec != MOE_PREC_W4A8_MX) return MOE_ERR_UNSUPPORTED;
     if (E < 1 || N < 32 || N % 32 != 0 || K < 256 || K % 256 != 0) return MOE_ERR_SHAPE;
@@ -342,7 +347,7 @@ int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_til
         overlap(codes, nc, bscale_tiled, ns) || overlap(bscale, ns, codes_tiled, nc))
         return MOE_ERR_UNSUPPORTED;
     return hip_status(launch_tile_weights((const uint8_t *)codes, (const uint8_t *)bscale, (uint8_t *)codes_tiled,
-                                          (uint8_t *)bscale_tiled, E, N, K, mx, (hipStream_t)stream));
+                                          (uint8_t *)bscale_tiled, E, N, K, mx, stream));
 }
 
 }  // extern "C"

@@ -14,8 +14,9 @@
 // row-wide minimum of the ids holding it (equal logits -> lower id), four DPP steps each
 // (quad_perm, row_half_mirror, row_mirror), so the rows never exchange data.  Every lane of the
 // row learns each round's winner, so the normaliser is summed in slot order identically in
-// every lane; lane i keeps slots i and i + 16 (k <= 32).  If `ids` is not null, the slots'
-// expert ids (or -1) are also stored at ids[j] (e.g. in LDS).
+// every lane; lane i keeps slots i, i + 16, ... (two of them for k <= 32, sixteen for k up to
+// 256).  If `ids` is not null, the slots' expert ids (or -1) are also stored at ids[j] (e.g. in
+// LDS).
 #pragma once
 #include "wave_ops.h"
 
@@ -49,9 +50,9 @@ __device__ __forceinline__ uint32_t row_min(uint32_t x) {
     return min(x, dpp<kRowMirror, 0xf>(x, ~0u));
 }
 
-// V: experts per lane (16 V >= E).  t is a valid token for every row; only rows with `valid`
-// store.
-template <int V>
+// V: experts per lane (16 V >= E); J: slots per lane (16 J >= k).  t is a valid token for every
+// row; only rows with `valid` store.
+template <int V, int J>
 __device__ __forceinline__ void route_row(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
                                           int64_t t, bool valid, int E, int k, int i,
                                           int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *ids) {
@@ -62,8 +63,14 @@ __device__ __forceinline__ void route_row(const float *__restrict__ logits, cons
         const int e = i + 16 * q;
         key[q] = e < E ? logit_key(l[e]) : 0u;  // 0: no expert (or already taken)
     }
-    int id0 = -1, id1 = -1;
-    float ex0 = 0.0f, ex1 = 0.0f, lmax = 0.0f, z = 0.0f;
+    int id[J];
+    float exs[J];
+#pragma unroll
+    for (int h = 0; h < J; ++h) {
+        id[h] = -1;
+        exs[h] = 0.0f;
+    }
+    float lmax = 0.0f, z = 0.0f;
     for (int j = 0; j < k; ++j) {
         // this lane's best remaining expert: ids grow with q, so strict '>' keeps the lower id
         uint32_t bk = 0u;
@@ -86,26 +93,24 @@ __device__ __forceinline__ void route_row(const float *__restrict__ logits, cons
         // renormalised softmax weights: exp(l_j - l_max) summed over the chosen slots in order
         const float ex = expf(lj - lmax);
         z += ex;
-        if (j == i) {
-            id0 = win;
-            ex0 = ex;
-        }
-        if (j == i + 16) {
-            id1 = win;
-            ex1 = ex;
-        }
+#pragma unroll
+        for (int h = 0; h < J; ++h)
+            if (j == i + 16 * h) {
+                id[h] = win;
+                exs[h] = ex;
+            }
     }
     if (!valid) return;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < J; ++h) {
         const int j = i + 16 * h;
         if (j < k) {
             const int64_t s = t * k + j;
             const bool dropped = slot_drop != nullptr && slot_drop[s] != 0;
-            const int id = dropped ? -1 : (h ? id1 : id0);
-            topk_idx[s] = id;
-            topk_w[s] = (h ? ex1 : ex0) / z;
-            if (ids) ids[j] = id;
+            const int sid = dropped ? -1 : id[h];
+            topk_idx[s] = sid;
+            topk_w[s] = exs[h] / z;
+            if (ids) ids[j] = sid;
         }
     }
 }
@@ -119,16 +124,24 @@ __device__ __forceinline__ void route_token16(const float *__restrict__ logits, 
                                               int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                               int32_t *ids) {
     using namespace route_detail;
-    if (E <= 16)
-        route_row<1>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
-    else if (E <= 32)
-        route_row<2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
-    else if (E <= 64)
-        route_row<4>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
-    else if (E <= 128)
-        route_row<8>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
-    else
-        route_row<16>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    if (k > 32) {  // k <= E, so E > 32
+        if (E <= 64)
+            route_row<4, 16>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+        else if (E <= 128)
+            route_row<8, 16>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+        else
+            route_row<16, 16>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    } else if (E <= 16) {
+        route_row<1, 2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    } else if (E <= 32) {
+        route_row<2, 2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    } else if (E <= 64) {
+        route_row<4, 2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    } else if (E <= 128) {
+        route_row<8, 2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    } else {
+        route_row<16, 2>(logits, slot_drop, t, valid, E, k, i, topk_idx, topk_w, ids);
+    }
 }
 
 }  // namespace tpg
