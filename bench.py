@@ -19,7 +19,13 @@ On bf16 data the forward folds the row gather into GEMM1; the permute kernel's o
 HBM rate comes from K calls of moe_permute_timed on the same routing.
 
 Prints one JSON line.  The CPU baseline is the fp64 oracle (test infrastructure)
-timed on a bounded sample of the same workload on the host cores.
+timed on a bounded, stratified sample of the same workload on the host cores (one
+token routed to every non-empty expert plus evenly spaced tokens, at least 2048),
+with the full layer's time extrapolated from that rate and labelled so.  With the
+default workload the line also carries `per_config`: the same measurements (fewer
+steps, no standalone permute) for the tiny and mid layers, the W4A8 decode layer at
+1, 16 and 256 tokens with NVFP4 and MXFP4 weights (HBM roofline of the expert FFN),
+and the ep_share layer.
 """
 from __future__ import annotations
 
@@ -94,23 +100,47 @@ def measured_traffic(kernel_file, kernel, workload, seed, launches_bytes_key="by
     return rec.get(launches_bytes_key)
 
 
-def cpu_baseline(inp, budget_s):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, budget_s, min_tokens=2048):
+    """The fp64 oracle on the host cores: a stratified sample of at least min_tokens tokens (all of
+    them if T is smaller) that holds one token routed to every non-empty expert, the rest evenly
+    spaced; the rate is extrapolated to the whole layer and labelled so."""
     import oracle
     cfg = inp["cfg"]
     cores = oracle.max_threads()
+    idx, _ = oracle.route(inp["logits"], cfg.k, inp.get("slot_drop"))   # cheap: T x E
+    live = np.unique(idx[idx >= 0])
+    strata = np.unique([int(np.argmax((idx == e).any(axis=1))) for e in live]).astype(np.int32)
     probe = np.linspace(0, cfg.T - 1, 2 * cores).astype(np.int32)  # two tokens per thread
     t0 = time.perf_counter()
     oracle.moe_forward(inp, probe)
     per_tok = (time.perf_counter() - t0) / probe.size
-    n = int(max(4, min(cfg.T, budget_s / max(per_tok, 1e-9))))
-    tokens = np.linspace(0, cfg.T - 1, n).astype(np.int32)
-    log(f"cpu baseline: oracle on {n} tokens with {cores} threads (~{n * per_tok:.0f} s)")
+    n = int(min(cfg.T, max(min_tokens, budget_s / max(per_tok, 1e-9))))
+    spread = np.linspace(0, cfg.T - 1, max(n - strata.size, 1)).astype(np.int32)
+    tokens = np.union1d(strata, spread).astype(np.int32)
+    hit = np.unique(idx[tokens][idx[tokens] >= 0]).size
+    log(f"cpu baseline: oracle on {tokens.size} tokens ({hit} of {live.size} non-empty experts) with {cores} "
+        f"threads (~{tokens.size * per_tok:.0f} s)")
     t0 = time.perf_counter()
     oracle.moe_forward(inp, tokens)
     dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} evenly spaced tokens of the {cfg.name} workload (all k slots each), fp64, "
-                      f"{dt:.1f} s"}
+    rate = tokens.size / dt
+    return {"value": round(rate, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{tokens.size} tokens of the {cfg.name} workload (T={cfg.T}), all k slots each, fp64: one "
+                      f"token routed to each of the {live.size} non-empty experts plus evenly spaced tokens; "
+                      f"{hit} experts hit; {dt:.1f} s",
+            "experts_hit": int(hit), "experts_nonempty": int(live.size),
+            "full_layer_s_extrapolated": round(cfg.T / rate, 1)}
 
 
 def dense_gemm_reference(args):
@@ -155,6 +185,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs", choices=("all", "none"), default="all",
+                    help="with the default workload, also report every other configuration (fewer steps each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference kernel for HBM byte counters)")
     ap.add_argument("--dense-gemm-reference", action="store_true",
@@ -181,15 +213,67 @@ def main():
         dense_gemm_reference(args)
         return
 
-    import token_permute_grouped_amd as tpg
-    from moe_synth import CONFIGS, generate
+    from moe_synth import CONFIGS
 
     cfg = CONFIGS[args.workload]
     if args.tokens is not None:
         cfg = cfg.with_tokens(args.tokens)
-    t0 = time.perf_counter()
-    inp = generate(cfg, seed=args.seed)
-    log(f"generated {cfg.name} (seed {args.seed}) in {time.perf_counter() - t0:.1f} s")
+    result, inp = measure(cfg, args, detail=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    del inp
+    if args.configs == "all" and args.workload == "skewed" and args.tokens is None:
+        result["per_config"] = per_config(args)
+    print(json.dumps(result), flush=True)
+
+
+# The other configurations of the workload set, reported beside the headline line (fewer steps
+# each; every record from the same run): the mid layer, the W4A8 decode layer at 1, 16 and 256
+# tokens with NVFP4 and MXFP4 weights, and one GPU's share of an expert-parallel layer.
+PER_CONFIG = [("tiny", None), ("mid", None), ("w4a8", 1), ("w4a8", 16), ("w4a8", 256), ("w4a8_mx", 1),
+              ("w4a8_mx", 16), ("w4a8_mx", 256), ("ep_share", None)]
+
+
+def per_config(args):
+    from moe_synth import CONFIGS
+
+    from moe_synth import generate
+
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup = min(args.steps, 10), min(args.warmup, 3)
+    out = []
+    base = {}  # one draw per W4A8 workload: the first T tokens of it are the T-token draw
+    for name, T in PER_CONFIG:
+        cfg = CONFIGS[name] if T is None else CONFIGS[name].with_tokens(T)
+        inp = None
+        if T is not None:
+            if name not in base:
+                t0 = time.perf_counter()
+                base = {name: generate(CONFIGS[name], seed=args.seed)}
+                log(f"generated {name} (seed {args.seed}) in {time.perf_counter() - t0:.1f} s")
+            b = base[name]
+            inp = dict(b, cfg=cfg, logits=b["logits"][:T], x=b["x"][:T], x_scale=b["x_scale"][:T])
+        r, _ = measure(cfg, sub, detail=False, inp=inp)
+        keep = ("value", "unit", "ms_per_step", "dtype", "config", "tflops_forward", "tflops_gemms", "mfma_frac_gemms",
+                "combine_hbm_frac", "stage_ms", "cold_cache_ms_per_step", "graph_ms_per_step",
+                "graph_cold_ms_per_step", "roofline", "steps", "warmup")
+        out.append({k: r[k] for k in keep})
+    return out
+
+
+def measure(cfg, args, detail, inp=None):
+    """One workload: inputs resident on the GPU, then the timed moe_forward steps, cold-cache and
+    graph medians, the stage breakdown and the dominant kernel's roofline.  detail adds the
+    standalone permute measurement."""
+    import torch
+
+    import token_permute_grouped_amd as tpg
+    from moe_synth import generate
+
+    if inp is None:
+        t0 = time.perf_counter()
+        inp = generate(cfg, seed=args.seed)
+        log(f"generated {cfg.name} T={cfg.T} (seed {args.seed}) in {time.perf_counter() - t0:.1f} s")
 
     dev = torch.device("cuda:0")
 
@@ -310,38 +394,40 @@ def main():
         for e in row:
             hip.destroy(e)
 
-    # the permute (tables + row gather) on its own, on the forward's routing: the gather kernel's
-    # HBM rate (the bf16 forward runs no separate gather)
-    S = cfg.T * cfg.k
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
-    tpg.moe_route_topk(d["logits"], d["slot_drop"], p, idx, tw)
-    offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
-    rsrc = torch.empty(S, dtype=torch.int32, device=dev)
-    srow = torch.empty(S, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((S, cfg.H), dtype=torch.uint8 if w4 else torch.int16, device=dev)
-    x_perm_scale = torch.empty((S, cfg.H // 128), dtype=torch.float32, device=dev) if w4 else None
-    pws = torch.empty(max(1, tpg.moe_call_workspace_bytes(p, tpg.MOE_WS_PERMUTE)), dtype=torch.uint8, device=dev)
-    def permute_run(after_forward):
-        pev = [[hip.create() for _ in range(tpg.MOE_N_PERMUTE_EVENTS)] for _ in range(args.steps + 2)]
-        for i in range(args.steps + 2):  # the first two are warm-up
-            if after_forward:
-                step()
-            tpg.moe_permute_timed(d["x"], d["x_scale"], idx, p, offs, rsrc, srow, x_perm, x_perm_scale, pws, pev[i])
-        torch.cuda.synchronize()
-        tab = float(np.mean([hip.ms(pev[i][0], pev[i][1]) for i in range(2, args.steps + 2)]))
-        gat = float(np.mean([hip.ms(pev[i][1], pev[i][2]) for i in range(2, args.steps + 2)]))
-        for row in pev:
-            for e in row:
-                hip.destroy(e)
-        return tab, gat
+    permute_tables_ms = permute_gather_ms = permute_gather_after_fwd_ms = float("nan")
+    if detail:
+        # the permute (tables + row gather) on its own, on the forward's routing: the gather kernel's
+        # HBM rate (the bf16 forward runs no separate gather)
+        S = cfg.T * cfg.k
+        idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+        tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+        tpg.moe_route_topk(d["logits"], d["slot_drop"], p, idx, tw)
+        offs = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
+        rsrc = torch.empty(S, dtype=torch.int32, device=dev)
+        srow = torch.empty(S, dtype=torch.int32, device=dev)
+        x_perm = torch.empty((S, cfg.H), dtype=torch.uint8 if w4 else torch.int16, device=dev)
+        x_perm_scale = torch.empty((S, cfg.H // 128), dtype=torch.float32, device=dev) if w4 else None
+        pws = torch.empty(max(1, tpg.moe_call_workspace_bytes(p, tpg.MOE_WS_PERMUTE)), dtype=torch.uint8, device=dev)
+        def permute_run(after_forward):
+            pev = [[hip.create() for _ in range(tpg.MOE_N_PERMUTE_EVENTS)] for _ in range(args.steps + 2)]
+            for i in range(args.steps + 2):  # the first two are warm-up
+                if after_forward:
+                    step()
+                tpg.moe_permute_timed(d["x"], d["x_scale"], idx, p, offs, rsrc, srow, x_perm, x_perm_scale, pws, pev[i])
+            torch.cuda.synchronize()
+            tab = float(np.mean([hip.ms(pev[i][0], pev[i][1]) for i in range(2, args.steps + 2)]))
+            gat = float(np.mean([hip.ms(pev[i][1], pev[i][2]) for i in range(2, args.steps + 2)]))
+            for row in pev:
+                for e in row:
+                    hip.destroy(e)
+            return tab, gat
 
-    # back to back: each call also pays the write-back of the previous call's x_perm from the
-    # last-level cache (the steady state of a loop of permutes)
-    permute_tables_ms, permute_gather_ms = permute_run(False)
-    # right after a forward, as the permute would run inside a layer's pipeline
-    _, permute_gather_after_fwd_ms = permute_run(True)
-    del x_perm, x_perm_scale, pws
+        # back to back: each call also pays the write-back of the previous call's x_perm from the
+        # last-level cache (the steady state of a loop of permutes)
+        permute_tables_ms, permute_gather_ms = permute_run(False)
+        # right after a forward, as the permute would run inside a layer's pipeline
+        _, permute_gather_after_fwd_ms = permute_run(True)
+        del x_perm, x_perm_scale, pws
 
     T, H, I, k = cfg.T, cfg.H, cfg.I, cfg.k
     R = T * k - (int(inp["slot_drop"].sum()) if inp.get("slot_drop") is not None else 0)
@@ -429,9 +515,14 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    if not detail:
+        for k_ in [k_ for k_ in result if k_.startswith("gather") or k_ == "permute_tables_ms"]:
+            del result[k_]
+    del d, wts, ws, out
+    torch.cuda.empty_cache()
+    return result, inp
+
+
 
 
 if __name__ == "__main__":
