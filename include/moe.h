@@ -58,7 +58,8 @@ typedef enum moe_status {
     MOE_ERR_SHAPE = 2,       /* a size is out of range (see moe_problem) */
     MOE_ERR_UNSUPPORTED = 3, /* an option value this library does not implement */
     MOE_ERR_WORKSPACE = 4,   /* workspace smaller than moe_workspace_bytes() */
-    MOE_ERR_HIP = 5          /* a kernel launch failed */
+    MOE_ERR_HIP = 5,         /* a kernel launch failed */
+    MOE_ERR_SCRATCH = 6      /* moe_forward_noalloc: the problem needs more than MOE_NOALLOC_SCRATCH_BYTES */
 } moe_status;
 
 /* Arithmetic of the expert GEMMs. */
@@ -228,6 +229,22 @@ int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, co
 int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
                       const moe_weights *w, const moe_problem *p, void *out, void *ws, size_t ws_bytes, hipStream_t stream,
                       void *const *stage_events);
+
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The intermediates live in a scratch array the library holds
+ * in device memory, MOE_NOALLOC_SCRATCH_BYTES on each GPU it runs on (allocated
+ * with the library's code on that GPU, kept until the process ends; its address is
+ * looked up on the first call for a device, which should therefore not be made
+ * under graph capture).  The call allocates nothing.  Returns MOE_ERR_SCRATCH when
+ * moe_workspace_bytes(p) exceeds the scratch (it covers, e.g., the W4A8 layer with
+ * H = 7168, I = 2048, E = 32, top-8 up to 256 tokens).  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap in time on one GPU (different streams
+ * without ordering between them) race and give undefined results.  Otherwise the
+ * same work and bitwise the same output as moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
+                        const moe_weights *w, const moe_problem *p, void *out, hipStream_t stream);
 
 /* Diagnostic: the W4A8 dequant of every (e2m1 code, e4m3 block scale s) pair at
  * every nibble position, through the same device routine as the W4A8 GEMMs

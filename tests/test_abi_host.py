@@ -65,6 +65,7 @@ def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     assert lib.moe_grouped_ffn(FAKE, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
     assert lib.moe_unpermute_combine(FAKE, FAKE, FAKE, p, FAKE, None) == status
     assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, p, FAKE, FAKE, 1 << 40, None) == status
+    assert lib.moe_forward_noalloc(FAKE, None, FAKE, FAKE, w, p, FAKE, None) == status
     assert lib.moe_workspace_bytes(p) == 0
     assert lib.moe_call_workspace_bytes(p, tpg.MOE_WS_PERMUTE) == 0
 
@@ -185,8 +186,22 @@ def test_workspace_sizes():
     assert tpg.moe_call_workspace_bytes(big, 99) == 0
 
 
+def test_noalloc_refuses_problems_beyond_its_scratch_on_the_host():
+    """the check comes before any HIP call (no device is touched here)"""
+    lib = tpg.load()
+    w = ctypes.byref(tpg.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    big = _p(T=4096, H=7168, I=2048, E=32, k=8)
+    assert tpg.moe_workspace_bytes(big) > tpg.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(FAKE, None, FAKE, None, w, ctypes.byref(big), FAKE, None) == tpg.MOE_ERR_SCRATCH
+    assert b"64 MiB" in lib.moe_status_str(tpg.MOE_ERR_SCRATCH)
+    # the W4A8 decode layer up to 256 tokens fits
+    dec = _p(T=256, H=7168, I=2048, E=32, k=8, prec=tpg.MOE_PREC_W4A8_MX, swiglu_clamp=10.0)
+    assert tpg.moe_workspace_bytes(dec) <= tpg.MOE_NOALLOC_SCRATCH_BYTES
+    assert lib.moe_forward_noalloc(FAKE, None, FAKE, FAKE, w, ctypes.byref(_p(T=0)), FAKE, None) == tpg.MOE_OK
+
+
 def test_status_strings():
     lib = tpg.load()
-    for s in range(6):
+    for s in range(7):
         assert lib.moe_status_str(s)
     assert lib.moe_status_str(42) == b"unknown status"

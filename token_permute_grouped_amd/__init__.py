@@ -14,7 +14,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtpg_moe.so")
 
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_SCRATCH = range(7)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_PREC_BF16, MOE_PREC_W4A8, MOE_PREC_W4A8_MX = 0, 1, 2
 # precision of a synthetic workload's `prec` name
 PRECISIONS = {"bf16": MOE_PREC_BF16, "w4a8": MOE_PREC_W4A8, "w4a8_mx": MOE_PREC_W4A8_MX}
@@ -24,7 +25,7 @@ MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_FORWARD = 0, 1, 2
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_workspace_bytes", "moe_call_workspace_bytes", "moe_status_str", "moe_last_hip_error", "moe_route_topk", "moe_permute",
-    "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_w4a8_dequant_table",
+    "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward", "moe_forward_timed", "moe_forward_noalloc", "moe_w4a8_dequant_table",
     "moe_w4a8_tile_weights",
 )
 MOE_N_STAGE_EVENTS = 8
@@ -83,10 +84,11 @@ def load() -> ctypes.CDLL:
     lib.moe_unpermute_combine.argtypes = [P, P, P, PP, P, P]
     lib.moe_forward.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P]
     lib.moe_forward_timed.argtypes = [P, P, P, P, PW, PP, P, P, SZ, P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_forward_noalloc.argtypes = [P, P, P, P, PW, PP, P, P]
     lib.moe_w4a8_dequant_table.argtypes = [P, P]
     lib.moe_w4a8_tile_weights.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
     for name in ("moe_route_topk", "moe_permute", "moe_permute_timed", "moe_grouped_ffn", "moe_unpermute_combine", "moe_forward",
-                 "moe_forward_timed", "moe_w4a8_dequant_table", "moe_w4a8_tile_weights"):
+                 "moe_forward_timed", "moe_forward_noalloc", "moe_w4a8_dequant_table", "moe_w4a8_tile_weights"):
         getattr(lib, name).restype = I32
     _lib = lib
     return lib
@@ -200,6 +202,13 @@ def moe_forward_timed(logits, slot_drop, x, x_scale, weights: Weights, problem: 
     _check("moe_forward_timed", load().moe_forward_timed(_ptr(logits), _ptr(slot_drop), _ptr(x), _ptr(x_scale),
                                                          ctypes.byref(weights), ctypes.byref(problem), _ptr(out),
                                                          _ptr(ws), ws_bytes, _stream(stream), ev))
+
+
+def moe_forward_noalloc(logits, slot_drop, x, x_scale, weights: Weights, problem: Problem, out, stream=None):
+    """moe_forward on the library's own device scratch (no workspace argument, nothing allocated)"""
+    _check("moe_forward_noalloc", load().moe_forward_noalloc(_ptr(logits), _ptr(slot_drop), _ptr(x), _ptr(x_scale),
+                                                             ctypes.byref(weights), ctypes.byref(problem), _ptr(out),
+                                                             _stream(stream)))
 
 
 def moe_w4a8_tile_weights(codes, bscale, codes_tiled, bscale_tiled, E, N, K, prec, stream=None):

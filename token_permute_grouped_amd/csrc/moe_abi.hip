@@ -3,7 +3,14 @@
 // synchronises, allocates, or reads device memory on the host.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// Scratch of moe_forward_noalloc: one array per GPU the library runs on (each holds it until the
+// process ends).  In host code `scratch` is only a stand-in for the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is ever used.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace tpg {
 
@@ -247,6 +254,9 @@ const char *moe_status_str(int status) {
         case MOE_ERR_UNSUPPORTED: return "an option value is not supported";
         case MOE_ERR_WORKSPACE: return "workspace is smaller than moe_workspace_bytes()";
         case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        case MOE_ERR_SCRATCH:
+            return "moe_forward_noalloc: the problem's workspace exceeds the library's 64 MiB scratch "
+                   "(use moe_forward with a caller-allocated workspace)";
         default: return "unknown status";
     }
 }
@@ -325,6 +335,49 @@ int moe_forward_timed(const float *logits, const uint8_t *slot_drop, const void 
     for (int i = 0; i < MOE_N_STAGE_EVENTS; ++i)
         if (!stage_events[i]) return MOE_ERR_NULL;
     return forward_impl(logits, slot_drop, x, x_scale, w, p, out, ws, ws_bytes, stream, stage_events);
+}
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxScratchDevices];  // device address of `scratch` on each device, once known
+
+// The device address of `scratch` on the device `stream` belongs to (the current device for the
+// null stream), looked up on the first call for that device with the device made current.
+int scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_status(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e);
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return hip_status(e);
+        if (!ptr) return MOE_ERR_HIP;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+int moe_forward_noalloc(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
+                        const moe_weights *w, const moe_problem *p, void *out, hipStream_t stream) {
+    int st = check_problem(p);
+    if (st) return st;
+    if (p->T == 0) return MOE_OK;
+    if (ws_layout(*p).forward_end > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    void *ws = nullptr;
+    if ((st = scratch_address(stream, &ws))) return st;
+    return forward_impl(logits, slot_drop, x, x_scale, w, p, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int moe_w4a8_dequant_table(uint8_t *out8, hipStream_t stream) {
