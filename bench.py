@@ -185,6 +185,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-launch", action="store_true",
+                    help="W4A8 workloads: the whole forward in one launch (MOE_FLAG_SINGLE_LAUNCH)")
     ap.add_argument("--configs", choices=("all", "none"), default="all",
                     help="with the default workload, also report every other configuration (fewer steps each)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -232,6 +234,8 @@ def main():
 # tokens with NVFP4 and MXFP4 weights, and one GPU's share of an expert-parallel layer.
 PER_CONFIG = [("tiny", None), ("mid", None), ("w4a8", 1), ("w4a8", 16), ("w4a8", 256), ("w4a8_mx", 1),
               ("w4a8_mx", 16), ("w4a8_mx", 256), ("ep_share", None)]
+# also measured as one launch (MOE_FLAG_SINGLE_LAUNCH)
+PER_CONFIG_SINGLE = [("w4a8", 1), ("w4a8_mx", 1), ("w4a8_mx", 16)]
 
 
 def per_config(args):
@@ -243,7 +247,8 @@ def per_config(args):
     sub.steps, sub.warmup = min(args.steps, 10), min(args.warmup, 3)
     out = []
     base = {}  # one draw per W4A8 workload: the first T tokens of it are the T-token draw
-    for name, T in PER_CONFIG:
+    for name, T, single in [(n, t, False) for n, t in PER_CONFIG] + [(n, t, True) for n, t in PER_CONFIG_SINGLE]:
+        sub.single_launch = single
         cfg = CONFIGS[name] if T is None else CONFIGS[name].with_tokens(T)
         inp = None
         if T is not None:
@@ -257,7 +262,10 @@ def per_config(args):
         keep = ("value", "unit", "ms_per_step", "dtype", "config", "tflops_forward", "tflops_gemms", "mfma_frac_gemms",
                 "combine_hbm_frac", "stage_ms", "cold_cache_ms_per_step", "graph_ms_per_step",
                 "graph_cold_ms_per_step", "roofline", "steps", "warmup")
-        out.append({k: r[k] for k in keep})
+        rec = {k: r[k] for k in keep}
+        if single:
+            rec["single_launch"] = True
+        out.append(rec)
     return out
 
 
@@ -288,7 +296,7 @@ def measure(cfg, args, detail, inp=None):
     w4 = cfg.prec != "bf16"
     mx = cfg.prec == "w4a8_mx"
     p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.PRECISIONS[cfg.prec], cfg.glu_interleave,
-                         cfg.swiglu_clamp)
+                         cfg.swiglu_clamp, tpg.MOE_FLAG_SINGLE_LAUNCH if getattr(args, "single_launch", False) else 0)
     d = {k: dt(inp.get(k)) for k in ("logits", "slot_drop", "x", "x_scale", "w1", "w1_bscale", "w1_gscale", "w2",
                                       "w2_bscale", "w2_gscale")}
     layout = tpg.MOE_W4_LAYOUT_ROWS

@@ -104,7 +104,19 @@ typedef struct moe_problem {
      * activation ("ClampedSwiGLU" in Megatron-LM PR #5984's log; the clamped
      * SwiGLU of the FlashInfer fused kernel). */
     float swiglu_clamp;
+    /* 0 or MOE_FLAG_SINGLE_LAUNCH (moe_forward only). */
+    int32_t flags;
 } moe_problem;
+
+/* moe_forward runs the whole W4A8 forward (routing, tables, both GEMMs with the SwiGLU and
+ * the re-quantisation, the combine) in one persistent launch, as the FlashInfer fused kernel
+ * does through 256 tokens per rank (its opening description and Usage section).  Needs
+ * MOE_PREC_W4A8 or MOE_PREC_W4A8_MX, T <= 256, T*k <= 2048, H and I multiples of 1024, and
+ * every weight array below 2 GB (else MOE_ERR_UNSUPPORTED).  Bitwise the same output as the
+ * default multi-launch forward.  Workgroups hand work to each other through counters in the
+ * workspace, which the kernel resets itself (graph replay works); every wait is bounded.  On
+ * this library's kernels it is slower than the default path, which stays the default. */
+#define MOE_FLAG_SINGLE_LAUNCH 1
 
 /* Expert weights (device pointers, borrowed).  bf16: only w1 and w2 are used.
  * w4a8: w1 uint8 [E][2I][H/2], w1_bscale uint8 [E][2I][H/16], w1_gscale fp32 [E];

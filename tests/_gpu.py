@@ -62,12 +62,12 @@ def assert_all_rows_written(dev_bits, n_rows: int, ref_absmax: float, what: str)
 class DeviceProblem:
     """One workload resident on the GPU, plus the output and workspace buffers of each call."""
 
-    def __init__(self, inp: dict):
+    def __init__(self, inp: dict, flags: int = 0):
         self.inp = inp
         cfg = self.cfg = inp["cfg"]
         self.w4 = cfg.prec != "bf16"
         self.p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.PRECISIONS[cfg.prec],
-                                  cfg.glu_interleave, cfg.swiglu_clamp)
+                                  cfg.glu_interleave, cfg.swiglu_clamp, flags)
         self.logits = to_dev(inp["logits"])
         self.drop = to_dev(inp.get("slot_drop"))
         self.x = to_dev(inp["x"])

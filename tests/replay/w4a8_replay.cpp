@@ -1,0 +1,397 @@
+// Host replay of the index arithmetic of the W4A8 GEMMs (one tile per workgroup, persistent, and
+// the single-launch forward's item walk) and of the two front ends (the 1024-thread
+// frontend_small_kernel and the single-launch forward's 256-thread one).
+//
+// The GEMM offsets come from the kernels' own functions (w4a8_index.h, compiled here for the
+// host); the front ends' few index expressions are replayed loop by loop.  For every tile, chunk,
+// wave and lane it checks that each buffer load lies inside its descriptor (or starts beyond it,
+// so that it reads zero), that no 32-bit offset wraps, that every LDS access stays inside its
+// array and every global store inside its buffer.  Problem sizes: the W4A8 decode layer at every
+// token count of its sweep, the small test cases, and random ones up to E = 256, k = 32 and 2048
+// slots, with uniform, skewed, one-expert and dropped-slot routings.  Exit status 0: all in range.
+#include <cstdio>
+#include <cstdlib>
+#include <cstdint>
+#include <vector>
+#include <string>
+
+#include "../../token_permute_grouped_amd/csrc/w4a8_index.h"
+
+using namespace tpg::w4;
+
+static long g_checks = 0, g_fail = 0;
+static std::string g_case;
+
+static void fail(const char *what, long long a, long long b) {
+    if (g_fail < 20) std::printf("OUT OF RANGE [%s] %s: %lld vs %lld\n", g_case.c_str(), what, a, b);
+    ++g_fail;
+}
+// a load of `bytes` at voffset v + soffset so from a descriptor of n bytes: inside, or dead.  The
+// loads that end exactly at their descriptor's end are counted (the checks are tight: the last
+// bytes of every weight array and activation array are addressed).
+static long g_exact_end = 0;
+static void check_load(const char *what, uint32_t v, uint32_t so, int bytes, long long n) {
+    ++g_checks;
+    if ((unsigned long long)v + so >= (1ull << 32)) return fail(what, (long long)v + so, 1ll << 32);
+    if ((long long)v >= n) return;  // past the descriptor: reads zero
+    if ((long long)v + so + bytes > n) fail(what, (long long)v + so + bytes, n);
+    if ((long long)v + so + bytes == n) ++g_exact_end;
+}
+static void check_range(const char *what, long long first, long long bytes, long long n) {
+    ++g_checks;
+    if (first < 0 || first + bytes > n) fail(what, first + bytes, n);
+}
+
+struct Rng {
+    uint64_t s;
+    uint32_t next() {
+        s = s * 6364136223846793005ull + 1442695040888963407ull;
+        return (uint32_t)(s >> 33);
+    }
+    int below(int n) { return (int)(next() % (uint32_t)n); }
+};
+
+struct Problem {
+    int T, H, I, E, k;
+    bool mx, tiled;
+};
+
+// expert-major rows: counts per expert (dropped slots have none), offsets, row_src
+struct Routing {
+    std::vector<int> idx;  // [T*k]: expert or -1
+    std::vector<int> offsets, row_src, slot_row, tiles;
+    int n_mt = 0;
+};
+
+static Routing make_routing(const Problem &p, int mode, Rng &rng) {
+    Routing r;
+    const int S = p.T * p.k;
+    r.idx.assign(S, -1);
+    for (int t = 0; t < p.T; ++t) {
+        // k distinct experts per token
+        std::vector<int> taken;
+        for (int j = 0; j < p.k; ++j) {
+            int e;
+            for (;;) {
+                if (mode == 1) e = (int)((double)p.E * (rng.next() / 4294967296.0) * (rng.next() / 4294967296.0));
+                else if (mode == 2 && (int)taken.size() < p.k) e = (j == 0 ? 0 : rng.below(p.E));
+                else e = rng.below(p.E);
+                bool dup = false;
+                for (int x : taken) dup |= x == e;
+                if (!dup) break;
+                if (mode == 1) mode = 0;  // fall back to uniform for the remaining draws
+            }
+            taken.push_back(e);
+            r.idx[t * p.k + j] = e;
+        }
+        if (mode == 3)
+            for (int j = 0; j < p.k; ++j)
+                if (rng.below(10) == 0) r.idx[t * p.k + j] = -1;
+    }
+    r.offsets.assign(p.E + 1, 0);
+    for (int s = 0; s < S; ++s)
+        if (r.idx[s] >= 0) r.offsets[r.idx[s] + 1]++;
+    for (int e = 0; e < p.E; ++e) r.offsets[e + 1] += r.offsets[e];
+    r.row_src.assign(S, -1);
+    r.slot_row.assign(S, -1);
+    std::vector<int> fill(r.offsets.begin(), r.offsets.end() - 1);
+    for (int s = 0; s < S; ++s)
+        if (r.idx[s] >= 0) {
+            const int row = fill[r.idx[s]]++;
+            r.row_src[row] = s;
+            r.slot_row[s] = row;
+        }
+    // the tile list the forward builds for the W4A8 GEMMs: each expert's 64-row m-tiles together
+    for (int e = 0; e < p.E; ++e) {
+        const int cnt = r.offsets[e + 1] - r.offsets[e];
+        for (int m = 0; m * kBM < cnt; ++m) {
+            r.tiles.push_back(e);
+            r.tiles.push_back(m * kBM);
+        }
+    }
+    r.n_mt = (int)r.tiles.size() / 2;
+    return r;
+}
+
+// tile-list index of expert e's first m-tile
+static int first_mt_of(const Routing &r, int e) {
+    for (int i = 0; i < r.n_mt; ++i)
+        if (r.tiles[2 * i] == e) return i;
+    return -1;
+}
+
+static long long max_m_tiles(const Problem &p) { return ((long long)p.T * p.k + kBM - 1) / kBM + p.E; }
+
+// one GEMM (swiglu: the first) over every tile of the list; kloop: whole-array descriptors (the
+// persistent and single-launch forms), else per-tile ones; gather: activations from the token rows
+static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kloop, bool gather, bool rows_too) {
+    const int S = p.T * p.k, K = swiglu ? p.H : p.I, N = swiglu ? 2 * p.I : p.H;
+    const int sb = p.mx ? 32 : 16, nc = K / kKC, nb_n = N / kBN;
+    const int w_pitch = p.tiled ? kKC / 2 : K / 2, w_step = p.tiled ? 32 * (kKC / 2) : kKC / 2;
+    const int s_pitch = p.tiled ? kKC / sb : K / sb, s_step = p.tiled ? 32 * (kKC / sb) : kKC / sb;
+    const int a_rows = gather ? p.T : S;
+    const long long max_tiles = max_m_tiles(p);
+    if (r.n_mt > max_tiles) fail("tile count", r.n_mt, max_tiles);
+    for (int v = 0; v < r.n_mt * nb_n; ++v) {
+        const Tile t = tile_of(v, nb_n, r.offsets.data(), r.tiles.data(), r.n_mt);
+        if (!t.valid) fail("tile of a live block", v, r.n_mt * nb_n);
+        check_range("tile rows", t.row_begin, t.rows, (long long)r.offsets[t.e + 1]);
+        if (t.rows < 1 || t.row_begin < r.offsets[t.e]) fail("tile rows", t.rows, t.row_begin);
+        if (t.nt < 0 || t.nt >= nb_n) fail("n-tile", t.nt, nb_n);
+        if (t.mt < 0 || t.mt >= r.n_mt) fail("m-tile", t.mt, r.n_mt);
+        for (int NTB = t.rows > 32 ? 2 : 1; NTB <= 2; ++NTB) {  // token blocks the kernel stages
+        // descriptors
+        const long long w_rows = kloop ? (long long)p.E * N : N;
+        const long long nW = w_rows * (K / 2), nWs = w_rows * (K / sb);
+        const long long nA = (long long)(gather || kloop ? a_rows : t.rows) * K;
+        const long long nS = (long long)(gather || kloop ? a_rows : t.rows) * (K / 128) * 4;
+        const int er = kloop ? t.e * N : 0;
+        const int rb = kloop ? t.row_begin : 0;
+        for (int wave = 0; wave < 4; ++wave) {
+            const int blk = er + weight_row(swiglu, t.nt, wave, 0, p.I, 0);
+            // every interleaved row of the block must be the block's own (weight_row(r) = row(0) + r)
+            for (int il : {0, 32})
+                for (int rl = 0; rl < 32; ++rl)
+                    if (weight_row(swiglu, t.nt, wave, rl, p.I, il) != weight_row(swiglu, t.nt, wave, 0, p.I, il) + rl)
+                        fail("weight block rows", rl, il);
+            // weight offsets depend only on (expert, n-tile): once per pair; offsets grow linearly with
+            // the chunk, so its first and last chunk bound every other
+            if (t.mt != first_mt_of(r, t.e) || NTB != 2) continue;
+            for (int lane = 0; lane < 64; ++lane)
+                for (int c : {0, nc - 1}) {
+                    for (int i = 0; i < 4; ++i)
+                        check_load("weight codes", w_code_off(blk, K, lane, i, w_pitch), (uint32_t)(c * w_step), 16, nW);
+                    check_load("weight scales", w_scale_off(blk, K, sb, lane, s_pitch), (uint32_t)(c * s_step),
+                               w_scale_bytes(sb), nWs);
+                }
+        }
+        if (!rows_too) continue;  // the row addressing does not depend on the weight format or layout
+        for (int tid = 0; tid < kThreads; ++tid) {
+            const int g = act_gran(tid);
+            for (int i = 0; i < NTB * 2; ++i) {
+                const int row = act_row(tid, i);
+                int rr;
+                if (gather) {
+                    const int s = r.row_src[t.row_begin + imin(row, t.rows - 1)];
+                    if (s < 0 || s >= S) fail("row_src of a live row", s, S);
+                    rr = s / p.k;
+                } else {
+                    rr = rb + row;
+                }
+                const uint32_t off = row >= t.rows ? kDeadOff : a_off(rr, K, g);
+                for (int c : {0, nc - 1}) check_load("activations", off, (uint32_t)(c * kKC), 16, nA);
+            }
+            const int srow = act_scale_row(tid);
+            int rs = gather ? r.row_src[t.row_begin + imin(srow, t.rows - 1)] / p.k : rb + srow;
+            const uint32_t so = srow >= t.rows ? kDeadOff : s_off(rs, K);
+            for (int c : {0, nc - 1}) check_load("activation scales", so, (uint32_t)(c * 8), 8, nS);
+        }
+        // the epilogue's stores (the LDS accesses, the same for every tile, are checked by replay_lds)
+        for (int lane = 0; lane < 64; ++lane) {
+            const int h = lane >> 5;
+            (void)h;
+            if (false) {
+            for (int i = 0; i < 4; ++i) check_range("LDS weight write", lds_wcode(lane, i), 16, kWScales);
+            check_range("LDS weight scale write", lds_wscale(lane, p.mx), p.mx ? 4 : 8, kWSlot);
+            const int h = lane >> 5;
+            for (int q = 0; q < 2; ++q) {
+                for (int tt = 0; tt < 2; ++tt) {
+                    check_range("LDS weight read", lds_wread(lane) + 64 * q + 16 * tt, 16, kWScales);
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        const int rr = tb * 32 + (lane & 31);
+                        check_range("LDS activation read", lds_act(rr, gran_lo(p.mx, q, tt, h)), 16, kActBuf);
+                        check_range("LDS activation read", lds_act(rr, gran_hi(p.mx, q, tt, h)), 16, kActBuf);
+                    }
+                }
+                check_range("LDS scale read", p.mx ? lds_wsread(lane) - 4 * h + 4 * q : lds_wsread(lane) + 8 * q, 4,
+                            kWSlot);
+                for (int tb = 0; tb < NTB; ++tb)
+                    for (int buf = 0; buf < 2; ++buf)
+                        check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kBM * 2);
+            }
+            }
+            for (int wave = 0; wave < 4; ++wave)
+                for (int tb = 0; tb < NTB; ++tb) {
+                    const int tok = tb * 32 + (lane & 31);
+                    if (tok >= t.rows) continue;
+                    for (int g4 = 0; g4 < 4; ++g4) {
+                        if (swiglu && wave < 2) {
+                            const int col = h_col(t.nt, wave, g4, lane);
+                            if (col + 4 > p.I) fail("h column", col + 4, p.I);
+                            check_range("h store", ((long long)(t.row_begin + tok) * p.I + col) * 4, 16, (long long)S * p.I * 4);
+                        }
+                        if (!swiglu) {
+                            const int col = y_col(t.nt, wave, g4, lane);
+                            if (col + 4 > N) fail("y column", col + 4, N);
+                            check_range("y store", ((long long)(t.row_begin + tok) * p.H + col) * 2, 8, (long long)S * p.H * 2);
+                        }
+                    }
+                }
+        }
+        }
+    }
+}
+
+// every LDS access of the tile pipeline (the same for every tile): activation and scale staging,
+// weight staging, operand reads, the SwiGLU hand-over
+static void replay_lds() {
+    for (bool mx : {false, true})
+        for (int NTB = 1; NTB <= 2; ++NTB) {
+            for (int tid = 0; tid < kThreads; ++tid) {
+                for (int i = 0; i < NTB * 2; ++i) check_range("LDS activation write", lds_act(act_row(tid, i), act_gran(tid)), 16, kActBuf);
+                if (tid < NTB * 32)
+                    for (int buf = 0; buf < 2; ++buf) check_range("LDS scale write", 4 * lds_xs(buf, tid, 0), 8, 4 * 2 * kBM * 2);
+            }
+            for (int lane = 0; lane < 64; ++lane) {
+                const int h = lane >> 5;
+                for (int i = 0; i < 4; ++i) check_range("LDS weight write", lds_wcode(lane, i), 16, kWScales);
+                check_range("LDS weight scale write", lds_wscale(lane, mx), mx ? 4 : 8, kWSlot);
+                for (int q = 0; q < 2; ++q) {
+                    for (int tt = 0; tt < 2; ++tt) {
+                        check_range("LDS weight read", lds_wread(lane) + 64 * q + 16 * tt, 16, kWScales);
+                        for (int tb = 0; tb < NTB; ++tb) {
+                            const int rr = tb * 32 + (lane & 31);
+                            check_range("LDS activation read", lds_act(rr, gran_lo(mx, q, tt, h)), 16, kActBuf);
+                            check_range("LDS activation read", lds_act(rr, gran_hi(mx, q, tt, h)), 16, kActBuf);
+                        }
+                    }
+                    check_range("LDS scale read", mx ? lds_wsread(lane) - 4 * h + 4 * q : lds_wsread(lane) + 8 * q, 4,
+                                kWSlot);
+                    for (int tb = 0; tb < NTB; ++tb)
+                        for (int buf = 0; buf < 2; ++buf)
+                            check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kBM * 2);
+                }
+                for (int wu = 0; wu < 2; ++wu)
+                    for (int tb = 0; tb < NTB; ++tb)
+                        for (int v16 = 0; v16 < 16; ++v16)
+                            check_range("LDS hand-over", 4 * lds_xch(wu, NTB, tb, v16, lane), 4, kActBuf);
+            }
+        }
+}
+
+// the single-launch forward's counters, re-quantisation and combine
+static void replay_fused_tails(const Problem &p, const Routing &r) {
+    const int S = p.T * p.k, n_cb = p.I / 128, nb1 = 2 * p.I / kBN;
+    const long long max_tiles = max_m_tiles(p);
+    constexpr int kLine = 32;  // counters one 128-byte line apart
+    const long long n_counters = (max_tiles * n_cb + max_tiles) * kLine;
+    for (int v = 0; v < r.n_mt * nb1; ++v) {
+        const Tile t = tile_of(v, nb1, r.offsets.data(), r.tiles.data(), r.n_mt);
+        const int cb = t.nt >> 1;
+        check_range("re-quantisation counter", ((long long)t.mt * n_cb + cb) * kLine, 1, max_tiles * n_cb * kLine);
+        check_range("ready counter", (max_tiles * n_cb + t.mt) * kLine, 1, n_counters);
+        for (int wave = 0; wave < 4; ++wave)
+            for (int i = 0; i < kBM / 4; ++i) {
+                const int rr = wave + 4 * i;
+                if (rr >= t.rows) continue;
+                const long long row = t.row_begin + rr;
+                for (int lane = 0; lane < 64; ++lane) {
+                    check_range("h32 read", (row * p.I + cb * 128 + 2 * lane) * 4, 8, (long long)S * p.I * 4);
+                    check_range("h8 store", row * p.I + cb * 128 + 2 * lane, 2, (long long)S * p.I);
+                }
+                check_range("hs store", row * n_cb + cb, 1, (long long)S * n_cb);
+            }
+    }
+    // each 128-column block of h: exactly two GEMM1 tiles per m-tile
+    std::vector<int> pairs((size_t)r.n_mt * n_cb, 0);
+    for (int v = 0; v < r.n_mt * nb1; ++v) {
+        const Tile t = tile_of(v, nb1, r.offsets.data(), r.tiles.data(), r.n_mt);
+        pairs[(size_t)t.mt * n_cb + (t.nt >> 1)]++;
+    }
+    for (int c : pairs)
+        if (c != 2) fail("GEMM1 tiles per 128-column block", c, 2);
+    // the combine: token tok, 16-byte chunk c of its row, slots j (rows and weights staged in LDS)
+    for (int tok = 0; tok < p.T; ++tok)
+        for (int j = 0; j < p.k; ++j) {
+            check_range("slot_row read", (long long)tok * p.k + j, 1, S);
+            check_range("LDS slot row", j * 4, 4, 4096);
+            const int row = r.slot_row[tok * p.k + j];
+            if (row < 0) continue;
+            check_range("y read", ((long long)row * p.H + (p.H / 8 - 1) * 8) * 2, 16, (long long)S * p.H * 2);
+            check_range("y read", (long long)row * p.H * 2, 16, (long long)S * p.H * 2);
+        }
+    check_range("out store", ((long long)(p.T - 1) * p.H + (p.H / 8 - 1) * 8) * 2, 16, (long long)p.T * p.H * 2);
+}
+
+// the front ends: routing rows, LDS ids and counts, tables and tile list
+static void replay_front_end(const Problem &p, const Routing &r, int threads) {
+    const int S = p.T * p.k, waves = threads / 64;
+    const int sid_n = threads == 1024 ? 1024 : 2048;
+    if (S > sid_n) fail("slots of the front end", S, sid_n);
+    // routing: four 16-lane rows per wave, tokens t0 + lane / 16, t0 = 4 w + 4 waves i
+    for (int w = 0; w < waves; ++w)
+        for (int t0 = w * 4; t0 < p.T; t0 += waves * 4)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int t = t0 + (lane >> 4);
+                if (t >= p.T) continue;  // loads use token T - 1, nothing is stored
+                const int i = lane & 15;
+                for (int h = 0; h < 16; ++h) {
+                    const int j = i + 16 * h;
+                    if (j >= p.k) continue;
+                    check_range("LDS expert id", (long long)t * p.k + j, 1, sid_n);
+                    check_range("topk store", (long long)t * p.k + j, 1, S);
+                }
+                for (int q = 0; q < 16; ++q)
+                    if (i + 16 * q < p.E) check_range("logit read", (long long)t * p.E + i + 16 * q, 1, (long long)p.T * p.E);
+            }
+    // counts, ranks: per-wave counters [waves][256], rows < S
+    for (int s = 0; s < S; ++s) {
+        const int x = r.idx[s];
+        const int w = (s % threads) / 64;
+        if (x >= 0) {
+            check_range("LDS count", (long long)w * 256 + x, 1, (long long)waves * 256);
+            check_range("row_src store", r.slot_row[s], 1, S);
+        }
+        check_range("slot_row store", s, 1, S);
+    }
+    check_range("offsets store", p.E, 1, p.E + 1);
+    check_range("tile list", (long long)r.n_mt * 2 - 1, 1, 2 * max_m_tiles(p));
+}
+
+int main() {
+    g_case = "LDS";
+    replay_lds();
+    Rng rng{12345};
+    std::vector<Problem> probs;
+    for (int T : {1, 2, 4, 8, 16, 32, 64, 128, 256})
+        for (bool mx : {false, true})
+            for (bool tiled : {false, true}) probs.push_back({T, 7168, 2048, 32, 8, mx, tiled});
+    // the small W4A8 GPU cases (K multiples of 256)
+    const int small[][5] = {{64, 256, 256, 8, 2}, {1, 256, 256, 4, 4}, {100, 512, 512, 6, 3}, {300, 768, 768, 5, 2},
+                            {90, 512, 256, 4, 2}, {32, 1024, 1024, 64, 8}, {30, 512, 512, 6, 3}, {16, 1024, 1024, 32, 8}};
+    for (auto &c : small)
+        for (bool mx : {false, true}) probs.push_back({c[0], c[1], c[2], c[3], c[4], mx, false});
+    // random shapes: E up to 256, k up to 32, up to 2048 slots, H, I multiples of 1024
+    for (int n = 0; n < 8; ++n) {
+        const int E = 1 + rng.below(n < 4 ? 256 : 64), k = 1 + rng.below(E < 32 ? E : 32);
+        const int T = 1 + rng.below(2048 / k < 256 ? 2048 / k : 256) / (n < 4 ? 4 : 1);
+        probs.push_back({T, 1024 * (1 + rng.below(4)), 1024 * (1 + rng.below(3)), E, k, rng.below(2) == 1,
+                         rng.below(2) == 1});
+    }
+    for (const Problem &p : probs)
+        for (int mode = 0; mode < 4; ++mode) {
+            char buf[160];
+            std::snprintf(buf, sizeof buf, "T=%d H=%d I=%d E=%d k=%d %s %s routing %d", p.T, p.H, p.I, p.E, p.k,
+                          p.mx ? "mxfp4" : "nvfp4", p.tiled ? "tiled" : "rows", mode);
+            g_case = buf;
+            const Routing r = make_routing(p, mode, rng);
+            const bool fits = (long long)p.E * 2 * p.I * (p.H / 2) < (1ll << 31);
+            const bool kloop_ok = p.H % 1024 == 0 && p.I % 1024 == 0 && fits;
+            const bool rows_too = p.mx == p.tiled;  // once per shape and routing (two of the four formats)
+            for (bool kloop : {false, true}) {
+                if (kloop && !kloop_ok) continue;
+                replay_gemm(p, r, true, kloop, true, rows_too);   // the forward: GEMM1 gathers through row_src
+                replay_gemm(p, r, true, kloop, false, rows_too);  // moe_grouped_ffn: GEMM1 on x_perm
+                replay_gemm(p, r, false, kloop, false, rows_too);
+            }
+            const int S = p.T * p.k;
+            if (kloop_ok && p.T <= 256 && S <= 2048 && rows_too) {
+                replay_fused_tails(p, r);
+                replay_front_end(p, r, 256);
+            }
+            if (S <= 1024 && p.T <= 256) replay_front_end(p, r, 1024);
+        }
+    std::printf("%zu problems x 4 routings: %ld index checks, %ld out of range, %ld loads ending exactly at their "
+                "buffer's end\n", probs.size(), g_checks, g_fail, g_exact_end);
+    return g_fail == 0 && g_exact_end > 0 ? 0 : 1;
+}

@@ -51,7 +51,7 @@ def _p(**kw):
     (dict(swiglu_clamp=float("nan")), tpg.MOE_ERR_UNSUPPORTED),
     (dict(prec=1, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=1, I=384), tpg.MOE_ERR_SHAPE),
     (dict(prec=2, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=2, I=384), tpg.MOE_ERR_SHAPE), (dict(prec=3), tpg.MOE_ERR_UNSUPPORTED),
-    (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE),
+    (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE), (dict(flags=2), tpg.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     lib = tpg.load()
@@ -184,6 +184,22 @@ def test_workspace_sizes():
     assert (tpg.moe_call_workspace_bytes(big, tpg.MOE_WS_PERMUTE)
             < tpg.moe_call_workspace_bytes(big, tpg.MOE_WS_GROUPED_FFN) < n)
     assert tpg.moe_call_workspace_bytes(big, 99) == 0
+
+
+def test_single_launch_flag_needs_an_eligible_problem():
+    """MOE_FLAG_SINGLE_LAUNCH: W4A8 only, at most 256 tokens and 2048 slots, H and I multiples of 1024;
+    otherwise MOE_ERR_UNSUPPORTED before anything is enqueued"""
+    lib = tpg.load()
+    w = ctypes.byref(tpg.Weights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    one = tpg.MOE_FLAG_SINGLE_LAUNCH
+    for kw in (dict(prec=0, H=1024, I=1024), dict(prec=1, T=300, H=1024, I=1024),
+               dict(prec=2, T=256, k=16, E=32, H=1024, I=1024), dict(prec=1, H=1536, I=1024),
+               dict(prec=2, H=1024, I=512)):
+        pr = _p(flags=one, **kw)
+        n = tpg.moe_workspace_bytes(pr)
+        assert n > 0
+        assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, ctypes.byref(pr), FAKE, FAKE, n, None) == \
+            tpg.MOE_ERR_UNSUPPORTED, kw
 
 
 def test_noalloc_refuses_problems_beyond_its_scratch_on_the_host():

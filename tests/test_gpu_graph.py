@@ -27,6 +27,9 @@ CASES = [
     MoeConfig("graph_w4a8_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8", swiglu_clamp=10.0),
     MoeConfig("graph_w4a8_mx_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
     MoeConfig("graph_w4a8_mx", T=64, H=512, I=256, E=8, k=2, prec="w4a8_mx", swiglu_clamp=10.0),
+    # the single-launch forward with two token blocks per tile (its hand-off words reset in-kernel)
+    MoeConfig("graph_w4a8_mx_fused_t100", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8_mx", glu_interleave=32,
+              swiglu_clamp=10.0, drop_p=0.1),
 ]
 
 
@@ -34,13 +37,19 @@ def _eager(d: DeviceProblem):
     return bf16_host(d.forward())
 
 
-@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
-def test_forward_graph_replay(cfg):
-    print(f"[gpu graph] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec}", flush=True)
+SINGLE = {"graph_w4a8_persistent", "graph_w4a8_mx_fused_t100"}  # also with MOE_FLAG_SINGLE_LAUNCH
+
+
+@pytest.mark.parametrize("cfg,flags", [(c, 0) for c in CASES]
+                         + [(c, tpg.MOE_FLAG_SINGLE_LAUNCH) for c in CASES if c.name in SINGLE],
+                         ids=lambda v: v.name if isinstance(v, MoeConfig) else ("single_launch" if v else "default"))
+def test_forward_graph_replay(cfg, flags):
+    print(f"[gpu graph] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec} flags={flags}",
+          flush=True)
     inp_a, other = generate(cfg, seed=0), generate(cfg, seed=1)
     # the second input set: seed 1's logits, activations (and drop mask) with seed 0's weights
     inp_b = dict(inp_a, **{k: other[k] for k in ("logits", "x", "x_scale", "slot_drop") if k in other})
-    da, db = DeviceProblem(inp_a), DeviceProblem(inp_b)
+    da, db = DeviceProblem(inp_a, flags), DeviceProblem(inp_b, flags)
     want = [_eager(da), _eager(db)]
     assert (want[0] != want[1]).any()  # the two routings differ
 

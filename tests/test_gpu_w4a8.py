@@ -37,6 +37,11 @@ SMALL = {
     # tiles per workgroup, each next tile's first chunks prefetched), interleave-32 and dropped slots
     "w4_persistent_il_drop": MoeConfig("w4_persistent_il_drop", T=32, H=1024, I=1024, E=64, k=8, prec="w4a8",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    # the single-launch forward (H, I multiples of 1024, at most 256 tokens and 2048 slots): two
+    # token blocks per tile, interleave and drops; and many small experts (m-tiles of a few rows)
+    "w4_fused_t100_il_drop": MoeConfig("w4_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8",
+                                       glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    "w4_fused_e256": MoeConfig("w4_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8", swiglu_clamp=10.0),
 }
 
 
@@ -172,6 +177,52 @@ def test_grouped_ffn_full_layer_sampled_rows():
     R = int(off[-1])
     assert_all_rows_written(y, R, float(np.abs(ref).max()), "w4a8 T=256 y_perm")
     assert (bf16_host(y)[R:] == 0xFFFF).all()
+
+
+def _fused_words(ws):
+    """(go, next_item, done, err) of the single-launch forward's hand-off block (workspace offset 0,
+    one word per 128-byte line)"""
+    b = ws[:512].cpu().numpy()
+    return (int(b[:8].view(np.uint64)[0]), *(int(b[o:o + 4].view(np.uint32)[0]) for o in (128, 256, 384)))
+
+
+def single_launch(inp):
+    return DeviceProblem(inp, flags=tpg.MOE_FLAG_SINGLE_LAUNCH)
+
+
+@pytest.mark.parametrize("case", ["w4_persistent_il_drop", "w4_fused_t100_il_drop", "w4_fused_e256"]
+                         + [f"T{T}" for T in w4a8_sweep_tokens()])
+def test_single_launch_forward_equals_default(case):
+    """MOE_FLAG_SINGLE_LAUNCH: the whole forward in one persistent launch, bitwise the default
+    multi-launch forward (and within the bar of the oracle through it)"""
+    inp, d = small(case) if case in SMALL else sweep_case(int(case[1:]))
+    one = bf16_host(single_launch(inp).forward())
+    n_diff = int((one != bf16_host(d.forward())).sum())
+    print(f"[gpu w4a8] {case}: single-launch forward vs default, {n_diff} differing elements", flush=True)
+    assert n_diff == 0
+
+
+@pytest.mark.parametrize("T", [1, 16, 100, 256])
+def test_single_launch_forward_leaves_its_words_clean(T):
+    """after the single-launch forward: the go word reset, no bounded wait gave up, every workgroup
+    counted out, every item claimed; the same workspace then serves another token count"""
+    inp, d0 = sweep_case(T)
+    d = single_launch(inp)
+    ws = d.workspace(tpg.MOE_WS_FORWARD, fill=0x33)
+    out = bf16_host(d.forward(ws))
+    go, claimed, done, err = _fused_words(ws)
+    print(f"[gpu w4a8] T={T}: go={go:#x} items claimed={claimed} workgroups={done} err={err}", flush=True)
+    assert go == 0 and err == 0 and done > 0 and claimed >= done
+    assert (out == bf16_host(d0.forward())).all()
+    # a smaller problem on the same (larger) workspace, then this one again
+    inp2, d2 = sweep_case(max(1, T // 4))
+    d2 = single_launch(inp2)
+    n2 = tpg.moe_workspace_bytes(d2.p)
+    o2 = torch.full((d2.cfg.T, d2.cfg.H), -1, dtype=torch.int16, device=DEV)
+    tpg.moe_forward(d2.logits, d2.drop, d2.x, d2.x_scale, d2.weights, d2.p, o2, ws, n2)
+    assert (bf16_host(o2) == bf16_host(d2.forward())).all()
+    assert (bf16_host(d.forward(ws)) == out).all()
+    assert _fused_words(ws)[0] == 0 and _fused_words(ws)[3] == 0
 
 
 def test_forward_deterministic_and_workspace_reuse():

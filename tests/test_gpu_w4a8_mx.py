@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
+import token_permute_grouped_amd as tpg
 from moe_synth import CONFIGS, MoeConfig, generate
 from moe_synth.gen import w4a8_sweep_tokens
 from tests._gpu import DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, whole_tiles
@@ -31,6 +32,10 @@ SMALL = {
     # K a multiple of 1024 and T <= 32: the persistent GEMMs with several tiles per workgroup
     "mx_persistent_il_drop": MoeConfig("mx_persistent_il_drop", T=32, H=1024, I=1024, E=64, k=8, prec="w4a8_mx",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    # the single-launch forward: two token blocks per tile, interleave and drops; many small experts
+    "mx_fused_t100_il_drop": MoeConfig("mx_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8_mx",
+                                       glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
+    "mx_fused_e256": MoeConfig("mx_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
 }
 
 
@@ -148,3 +153,14 @@ def test_scales_outside_the_fp8_decoder_range_stay_exact(lo, hi):
     err = rel_err(bf16_f64(bf16_host(d.forward())), ref)
     print(f"[gpu w4a8_mx] scales {lo}..{hi - 1}: forward, max|err|/max|ref| = {err:.3e}")
     assert err <= W4A8_BAR
+
+
+@pytest.mark.parametrize("case", ["mx_persistent_il_drop", "mx_fused_t100_il_drop", "mx_fused_e256"]
+                         + [f"T{T}" for T in w4a8_sweep_tokens()])
+def test_single_launch_forward_equals_default(case):
+    """MOE_FLAG_SINGLE_LAUNCH with MXFP4 weights: bitwise the default multi-launch forward"""
+    inp, d = small(case) if case in SMALL else sweep_case(int(case[1:]))
+    one = bf16_host(DeviceProblem(inp, flags=tpg.MOE_FLAG_SINGLE_LAUNCH).forward())
+    n_diff = int((one != bf16_host(d.forward())).sum())
+    print(f"[gpu w4a8_mx] {case}: single-launch forward vs default, {n_diff} differing elements", flush=True)
+    assert n_diff == 0

@@ -24,6 +24,7 @@ CASES = [
     CONFIGS["w4a8_mx"].with_tokens(8),
     MoeConfig("na_w4_drop", T=30, H=512, I=512, E=6, k=3, prec="w4a8", glu_interleave=32, swiglu_clamp=10.0,
               drop_p=0.1),
+    CONFIGS["w4a8"].with_tokens(4),  # also run with MOE_FLAG_SINGLE_LAUNCH below
 ]
 
 
@@ -39,7 +40,7 @@ def test_noalloc_forward_equals_forward_on_calls_in_a_row():
         print(f"[no-alloc] call {i}: {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec}",
               flush=True)
         inp = generate(cfg, seed=i)
-        d = DeviceProblem(inp)
+        d = DeviceProblem(inp, tpg.MOE_FLAG_SINGLE_LAUNCH if i == len(CASES) - 1 else 0)
         assert tpg.moe_workspace_bytes(d.p) <= tpg.MOE_NOALLOC_SCRATCH_BYTES
         a = bf16_host(_noalloc(d))
         b = bf16_host(d.forward())

@@ -40,10 +40,13 @@ class MoeError(RuntimeError):
         self.hip_error = hip
 
 
+MOE_FLAG_SINGLE_LAUNCH = 1
+
+
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("prec", ctypes.c_int32), ("glu_interleave", ctypes.c_int32),
-                ("swiglu_clamp", ctypes.c_float)]
+                ("swiglu_clamp", ctypes.c_float), ("flags", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
@@ -124,8 +127,8 @@ def _check(fn: str, st: int):
         raise MoeError(fn, st, lib.moe_status_str(st).decode(), lib.moe_last_hip_error() if st == MOE_ERR_HIP else 0)
 
 
-def make_problem(T, H, I, E, k, prec=MOE_PREC_BF16, glu_interleave=0, swiglu_clamp=0.0) -> Problem:
-    return Problem(T, H, I, E, k, prec, glu_interleave, swiglu_clamp)
+def make_problem(T, H, I, E, k, prec=MOE_PREC_BF16, glu_interleave=0, swiglu_clamp=0.0, flags=0) -> Problem:
+    return Problem(T, H, I, E, k, prec, glu_interleave, swiglu_clamp, flags)
 
 
 def make_weights(w1, w2, w1_bscale=None, w1_gscale=None, w2_bscale=None, w2_gscale=None,

@@ -30,24 +30,6 @@ __device__ __forceinline__ uint4 load_once(const uint4 *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void fma8(float *acc, float w, const uint4 &v) {
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        acc[2 * q] = fmaf(w, __uint_as_float(u[q] << 16), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(w, __uint_as_float(u[q] & 0xffff0000u), acc[2 * q + 1]);
-    }
-}
-
-__device__ __forceinline__ uint4 pack8(const float *a) {
-    uint4 o;
-    o.x = pack_bf16x2(a[0], a[1]);
-    o.y = pack_bf16x2(a[2], a[3]);
-    o.z = pack_bf16x2(a[4], a[5]);
-    o.w = pack_bf16x2(a[6], a[7]);
-    return o;
-}
-
 constexpr int kThreads = 512;
 }  // namespace
 
@@ -77,14 +59,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4 *__restri
             for (int q = 0; q < 8; ++q) {
                 const int j = j0 + q;
                 if (j < k && rows[j] >= 0) {
-                    fma8(acc[0], w[j], v[0][q]);
-                    fma8(acc[1], w[j], v[1][q]);
+                    combine_fma8(acc[0], w[j], v[0][q]);
+                    combine_fma8(acc[1], w[j], v[1][q]);
                 }
             }
         }
         const __amdgpu_buffer_rsrc_t dst = row_rsrc(out + t * row_vec, row_vec * 16);
-        store16_through(dst, c0 * 16, pack8(acc[0]));
-        if (two) store16_through(dst, c1 * 16, pack8(acc[1]));
+        store16_through(dst, c0 * 16, combine_pack8(acc[0]));
+        if (two) store16_through(dst, c1 * 16, combine_pack8(acc[1]));
     }
 }
 

@@ -54,6 +54,9 @@
 #include <algorithm>
 
 #include "moe_internal.h"
+#include "route_token.h"
+#include "tile_list.h"
+#include "w4a8_index.h"
 
 namespace tpg {
 
@@ -66,13 +69,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = kGemmBMW4A8;  // token rows per m-tile (2 blocks of 32)
-constexpr int kBN = 128;          // weight rows per workgroup (4 waves x 32)
-constexpr int kKC = 256;          // K per chunk
-constexpr int kNBuf = 4;          // weight register sets (weights kNBuf - 1 chunks ahead)
-constexpr int kThreads = 256;
-constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB, two buffers)
-static_assert(kBM == 64, "the tile holds at most two 32-token blocks");
+static_assert(w4::kBM == kGemmBMW4A8, "the tile holds at most two 32-token blocks");
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
 
@@ -107,8 +104,14 @@ __device__ __forceinline__ u32x2 dequant8(uint32_t x, u32x2 t) {
 }
 
 
-// LDS slot (16-byte granule) of granule g of staged token row r: 16 granules per row
-__device__ __forceinline__ int aslot(int r, int g) { return g ^ (r & 15); }
+using w4::kActBuf;
+using w4::kBM;
+using w4::kBN;
+using w4::kKC;
+using w4::kNBuf;
+using w4::kThreads;
+using w4::kWSlot;
+using w4::Tile;
 
 // LDS barrier without a global-memory fence: register loads stay in flight across it
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -142,58 +145,35 @@ struct WChunk {
     u32x2 s;
 };
 
-// per-wave LDS staging of one chunk's weights in rows: 32 code rows of 128 bytes padded to
-// 144 (so that 16 consecutive rows read at one column hit 16 distinct bank groups), then
-// 32 scale rows of 16 bytes
-constexpr int kWRow = 144;
-constexpr int kWScales = 32 * kWRow;
-constexpr int kWSlot = kWScales + 32 * 16;  // 5120 bytes per chunk and wave
-
-// One work item of the block -> tile map: expert, first row, live rows, n-tile.
-struct W4Tile {
-    bool valid;
-    int e, row_begin, rows, nt;
+// Tile order of the multi-launch GEMMs: virtual blocks v0, v0 + stride, ... (the persistent
+// form), or v0 alone.  No waits and nothing to signal.
+struct StaticSched {
+    int v, stride, nb_n, n_mt;
+    const int32_t *offsets, *tiles;
+    __device__ Tile first() { return w4::tile_of(v, nb_n, offsets, tiles, n_mt); }
+    __device__ Tile next() {
+        v += stride;
+        return w4::tile_of(v, nb_n, offsets, tiles, n_mt);
+    }
+    __device__ void before_act(const Tile &) {}
+    __device__ void after_tile(const Tile &) {}
 };
 
-// Virtual block v -> tile.  The tile list holds each expert's m-tiles together.  Expert e's
-// blocks are [first * nb_n, (first + nm) * nb_n); they run in units of G n-tiles, the nm
-// m-tiles of an n-tile G blocks apart: with G = 8 those land on one XCD (block b runs on XCD
-// b mod 8, and the persistent grid's stride is a multiple of 8) at the same time, so the
-// weights an expert's second m-tile streams are L2 hits.
-__device__ __forceinline__ W4Tile w4a8_tile_of(int v, int nb_n, const int32_t *__restrict__ offsets,
-                                              const int32_t *__restrict__ tiles, int n_mt) {
-    W4Tile t{};
-    const int tq = v / nb_n;  // a tile of the expert this block works for
-    t.valid = tq < n_mt;
-    if (!t.valid) return t;
-    t.e = tiles[2 * tq];
-    const int first = tq - tiles[2 * tq + 1] / kBM;
-    const int nm = (offsets[t.e + 1] - offsets[t.e] + kBM - 1) / kBM;
-    const int G = nb_n % 8 == 0 ? 8 : nb_n % 4 == 0 ? 4 : nb_n % 2 == 0 ? 2 : 1;
-    const int r = v - first * nb_n, unit = nm * G;
-    const int mt = first + (r % unit) / G;
-    t.nt = (r / unit) * G + (r % unit) % G;
-    t.row_begin = offsets[t.e] + tiles[2 * mt + 1];
-    t.rows = min(kBM, offsets[t.e + 1] - t.row_begin);
-    return t;
-}
-
-// The tiles of virtual blocks v0, v0 + stride, ... (kLoop), or of v0 alone.  With kLoop the
-// loads a tile's last steps would issue past its last chunk fetch the next tile's first
-// chunks instead, so the pipeline runs on across tiles and only the first tile pays for a
-// prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at the same
-// register set and buffer phase).
-template <bool kSwiGLU, bool kMX, int NTB, bool kLoop>
-__device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, const int32_t *__restrict__ offsets,
-                                           const int32_t *__restrict__ tiles, int n_mt, unsigned char *act,
-                                           float *xsl, unsigned char *wlds, const u32x2 *lut) {
+// The tiles sc hands out, in its order (kLoop: all of them, one after another; otherwise its
+// first only).  With kLoop the loads a tile's last steps would issue past its last chunk fetch
+// the next tile's first chunks instead, so the pipeline runs on across tiles and only the first
+// tile pays for a prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at
+// the same register set and buffer phase).  sc.before_act(t) runs (uniformly, in every thread)
+// before the first activation load of tile t, sc.after_tile(t) after t's output is written.
+template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched>
+__device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned char *act, float *xsl,
+                                           unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, kb_n = K / 128;
     const int nc = K / kKC;
-    const int nb_n = g.N / kBN;
-    const int sg = tid & 15, sr = tid >> 4;
-    const int srow = min(tid, kBM - 1);
+    const int sg = w4::act_gran(tid);
+    const int srow = w4::act_scale_row(tid);
     constexpr int kSB = kMX ? 32 : 16;  // K values per weight block scale
     const bool gather = g.row_src != nullptr;
 
@@ -213,7 +193,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     struct Rs {
         __amdgpu_buffer_rsrc_t W, Ws, A, S;
     };
-    auto make_rs = [&](const W4Tile &t) {
+    auto make_rs = [&](const Tile &t) {
         Rs r;
         const int64_t w0 = kLoop ? 0 : (int64_t)t.e * g.N;  // first weight row the descriptor starts at
         const int64_t nw = kLoop ? (int64_t)g.E * g.N : g.N;
@@ -232,43 +212,35 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
         uint32_t woff[4], wsoff, aoff[NTB * 2], soff;
         int src[NTB * 2 + 1];
     };
-    auto start_addr = [&](Addr &a, const W4Tile &t) {
-        auto weight_row = [&](int rl) {  // weight matrix row of row rl of this wave
-            if (kSwiGLU) {  // waves 0, 1: gate rows of h columns nt*64 + [0, 64); waves 2, 3: the matching up rows
-                const bool up = wave >= 2;
-                const int c = t.nt * (kBN / 2) + (wave & 1) * 32 + rl;
-                return g.il == 0 ? (up ? g.I + c : c) : (c / g.il) * 2 * g.il + (up ? g.il : 0) + c % g.il;
-            }
-            return t.nt * kBN + wave * 32 + rl;
-        };
+    auto start_addr = [&](Addr &a, const Tile &t) {
         const int er = kLoop ? t.e * g.N : 0;  // expert's first row within the descriptor
         // a wave's 32 weight rows are one 32-row block of the matrix (weight_row(r) = weight_row(0) + r)
-        const int blk = er + weight_row(0);
+        const int blk = er + w4::weight_row(kSwiGLU, t.nt, wave, 0, g.I, g.il);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a.woff[i] = (uint32_t)(blk * (K / 2) + ((lane >> 3) + 8 * i) * g.w_pitch + (lane & 7) * 16);
-        a.wsoff = (uint32_t)(blk * (K / kSB) + (lane >> 1) * g.s_pitch + (lane & 1) * (kKC / kSB / 2));
+        for (int i = 0; i < 4; ++i) a.woff[i] = w4::w_code_off(blk, K, lane, i, g.w_pitch);
+        a.wsoff = w4::w_scale_off(blk, K, kSB, lane, g.s_pitch);
 #pragma unroll
         for (int i = 0; i < NTB * 2 + 1; ++i) a.src[i] = 0;
         if (gather) {
 #pragma unroll
-            for (int i = 0; i < NTB * 2; ++i) a.src[i] = g.row_src[t.row_begin + min(sr + 16 * i, t.rows - 1)];
+            for (int i = 0; i < NTB * 2; ++i)
+                a.src[i] = g.row_src[t.row_begin + min(w4::act_row(tid, i), t.rows - 1)];
             a.src[NTB * 2] = g.row_src[t.row_begin + min(srow, t.rows - 1)];
         }
     };
-    auto finish_addr = [&](Addr &a, const W4Tile &t) {
+    auto finish_addr = [&](Addr &a, const Tile &t) {
         // token of slot s = t*k + j: s / k in double precision, exact for integers below 2^31
 #pragma unroll
         for (int i = 0; i < NTB * 2 + 1; ++i) asm volatile("" : "+v"(a.src[i])::"memory");
         const int rb = kLoop ? t.row_begin : 0;  // tile's first row within the descriptor (no gather)
 #pragma unroll
         for (int i = 0; i < NTB * 2; ++i) {
-            const int r = sr + 16 * i;
+            const int r = w4::act_row(tid, i);
             const int tok = (int)((double)a.src[i] / (double)g.gather_k);
-            a.aoff[i] = r >= t.rows ? 0x80000000u : (uint32_t)((gather ? tok : rb + r) * K + sg * 16);
+            a.aoff[i] = r >= t.rows ? w4::kDeadOff : w4::a_off(gather ? tok : rb + r, K, sg);
         }
         const int ts = (int)((double)a.src[NTB * 2] / (double)g.gather_k);
-        a.soff = srow >= t.rows ? 0x80000000u : (uint32_t)((gather ? ts : rb + srow) * kb_n * 4);
+        a.soff = srow >= t.rows ? w4::kDeadOff : w4::s_off(gather ? ts : rb + srow, K);
     };
 
     Rs rs;
@@ -284,11 +256,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     auto store_w = [&](const WChunk &w, int slot) {
         unsigned char *d = wl + slot * kWSlot;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)(d + ((lane >> 3) + 8 * i) * kWRow + (lane & 7) * 16) = w.c[i];
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
         if constexpr (kMX)
-            *(uint32_t *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 4) = w.s.x;
+            *(uint32_t *)(d + w4::lds_wscale(lane, true)) = w.s.x;
         else
-            *(u32x2 *)(d + kWScales + (lane >> 1) * 16 + (lane & 1) * 8) = w.s;
+            *(u32x2 *)(d + w4::lds_wscale(lane, false)) = w.s;
     };
     u32x4 ar[NTB * 2];
     u32x2 ars;
@@ -300,11 +272,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     auto store_a = [&](int buf) {
         unsigned char *dst = act + buf * kActBuf;
 #pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) {
-            const int r = sr + 16 * i;
-            *(u32x4 *)(dst + r * kKC + aslot(r, sg) * 16) = ar[i];
-        }
-        if (tid < NTB * 32) *(u32x2 *)(xsl + buf * (kBM * 2) + tid * 2) = ars;
+        for (int i = 0; i < NTB * 2; ++i) *(u32x4 *)(dst + w4::lds_act(w4::act_row(tid, i), sg)) = ar[i];
+        if (tid < NTB * 32) *(u32x2 *)(xsl + w4::lds_xs(buf, tid, 0)) = ars;
     };
 
     f32x16 acc[NTB];
@@ -313,14 +282,13 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
     auto compute = [&](int buf) {
         const unsigned char *ab = act + buf * kActBuf;
-        const float *xr = xsl + buf * (kBM * 2);
-        const unsigned char *wr = wl + buf * kWSlot + (lane & 31) * kWRow + half * 32;
-        const unsigned char *wsr = wl + buf * kWSlot + kWScales + (lane & 31) * 16 + half * 4;
+        const unsigned char *wr = wl + buf * kWSlot + w4::lds_wread(lane);
+        const unsigned char *wsr = wl + buf * kWSlot + w4::lds_wsread(lane);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             float xs[NTB];
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) xs[tb] = xr[(tb * 32 + (lane & 31)) * 2 + q];
+            for (int tb = 0; tb < NTB; ++tb) xs[tb] = xsl[w4::lds_xs(buf, tb * 32 + (lane & 31), q)];
             f32x16 part[NTB];
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
@@ -350,13 +318,12 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
                 // the weight run of lane half h (K 32h..32h+31 of the step) with activation bytes
                 // 0-15 of half 0 and of half 1, so a lane of half h holds granules h and h + 2 of
                 // the step's weight K (measured on the device with one wave and chosen operands)
-                const int gk_lo = kMX ? 8 * q + 2 * t + half : 8 * q + 4 * half + 2 * t;
-                const int gk_hi = kMX ? gk_lo + 4 : gk_lo + 1;
+                const int gk_lo = w4::gran_lo(kMX, q, t, half), gk_hi = w4::gran_hi(kMX, q, t, half);
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb) {
                     const int r = tb * 32 + (lane & 31);
-                    const u32x4 lo = *(const u32x4 *)(ab + r * kKC + aslot(r, gk_lo) * 16);
-                    const u32x4 hi = *(const u32x4 *)(ab + r * kKC + aslot(r, gk_hi) * 16);
+                    const u32x4 lo = *(const u32x4 *)(ab + w4::lds_act(r, gk_lo));
+                    const u32x4 hi = *(const u32x4 *)(ab + w4::lds_act(r, gk_hi));
                     const i32x8 xb = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                     // operand formats: weights fp4 e2m1 (4) or fp8 e4m3 (0), activations fp8 e4m3
@@ -373,14 +340,14 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
 
     // ---- epilogue of tile t.  xch: LDS the up waves hand their accumulators to the gate waves
     // through (an activation buffer no chunk still needs).
-    auto epilogue = [&](const W4Tile &t, float *xch) {
+    auto epilogue = [&](const Tile &t, float *xch) {
         const float gs = g.Wgs[t.e];
         if (kSwiGLU) {
             if (wave >= 2)
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) xch[(((wave - 2) * NTB + tb) * 16 + v) * 64 + lane] = acc[tb][v];
+                    for (int v = 0; v < 16; ++v) xch[w4::lds_xch(wave - 2, NTB, tb, v, lane)] = acc[tb][v];
             lds_barrier();
             if (wave < 2) {
 #pragma unroll
@@ -390,13 +357,13 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
                     float *hrow = g.Hout + (int64_t)(t.row_begin + tok) * g.I;
 #pragma unroll
                     for (int g4 = 0; g4 < 4; ++g4) {
-                        const int c0 = t.nt * (kBN / 2) + wave * 32 + g4 * 8 + half * 4;
+                        const int c0 = w4::h_col(t.nt, wave, g4, lane);
                         f32x4 o;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int v = g4 * 4 + q;
                             float gv = gs * acc[tb][v];
-                            float uv = gs * xch[((wave * NTB + tb) * 16 + v) * 64 + lane];
+                            float uv = gs * xch[w4::lds_xch(wave, NTB, tb, v, lane)];
                             if (g.clamp > 0.f) {
                                 gv = fminf(fmaxf(gv, -g.clamp), g.clamp);
                                 uv = fminf(fmaxf(uv, -g.clamp), g.clamp);
@@ -415,7 +382,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
                 uint16_t *yrow = g.Yout + (int64_t)(t.row_begin + tok) * g.ldy;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c0 = t.nt * kBN + wave * 32 + g4 * 8 + half * 4;
+                    const int c0 = w4::y_col(t.nt, wave, g4, lane);
                     u32x2 o;
                     o.x = pack_bf16x2(gs * acc[tb][g4 * 4 + 0], gs * acc[tb][g4 * 4 + 1]);
                     o.y = pack_bf16x2(gs * acc[tb][g4 * 4 + 2], gs * acc[tb][g4 * 4 + 3]);
@@ -425,8 +392,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
         }
     };
 
-    W4Tile cur = w4a8_tile_of(v0, nb_n, offsets, tiles, n_mt);
-    if (!cur.valid) return;  // before any barrier: the whole workgroup leaves
+    Tile cur = sc.first();
+    if (!cur.valid) return;  // uniform: the whole workgroup leaves (no barrier passed yet)
     rs = make_rs(cur);
     Addr A;
     start_addr(A, cur);
@@ -437,6 +404,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     // and the compiler's waits there stay exact.
     WChunk w[kNBuf];
     load_w(w[0], A, 0);
+    sc.before_act(cur);
     finish_addr(A, cur);
     load_a(A, 0);
 #pragma unroll
@@ -447,15 +415,14 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
     store_w(w[0], 0);
     lds_barrier();  // chunk 0 staged, scale table built
 
-    int v = v0;
     for (;;) {
         // the next tile's addressing (kLoop only; otherwise requests past the last chunk repeat
         // it).  Its row_src loads are issued now and consumed at step 2, when every older load in
-        // flight is one this tile needs by then anyway; its first request comes at step nc - 2.
-        W4Tile nxt{};
+        // flight is one this tile needs by then anyway; its first request comes at step nc - 3.
+        Tile nxt{};
         Addr B = A;
         if (kLoop) {
-            nxt = w4a8_tile_of(v + stride, nb_n, offsets, tiles, n_mt);
+            nxt = sc.next();
             if (nxt.valid) start_addr(B, nxt);
         }
         const bool go_on = kLoop && nxt.valid;
@@ -485,6 +452,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
                 store_w(w[(sidx + 1) % kNBuf], (c + 1) & 1);
                 store_a((c + 1) & 1);
                 const int ca = req(c + 2), cw = req(c + kNBuf - 1);
+                if (go_on && c + 2 == nc) sc.before_act(nxt);  // the next tile's first activation load
                 load_a(c + 2 < nc ? A : B, ca);
                 load_w(w[(sidx + kNBuf - 1) % kNBuf], c + kNBuf - 1 < nc ? A : B, cw);
                 lds_barrier();
@@ -493,11 +461,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, int v0, int stride, 
         // every wave has passed the last chunk's barrier; buffer nc % 2 holds the next tile's
         // first chunk (kLoop: nc is even), so the exchange uses the other one
         epilogue(cur, (float *)(act + ((nc + 1) & 1) * kActBuf));
+        sc.after_tile(cur);
         if (!go_on) break;
         lds_barrier();  // the exchange buffer is read before chunk 1 of the next tile is staged in it
         cur = nxt;
         A = B;
-        v += stride;
     }
 }
 
@@ -516,13 +484,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    const int n_mt = n_tiles[0];
-    const W4Tile t = w4a8_tile_of(blockIdx.x, g.N / kBN, offsets, tiles, n_mt);
+    StaticSched sc{(int)blockIdx.x, 0, g.N / kBN, n_tiles[0], offsets, tiles};
+    const Tile t = sc.first();
     if (!t.valid) return;
     if (t.rows > 32)
-        w4a8_tiles<kSwiGLU, kMX, 2, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 2, false>(g, sc, act, xsl, wlds, lut);
     else
-        w4a8_tiles<kSwiGLU, kMX, 1, false>(g, blockIdx.x, 0, offsets, tiles, n_mt, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false>(g, sc, act, xsl, wlds, lut);
 }
 
 // persistent (at most 32 rows per tile): workgroup b takes virtual blocks b, b + gridDim.x, ...
@@ -531,8 +499,423 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kern
     W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    w4a8_tiles<kSwiGLU, kMX, 1, true>(g, blockIdx.x, gridDim.x, offsets, tiles, n_tiles[0], act, xsl, wlds, lut);
+    StaticSched sc{(int)blockIdx.x, (int)gridDim.x, g.N / kBN, n_tiles[0], offsets, tiles};
+    w4a8_tiles<kSwiGLU, kMX, 1, true>(g, sc, act, xsl, wlds, lut);
 }
+
+// ---------------------------------------------------------------- single-launch small-token forward
+//
+// The whole W4A8 forward in one persistent launch for up to 256 tokens and 2048 slots, as the
+// FlashInfer pull request "[SM90] Add W4A8 MegaMoE support" runs dispatch, both FFN GEMMs, the
+// SwiGLU and the top-k reduction in one persistent kernel through 256 tokens per rank (its
+// opening description and Usage section).  The work and the arithmetic are those of the
+// step-by-step kernels (the same routing and table results, the same GEMM tile pipeline, the
+// same re-quantisation and combine arithmetic), so the output is bitwise the same.
+//
+//   workgroup 0   routes the tokens, builds offsets, row_src, slot_row and the tile list, zeroes
+//                 the counters below, then publishes a "go" word; the others wait for it
+//   items         GEMM1 tiles, then GEMM2 tiles.  Workgroup b starts with item b; later items
+//                 come from one counter (each claimed while the previous item runs)
+//   GEMM1 tile    writes its 64 h columns (fp32); of the two tiles that make one 128-column block
+//                 of an m-tile, the second to finish re-quantises the block to fp8 and counts it
+//                 in the m-tile's ready counter
+//   GEMM2 tile    streams its first weight chunks, then waits until its m-tile has all I/128
+//                 blocks (no more waiting once every block of every m-tile is done)
+//   combine       once every workgroup is past its GEMM tiles, workgroup b combines tokens
+//                 b, b + grid, ...; the last workgroup out resets the go word
+// No GEMM item waits on an item claimed after it (a GEMM2 tile waits only on GEMM1 tiles, all
+// handed out earlier to running workgroups, which never wait), so the GEMM phase completes on
+// whatever share of the device the grid gets; every wait is bounded, and a wait that gives up
+// sets the error word.  Hand-offs between workgroups: every wave waits for its stores, a
+// barrier, one agent-scope release fence (a write-back of the XCD's L2) and a counter update by
+// one thread; the consumer polls the counter and takes an agent-scope acquire fence (an
+// invalidation of its L1 and L2) before the workgroup reads.
+
+constexpr uint64_t kGoWord = 0x7ff47ff47ff47ff4ull;  // a pattern the workspace holds nowhere else
+constexpr int kSpinLimit = 1 << 21;                   // polls (each after a short sleep) before giving up
+
+struct FusedArgs {
+    const float *logits;
+    const uint8_t *slot_drop;
+    int T, E, k;
+    int32_t *topk_idx, *offsets, *row_src, *slot_row, *tiles, *n_tiles;
+    float *topk_w;
+    FusedSync *sync;
+    uint32_t *rq_cnt, *mt_ready;
+    W4Args g1, g2;      // GEMM1 (x through row_src -> h32), GEMM2 (h8 -> y)
+    float *h32;
+    uint8_t *h8;
+    float *hs;
+    uint16_t *y, *out;
+    int H, I;
+};
+
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ uint32_t atomic_add(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_get(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every store this wave issued has completed (reached the XCD's L2)
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// thread 0: poll until *p >= want (bounded), then the acquire fence for the workgroup (it
+// invalidates the caches its waves share); false if the wait gave up
+__device__ __forceinline__ bool poll_at_least(const FusedArgs &f, const uint32_t *p, uint32_t want) {
+    int n = 0;
+    while (atomic_get(p) < want) {
+        if (++n > kSpinLimit) {
+            __hip_atomic_fetch_or(&f.sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(16);
+    }
+    fence_acquire();
+    return true;
+}
+
+// The stores of every wave reach the XCD's L2, then thread 0's release fence writes the L2's
+// dirty lines back (one write-back for the whole workgroup) and it adds one to *p.  Returns the
+// counter's previous value to every thread (through word, a workgroup-shared int, which every
+// thread has read before the call returns); the thread that reads acquire_at takes the acquire
+// fence for the workgroup.
+__device__ __forceinline__ uint32_t publish_and_count(uint32_t *p, int *word, uint32_t acquire_at = ~0u,
+                                                      uint32_t *also = nullptr) {
+    stores_done();
+    lds_barrier();
+    if (threadIdx.x == 0) {
+        fence_release();
+        const uint32_t old = atomic_add(p, 1u);
+        if (also) atomic_add(also, 1u);
+        if (old == acquire_at) fence_acquire();
+        *word = (int)old;
+    }
+    lds_barrier();
+    const uint32_t v = (uint32_t)*word;
+    lds_barrier();
+    return v;
+}
+
+// Routing of token t by one thread: the same selection (the largest key, the lower id on
+// ties) and the same fp32 arithmetic in the same order as route_row, so the same ids and
+// weights.  NE >= E keys in registers; exs: per-slot scratch for the unnormalised weights.
+template <int NE>
+__device__ __forceinline__ void route_thread(const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop,
+                                             int t, int E, int k, int32_t *__restrict__ topk_idx,
+                                             float *__restrict__ topk_w, int32_t *ids, float *exs) {
+    using namespace route_detail;
+    const float *l = logits + (int64_t)t * E;
+    uint32_t key[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) key[e] = e < E ? logit_key(l[e]) : 0u;
+    float lmax = 0.0f, z = 0.0f;
+    for (int j = 0; j < k; ++j) {
+        uint32_t bk = 0u;
+        int be = 0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (key[e] > bk) {
+                bk = key[e];
+                be = e;
+            }
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+            if (e == be) key[e] = 0u;
+        const float lj = key_logit(bk);
+        if (j == 0) lmax = lj;
+        const float ex = expf(lj - lmax);
+        z += ex;
+        ids[j] = be;
+        exs[j] = ex;
+    }
+    for (int j = 0; j < k; ++j) {
+        const int64_t s = (int64_t)t * k + j;
+        const bool dropped = slot_drop != nullptr && slot_drop[s] != 0;
+        const int id = dropped ? -1 : ids[j];
+        topk_idx[s] = id;
+        topk_w[s] = exs[j] / z;
+        ids[j] = id;
+    }
+}
+
+// Routing, tables and tile list of up to 2048 slots in workgroup 0 (256 threads): the same
+// results as route_topk + the table kernels.  LDS: sid [2048] ids, exs [2048] scratch, cnt
+// [4][256], off [257], run [256], ws8 [8].
+__device__ void fused_front_end(const FusedArgs &f, int32_t *sid, float *exs, int (*cnt)[256], int *off, int *run,
+                                int *ws8, int *n_mt_out) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int T = f.T, E = f.E, k = f.k, S = T * k;
+    auto valid = [E](int32_t x) { return ((unsigned)x < (unsigned)E) ? x : -1; };
+    if (T > 16 && E <= 64) {
+        // one thread per token (one pass for up to 256 tokens)
+        for (int t = tid; t < T; t += kThreads) {
+            if (E <= 32)
+                route_thread<32>(f.logits, f.slot_drop, t, E, k, f.topk_idx, f.topk_w, sid + t * k, exs + t * k);
+            else
+                route_thread<64>(f.logits, f.slot_drop, t, E, k, f.topk_idx, f.topk_w, sid + t * k, exs + t * k);
+        }
+    } else {
+        // one 16-lane row per token, four tokens per wave, 16 per pass
+        for (int t0 = w * 4; t0 < T; t0 += 16) {
+            const int t = t0 + (lane >> 4);
+            route_token16(f.logits, f.slot_drop, t < T ? t : T - 1, t < T, E, k, lane & 15, f.topk_idx, f.topk_w,
+                          sid + t * k);
+        }
+    }
+    run[tid] = 0;
+    __syncthreads();
+    for (int s = tid; s < S; s += kThreads) {
+        const int x = valid(sid[s]);
+        if (x >= 0) atomicAdd(&run[x], 1);
+    }
+    __syncthreads();
+    const int tot = tid < E ? run[tid] : 0;
+    int incl = tot, unused = 0, R, unused_total;
+    block_incl_sum256(incl, unused, ws8, &R, &unused_total);
+    if (tid < E) {
+        off[tid] = incl - tot;
+        f.offsets[tid] = incl - tot;
+        run[tid] = 0;  // rows of expert tid placed by earlier passes
+    }
+    if (tid == 0) {
+        off[E] = R;
+        f.offsets[E] = R;
+    }
+    // stable rank, 256 slots per pass: a slot's rank among equal ids of lower lanes of its wave
+    // from 9 ballots, its wave's base from the lower waves' counts and the earlier passes
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int p0 = 0; p0 < S; p0 += kThreads) {
+        const int s = p0 + tid;
+        const int x = s < S ? valid(sid[s]) : -1;
+        const unsigned key = (unsigned)(x + 1);
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            const bool bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & lt);
+        for (int i = tid; i < 4 * 256; i += kThreads) (&cnt[0][0])[i] = 0;
+        __syncthreads();
+        if (x >= 0 && rank == 0) cnt[w][x] = __popcll(peers);
+        __syncthreads();
+        if (tid < E) {
+            int b = run[tid];
+            for (int ww = 0; ww < 4; ++ww) {
+                const int v = cnt[ww][tid];
+                cnt[ww][tid] = b;
+                b += v;
+            }
+            run[tid] = b;
+        }
+        __syncthreads();
+        if (s < S) {
+            const int r = x >= 0 ? off[x] + cnt[w][x] + rank : -1;
+            f.slot_row[s] = r;
+            if (r >= 0) f.row_src[r] = s;
+        }
+        __syncthreads();
+    }
+    *n_mt_out = build_tile_list(off, E, kBM, 1, f.tiles, f.n_tiles, ws8);
+}
+
+// Items of the fused forward: [0, n1) GEMM1 tiles, [n1, n1 + n2) GEMM2 tiles.
+struct FusedState {
+    int pending;     // thread 0: the item claimed ahead
+    int item;        // the current item (uniform)
+    bool have;       // item is claimed and not yet started
+    int ready_mt;    // GEMM2: the last m-tile seen complete
+    bool all_ready;  // GEMM2: every block of every m-tile seen complete
+};
+
+template <bool kG1>
+struct FusedSched {
+    const FusedArgs &f;
+    FusedState &st;
+    int *word;  // workgroup-shared int
+    int n_mt, n1, n2;
+    // the item claimed ahead becomes current (to every thread); thread 0 claims the next one
+    __device__ int take() {
+        if (threadIdx.x == 0) {
+            *word = st.pending;
+            st.pending = (int)atomic_add(&f.sync->next_item, 1u);
+        }
+        lds_barrier();
+        const int it = *word;
+        lds_barrier();  // every thread has read the word before it can be written again
+        return it;
+    }
+    __device__ Tile decode(int it) {
+        if (kG1 ? it >= n1 : (it < n1 || it >= n1 + n2)) return Tile{};
+        return kG1 ? w4::tile_of(it, 2 * f.I / kBN, f.offsets, f.tiles, n_mt)
+                   : w4::tile_of(it - n1, f.H / kBN, f.offsets, f.tiles, n_mt);
+    }
+    __device__ Tile first() {
+        if (!st.have) {
+            // workgroup b starts with item b; the counter starts at the grid size
+            st.item = (int)blockIdx.x;
+            if (threadIdx.x == 0) st.pending = (int)atomic_add(&f.sync->next_item, 1u);
+        }
+        st.have = false;
+        const Tile t = decode(st.item);
+        if (!t.valid) st.have = true;  // handed to the next phase
+        return t;
+    }
+    __device__ Tile next() {
+        st.item = take();
+        const Tile t = decode(st.item);
+        if (!t.valid) st.have = true;
+        return t;
+    }
+    __device__ void before_act(const Tile &t) {
+        if (kG1 || st.all_ready || t.mt == st.ready_mt) return;
+        if (threadIdx.x == 0) {
+            const uint32_t n_cb = f.I / 128;
+            const bool ok = poll_at_least(f, f.mt_ready + t.mt * kSyncLine, n_cb);
+            *word = ok && atomic_get(&f.sync->rq_total) == (uint32_t)n_mt * n_cb;
+        }
+        lds_barrier();
+        st.all_ready = *word != 0;
+        lds_barrier();
+        st.ready_mt = t.mt;
+    }
+    __device__ void after_tile(const Tile &t) {
+        if (!kG1) return;  // GEMM2 outputs are published once, after the workgroup's last tile
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        // two GEMM1 tiles (n-tiles 2 cb, 2 cb + 1) make the 128-column block cb of h
+        const int cb = t.nt >> 1, n_cb = f.I / 128;
+        if (publish_and_count(f.rq_cnt + (t.mt * n_cb + cb) * kSyncLine, word, 1u) != 1) return;
+        // the same arithmetic as requant_fp8_kernel, one wave per (row, 128 columns): rows
+        // wave, wave + 4, ... of the tile, all loads first
+        f32x2 v[kBM / 4];
+#pragma unroll
+        for (int i = 0; i < kBM / 4; ++i) {
+            const int r = wave + 4 * i;
+            if (r < t.rows) v[i] = *(const f32x2 *)(f.h32 + (int64_t)(t.row_begin + r) * f.I + cb * 128 + 2 * lane);
+        }
+#pragma unroll
+        for (int i = 0; i < kBM / 4; ++i) {
+            const int r = wave + 4 * i;
+            if (r >= t.rows) break;
+            const int64_t row = t.row_begin + r;
+            float m = fmaxf(fabsf(v[i].x), fabsf(v[i].y));
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            float s = m / 448.0f;
+            if (s == 0.0f) s = 1.0f;
+            const uint32_t q = to_fp8x2<false>(v[i].x / s, v[i].y / s, 0u);
+            *(uint16_t *)(f.h8 + row * f.I + cb * 128 + 2 * lane) = (uint16_t)(q & 0xffffu);
+            if (lane == 0) f.hs[row * n_cb + cb] = s;
+        }
+        publish_and_count(f.mt_ready + t.mt * kSyncLine, word, ~0u, &f.sync->rq_total);
+    }
+};
+
+// out[tok] for tokens blockIdx.x, blockIdx.x + gridDim.x, ...: the arithmetic of combine_kernel
+// (an fp32 chain over the slots in ascending j, one rounding); the token's rows and weights go
+// to LDS first, then every thread loads its chunk of up to 8 slot rows at once.
+__device__ void fused_combine(const FusedArgs &f, int *rows_s, float *w_s) {
+    const int tid = threadIdx.x, k = f.k, nch = f.H / 8;
+    for (int tok = blockIdx.x; tok < f.T; tok += gridDim.x) {
+        for (int j = tid; j < k; j += kThreads) {
+            rows_s[j] = f.slot_row[(int64_t)tok * k + j];
+            w_s[j] = f.topk_w[(int64_t)tok * k + j];
+        }
+        __syncthreads();
+        for (int c = tid; c < nch; c += kThreads) {
+            float acc[8] = {};
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                uint4 v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int r = j0 + q < k ? rows_s[j0 + q] : -1;
+                    v[q] = r >= 0 ? *(const uint4 *)(f.y + (int64_t)r * f.H + c * 8) : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (j0 + q < k && rows_s[j0 + q] >= 0) combine_fma8(acc, w_s[j0 + q], v[q]);
+            }
+            *(uint4 *)(f.out + (int64_t)tok * f.H + c * 8) = combine_pack8(acc);
+        }
+        __syncthreads();
+    }
+}
+
+template <bool kMX, int NTB>
+__global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedArgs f) {
+    TPG_W4A8_LDS
+    __shared__ int word, n_mt_s;
+    const int tid = threadIdx.x;
+    FusedSync *sy = f.sync;
+    if (blockIdx.x == 0) {
+        // front end in the activation buffers (idle until the first GEMM tile)
+        int32_t *sid = (int32_t *)act;                        // 2048 slots
+        float *exs = (float *)(act + 8192);                    // 2048 slots
+        int(*cnt)[256] = (int(*)[256])(act + 16384);          // [4][256]
+        int *off = (int *)(act + 20480), *run = off + 260, *ws8 = run + 256;
+        fused_front_end(f, sid, exs, cnt, off, run, ws8, &n_mt_s);
+        const int n_mt = n_mt_s, n_cb = f.I / 128;
+        for (int i = tid; i < n_mt * n_cb; i += kThreads) f.rq_cnt[i * kSyncLine] = 0;
+        for (int i = tid; i < n_mt; i += kThreads) f.mt_ready[i * kSyncLine] = 0;
+        if (tid == 0) {
+            sy->next_item = gridDim.x;  // workgroup b starts with item b
+            sy->done = 0;
+            sy->err = 0;
+            sy->rq_total = 0;
+            sy->gemm_done = 0;
+        }
+        stores_done();
+        lds_barrier();
+        if (tid == 0) {
+            fence_release();
+            __hip_atomic_store(&sy->go, kGoWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        if (tid == 0) {
+            int n = 0;
+            bool ok = true;
+            while (__hip_atomic_load(&sy->go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kGoWord) {
+                if (++n > kSpinLimit) {
+                    ok = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(16);
+            }
+            fence_acquire();
+            word = ok;
+            n_mt_s = f.n_tiles[0];
+        }
+        lds_barrier();
+        if (!word) {  // workgroup 0 never published (it cannot have run): do nothing, flag it
+            if (tid == 0) __hip_atomic_fetch_or(&sy->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+    }
+    const int n_mt = n_mt_s;
+    FusedState st{0, 0, false, -1, false};
+    const int n1 = n_mt * (2 * f.I / kBN), n2 = n_mt * (f.H / kBN);
+    {
+        FusedSched<true> sc{f, st, &word, n_mt, n1, n2};
+        w4a8_tiles<true, kMX, NTB, true>(f.g1, sc, act, xsl, wlds, lut);
+    }
+    {
+        FusedSched<false> sc{f, st, &word, n_mt, n1, n2};
+        w4a8_tiles<false, kMX, NTB, true>(f.g2, sc, act, xsl, wlds, lut);
+    }
+    // every workgroup's GEMM2 rows are written before any combine reads them
+    publish_and_count(&sy->gemm_done, &word);
+    if (tid == 0) poll_at_least(f, &sy->gemm_done, gridDim.x);
+    lds_barrier();
+    fused_combine(f, (int *)act, (float *)(act + 4096));
+    // the last workgroup out resets the go word for the next forward on this workspace
+    lds_barrier();
+    if (tid == 0 && atomic_add(&sy->done, 1u) == gridDim.x - 1)
+        __hip_atomic_store(&sy->go, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 #undef TPG_W4A8_LDS
 
 // h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows: one wave per
@@ -684,6 +1067,105 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     g2.ldy = H;
     set_layout(g2, I, mx, w.w4_layout);
     launch_w4a8_gemm<false>(mx, l2, g2, offsets, tiles, n_tiles, s);
+    return hipGetLastError();
+}
+
+bool forward_small_w4a8_fits(const moe_problem &p) {
+    const int64_t S = n_slots(p), lim = 0x7FFFFFFF;
+    return (p.prec == MOE_PREC_W4A8 || p.prec == MOE_PREC_W4A8_MX) && p.T <= 256 && S <= 2048 &&
+           p.H % (kKC * kNBuf) == 0 && p.I % (kKC * kNBuf) == 0 && (int64_t)p.E * 2 * p.I * (p.H / 2) <= lim &&
+           (int64_t)p.E * p.H * (p.I / 2) <= lim && (int64_t)p.T * p.H <= lim && S * p.I <= lim;
+}
+
+hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_drop, const uint8_t *x,
+                                     const float *x_scale, const moe_weights &w, const moe_problem &p,
+                                     int64_t max_tiles, FusedSync *sync, int32_t *topk_idx, float *topk_w,
+                                     int32_t *offsets, int32_t *row_src, int32_t *slot_row, int32_t *tiles,
+                                     int32_t *n_tiles, float *h32, uint8_t *h8, float *hs, uint16_t *y,
+                                     uint16_t *out, hipStream_t s) {
+    if (!forward_small_w4a8_fits(p)) return hipErrorInvalidValue;
+    const bool mx = p.prec == MOE_PREC_W4A8_MX;
+    const int S = (int)n_slots(p);
+    FusedArgs f{};
+    f.logits = logits;
+    f.slot_drop = slot_drop;
+    f.T = p.T;
+    f.E = p.E;
+    f.k = p.k;
+    f.topk_idx = topk_idx;
+    f.offsets = offsets;
+    f.row_src = row_src;
+    f.slot_row = slot_row;
+    f.tiles = tiles;
+    f.n_tiles = n_tiles;
+    f.topk_w = topk_w;
+    f.sync = sync;
+    f.rq_cnt = (uint32_t *)(sync + 1);  // counters kSyncLine words apart
+    f.mt_ready = f.rq_cnt + max_tiles * (p.I / 128) * kSyncLine;
+    f.h32 = h32;
+    f.h8 = h8;
+    f.hs = hs;
+    f.y = y;
+    f.out = out;
+    f.H = p.H;
+    f.I = p.I;
+    W4Args &g1 = f.g1;
+    g1.A8 = x;
+    g1.As = x_scale;
+    g1.row_src = row_src;
+    g1.gather_k = p.k;
+    g1.a_rows = p.T;
+    g1.Wq = (const uint8_t *)w.w1;
+    g1.Wbs = (const uint8_t *)w.w1_bscale;
+    g1.Wgs = w.w1_gscale;
+    g1.K = p.H;
+    g1.N = 2 * p.I;
+    g1.I = p.I;
+    g1.il = p.glu_interleave;
+    g1.E = p.E;
+    g1.clamp = p.swiglu_clamp;
+    g1.Hout = h32;
+    set_layout(g1, p.H, mx, w.w4_layout);
+    W4Args &g2 = f.g2;
+    g2.A8 = h8;
+    g2.As = hs;
+    g2.gather_k = 1;
+    g2.a_rows = S;
+    g2.Wq = (const uint8_t *)w.w2;
+    g2.Wbs = (const uint8_t *)w.w2_bscale;
+    g2.Wgs = w.w2_gscale;
+    g2.K = p.I;
+    g2.N = p.H;
+    g2.I = p.I;
+    g2.E = p.E;
+    g2.Yout = y;
+    g2.ldy = p.H;
+    set_layout(g2, p.I, mx, w.w4_layout);
+    // every workgroup resident at once (two per CU: the kernel's LDS and register budget); the
+    // kernel does not depend on it, but idle waits are shortest then
+    int dev = 0, n_cu = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const bool one_block = p.T <= 32;  // every m-tile fits one 32-row token block
+    const void *fn = mx ? (one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
+                                     : (const void *)forward_small_w4a8_kernel<true, 2>)
+                        : (one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
+                                     : (const void *)forward_small_w4a8_kernel<false, 2>);
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
+    if (err != hipSuccess) return err;
+    const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
+    if (mx) {
+        if (one_block)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, f);
+        else
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 2>), dim3(grid), dim3(kThreads), 0, s, f);
+    } else {
+        if (one_block)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, f);
+        else
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, f);
+    }
     return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ int check_problem(const moe_problem *p) {
     if (p->prec != MOE_PREC_BF16 && (p->H % 256 != 0 || p->I % 256 != 0)) return MOE_ERR_SHAPE;
     if (p->glu_interleave != 0 && p->glu_interleave != 32) return MOE_ERR_UNSUPPORTED;
     if (!(p->swiglu_clamp >= 0.0f) || p->swiglu_clamp > 3.0e38f) return MOE_ERR_UNSUPPORTED;  // also rejects NaN
+    if (p->flags != 0 && p->flags != MOE_FLAG_SINGLE_LAUNCH) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -61,6 +62,10 @@ WsLayout ws_layout(const moe_problem &p) {
     const size_t S = (size_t)n_slots(p), E = (size_t)p.E;
     const size_t act = is_w4a8(&p) ? 1 : 2;  // bytes per activation element
     size_t o = 0;
+    L.fsync = o;
+    if (is_w4a8(&p))
+        o = align256(o + sizeof(FusedSync) +
+                     4 * kSyncLine * ((size_t)max_m_tiles(p) * (p.I / 128) + (size_t)max_m_tiles(p)));
     L.chunk_counts = o;
     o = align256(o + (size_t)n_chunks(p) * E * 4);
     L.permute_end = o;
@@ -165,6 +170,22 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         return ev ? hip_status(hipEventRecord((hipEvent_t)ev[i], s)) : MOE_OK;
     };
     const bool w4 = is_w4a8(p);
+    if (p->flags & MOE_FLAG_SINGLE_LAUNCH) {
+        if (!w4 || !forward_small_w4a8_fits(*p)) return MOE_ERR_UNSUPPORTED;
+        // the whole forward in one launch: its stages have no marks of their own (0-4 before it,
+        // 5-7 after it)
+        for (int i = 0; i < 5; ++i)
+            if ((st = mark(i))) return st;
+        char *fs = b + L.fsync;
+        if ((st = hip_status(launch_forward_small_w4a8(
+                 logits, slot_drop, (const uint8_t *)x, x_scale, *w, *p, max_tiles, (FusedSync *)fs, topk_idx,
+                 topk_w, offsets, row_src, slot_row, tiles, n_tiles, (float *)(b + L.h32), (uint8_t *)(b + L.h),
+                 (float *)(b + L.h_scale), (uint16_t *)y_perm, (uint16_t *)out, s))))
+            return st;
+        for (int i = 5; i < 8; ++i)
+            if ((st = mark(i))) return st;
+        return MOE_OK;
+    }
     // up to kChunk slots and 256 tokens (one workgroup routes 64 tokens at a time, four per wave):
     // routing, tables and tile list in one launch (stage marks 1, 2 and the tile-list stage then
     // take no time of their own).  W4A8 layer at T = 64, timed with stage events: 222.6 -> 213.5

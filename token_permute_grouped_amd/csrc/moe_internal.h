@@ -16,7 +16,27 @@ constexpr int kWave = 64;
 // One layout for every entry point, computed on the host from the problem only
 // (never from the routing), so a workspace allocated once serves every call of that
 // shape.  Offsets are 256-byte aligned.
+// Hand-off words of the single-launch small-token forward (the first bytes of a W4A8 workspace),
+// each in a 128-byte line of its own, followed by its counters, one per line too:
+// rq_cnt [max_tiles][I/128], mt_ready [max_tiles].
+constexpr int kSyncLine = 32;  // uint32 per 128-byte line
+struct FusedSync {
+    uint64_t go;  // set while a forward runs (after its tables are built), 0 after
+    uint32_t pad0[kSyncLine - 2];
+    uint32_t next_item;  // item claims
+    uint32_t pad1[kSyncLine - 1];
+    uint32_t done;  // workgroups finished
+    uint32_t pad2[kSyncLine - 1];
+    uint32_t err;  // nonzero: a bounded wait gave up
+    uint32_t pad3[kSyncLine - 1];
+    uint32_t rq_total;  // 128-column blocks of h re-quantised
+    uint32_t pad4[kSyncLine - 1];
+    uint32_t gemm_done;  // workgroups past their last GEMM tile
+    uint32_t pad5[kSyncLine - 1];
+};
+
 struct WsLayout {
+    size_t fsync;         // W4A8: FusedSync + counters (always at offset 0)
     size_t chunk_counts;  // int32 [n_chunks][E]   permutation: per-chunk histograms
     size_t tiles;         // int32 [2 * max_tiles]  grouped GEMMs: (expert, first row) per m-tile
     size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count, full-tile count
@@ -100,6 +120,17 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,
                           uint16_t *out, hipStream_t s);
 
+// The whole W4A8 forward in one launch (up to 256 tokens and 2048 slots, H and I multiples of
+// 1024, every byte offset below 2^31): routing, tables, both GEMMs with the SwiGLU and the
+// re-quantisation, and the combine.  Buffers are the forward's workspace regions.
+bool forward_small_w4a8_fits(const moe_problem &p);
+hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_drop, const uint8_t *x,
+                                     const float *x_scale, const moe_weights &w, const moe_problem &p,
+                                     int64_t max_tiles, FusedSync *sync, int32_t *topk_idx, float *topk_w,
+                                     int32_t *offsets, int32_t *row_src, int32_t *slot_row, int32_t *tiles,
+                                     int32_t *n_tiles, float *h32, uint8_t *h8, float *hs, uint16_t *y,
+                                     uint16_t *out, hipStream_t s);
+
 hipError_t launch_w4a8_dequant_table(uint8_t *out8, hipStream_t s);
 
 hipError_t launch_tile_weights(const uint8_t *codes, const uint8_t *bscale, uint8_t *codes_tiled,
@@ -114,6 +145,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// One step of the combine's fp32 chain for 8 consecutive columns: acc[i] = fma(w, y[i], acc[i])
+// with y eight bf16 values (used by the combine kernel and by the single-launch forward, so both
+// give the same bits).
+__device__ __forceinline__ void combine_fma8(float *acc, float w, const uint4 &v) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = fmaf(w, __uint_as_float(u[q] << 16), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(w, __uint_as_float(u[q] & 0xffff0000u), acc[2 * q + 1]);
+    }
+}
+
+// eight fp32 values -> eight bf16 (round to nearest even) in 16 bytes
+__device__ __forceinline__ uint4 combine_pack8(const float *a) {
+    uint4 o;
+    o.x = pack_bf16x2(a[0], a[1]);
+    o.y = pack_bf16x2(a[2], a[3]);
+    o.z = pack_bf16x2(a[4], a[5]);
+    o.w = pack_bf16x2(a[6], a[7]);
+    return o;
 }
 
 // Streamed-out rows (written once, not read again by the kernel that writes them) are stored

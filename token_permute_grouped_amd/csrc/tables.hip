@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "route_token.h"
+#include "tile_list.h"
 
 namespace tpg {
 
@@ -48,41 +49,6 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t *__restri
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)blockIdx.x * E + e] = h[e];
-}
-
-// GEMM tile list from offsets (LDS or global, E+1 entries): tiles[2i] = expert, tiles[2i+1] =
-// first row of the tile within the expert (tiles of bm rows); n_tiles[0] = count, n_tiles[1] =
-// tiles before the partial section.  Default order: full tiles first (expert by expert), then each
-// expert's partial last tile.  by_expert: every expert's tiles together in row order (n_tiles[1] =
-// count).  Thread e < E handles expert e; every thread of the workgroup must call it (it holds a
-// barrier); ws is 8 ints of LDS (see block_incl_sum256).
-__device__ void build_tile_list(const int32_t *off, int E, int bm, int by_expert, int32_t *__restrict__ tiles,
-                                int32_t *__restrict__ n_tiles, int *ws) {
-    const int e = threadIdx.x;
-    int full = 0, part = 0;
-    if (e < E) {
-        const int cnt = off[e + 1] - off[e];
-        full = by_expert ? (cnt + bm - 1) / bm : cnt / bm;
-        part = !by_expert && (cnt % bm) ? 1 : 0;
-    }
-    int sf = full, sp = part, total_full, total_part;
-    block_incl_sum256(sf, sp, ws, &total_full, &total_part);
-    if (e < E) {
-        const int f0 = sf - full;
-        for (int m = 0; m < full; ++m) {
-            tiles[2 * (f0 + m)] = e;
-            tiles[2 * (f0 + m) + 1] = m * bm;
-        }
-        if (part) {
-            const int pos = total_full + sp - 1;
-            tiles[2 * pos] = e;
-            tiles[2 * pos + 1] = full * bm;
-        }
-    }
-    if (e == 0) {
-        n_tiles[0] = total_full + total_part;
-        n_tiles[1] = total_full;
-    }
 }
 
 constexpr int kScanThreads = 1024;
