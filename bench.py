@@ -85,19 +85,23 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_file, kernel, workload, seed, launches_bytes_key="bytes_per_launch"):
-    """HBM bytes per launch from the committed counter summary, if it was taken on the current source
-    and on this workload and seed (None otherwise)."""
+def measured_traffic(roles, workload, T, seed):
+    """HBM bytes per forward of the kernels in roles (each launched once per forward), summed from
+    the committed counter summary, if every record was taken on the current source of its kernel
+    and on this workload, token count and seed (None otherwise)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        rec = json.load(fh).get(kernel)
-    if not rec or rec.get("source_sha") != source_hash([kernel_file]):
-        return None
-    if rec.get("workload") != workload or rec.get("seed") != seed:
-        return None
-    return rec.get(launches_bytes_key)
+        recs = json.load(fh)
+    total = 0
+    for role in roles:
+        rec = next((r for r in recs if r.get("role") == role and r.get("workload") == workload
+                    and r.get("T") == T and r.get("seed") == seed), None)
+        if rec is None or rec.get("source_sha") != source_hash(rec["source_files"]):
+            return None
+        total += rec["bytes_per_launch"]
+    return total
 
 
 def cpu_model() -> str:
@@ -455,8 +459,7 @@ def measure(cfg, args, detail, inp=None):
             "kernel": "grouped_gemm_bf16_kernel<true> (GEMM1 + SwiGLU)",
             "bound": "mfma", "achieved": round(g1, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(g1 / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic("token_permute_grouped_amd/csrc/gemm_bf16.hip", "gemm1_swiglu",
-                                        cfg.name if args.tokens is None else None, args.seed),
+            "traffic": measured_traffic(["gemm1_swiglu"], cfg.name, T, args.seed),
             "algorithmic_per_launch": f"4*R*H*I = {gemm1_flops:.4g} flop (R={R} rows)",
         }
     else:
@@ -476,7 +479,10 @@ def measure(cfg, args, detail, inp=None):
             "kernel": "grouped W4A8 FFN (grouped_gemm_w4a8_kernel<true>, requant_fp8_kernel, "
                       "grouped_gemm_w4a8_kernel<false>)",
             "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(a / PEAK_HBM_GBS, 4),
+            # the counters were taken on the default launches (not the single-launch kernel)
+            "traffic": (None if getattr(args, "single_launch", False) else
+                        measured_traffic(["gemm1_swiglu", "requant", "gemm2"], cfg.name, T, args.seed)),
             "algorithmic_per_launch": f"{ffn_bytes} bytes ({n_exp} experts' packed weights {w_bytes} B "
                                       f"+ activations {act_bytes} B)",
         }
