@@ -48,6 +48,19 @@ def whole_tiles(offsets: np.ndarray, bm: int) -> np.ndarray:
     return np.concatenate(rows).astype(np.int64)
 
 
+def merged_tile_rows(offsets: np.ndarray, bm: int) -> np.ndarray:
+    """every row of the last m-tile of the largest expert whose rows end in a remainder of 1..bm/2
+    after at least one full tile (the W4A8 tile list merges that remainder into the tile before it,
+    a tile of up to 1.5 bm rows); empty if no expert has one"""
+    counts = np.diff(offsets)
+    ok = (counts > bm) & (counts % bm >= 1) & (counts % bm <= bm // 2)
+    if not ok.any():
+        return np.zeros(0, dtype=np.int64)
+    e = int(np.argmax(np.where(ok, counts, -1)))
+    start = int(offsets[e]) + (int(counts[e]) // bm - 1) * bm
+    return np.arange(start, int(offsets[e + 1]), dtype=np.int64)
+
+
 def assert_all_rows_written(dev_bits, n_rows: int, ref_absmax: float, what: str):
     """no element of the first n_rows rows still holds the 0xFFFF fill (a bf16 NaN), and the largest
     magnitude stays within 4x of the sampled reference's (a skipped GEMM1 tile would leave the

@@ -6,7 +6,9 @@
 // host); the front ends' few index expressions are replayed loop by loop.  For every tile, chunk,
 // wave and lane it checks that each buffer load lies inside its descriptor (or starts beyond it,
 // so that it reads zero), that no 32-bit offset wraps, that every LDS access stays inside its
-// array and every global store inside its buffer.  Problem sizes: the W4A8 decode layer at every
+// array and every global store inside its buffer, and that the tiles of each list cover every
+// row once (the multi-launch GEMMs' list, whose last tiles take up to 96 rows and three token
+// blocks, and the single-launch forward's 64-row one).  Problem sizes: the W4A8 decode layer at every
 // token count of its sweep, the small test cases, and random ones up to E = 256, k = 32 and 2048
 // slots, with uniform, skewed, one-expert and dropped-slot routings.  Exit status 0: all in range.
 #include <cstdio>
@@ -59,8 +61,9 @@ struct Problem {
 // expert-major rows: counts per expert (dropped slots have none), offsets, row_src
 struct Routing {
     std::vector<int> idx;  // [T*k]: expert or -1
-    std::vector<int> offsets, row_src, slot_row, tiles;
-    int n_mt = 0;
+    std::vector<int> offsets, row_src, slot_row;
+    std::vector<int> tiles[2];  // tile lists: [0] 64-row m-tiles, [1] with merged last tiles
+    int n_mt[2] = {0, 0};
 };
 
 static Routing make_routing(const Problem &p, int mode, Rng &rng) {
@@ -101,45 +104,70 @@ static Routing make_routing(const Problem &p, int mode, Rng &rng) {
             r.row_src[row] = s;
             r.slot_row[s] = row;
         }
-    // the tile list the forward builds for the W4A8 GEMMs: each expert's 64-row m-tiles together
-    for (int e = 0; e < p.E; ++e) {
-        const int cnt = r.offsets[e + 1] - r.offsets[e];
-        for (int m = 0; m * kBM < cnt; ++m) {
-            r.tiles.push_back(e);
-            r.tiles.push_back(m * kBM);
+    // the tile lists of the W4A8 GEMMs: each expert's 64-row m-tiles together ([0], the
+    // single-launch forward's), and the same with a last remainder of 1..32 rows (after at least
+    // one full tile) left to the tile before it ([1], the multi-launch GEMMs')
+    for (int merge = 0; merge < 2; ++merge) {
+        for (int e = 0; e < p.E; ++e) {
+            const int cnt = r.offsets[e + 1] - r.offsets[e];
+            int n = (cnt + kBM - 1) / kBM;
+            if (merge && cnt > kBM && cnt % kBM >= 1 && cnt % kBM <= kBM / 2) --n;
+            if (n != m_tiles(cnt, merge == 1)) fail("m-tiles of an expert", n, m_tiles(cnt, merge == 1));
+            for (int m = 0; m < n; ++m) {
+                r.tiles[merge].push_back(e);
+                r.tiles[merge].push_back(m * kBM);
+            }
         }
+        r.n_mt[merge] = (int)r.tiles[merge].size() / 2;
     }
-    r.n_mt = (int)r.tiles.size() / 2;
     return r;
 }
 
-// tile-list index of expert e's first m-tile
-static int first_mt_of(const Routing &r, int e) {
-    for (int i = 0; i < r.n_mt; ++i)
-        if (r.tiles[2 * i] == e) return i;
+// index of expert e's first m-tile in tile list m
+static int first_mt_of(const Routing &r, int m, int e) {
+    for (int i = 0; i < r.n_mt[m]; ++i)
+        if (r.tiles[m][2 * i] == e) return i;
     return -1;
 }
 
 static long long max_m_tiles(const Problem &p) { return ((long long)p.T * p.k + kBM - 1) / kBM + p.E; }
 
 // one GEMM (swiglu: the first) over every tile of the list; kloop: whole-array descriptors (the
-// persistent and single-launch forms), else per-tile ones; gather: activations from the token rows
-static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kloop, bool gather, bool rows_too) {
+// persistent and single-launch forms), else per-tile ones; gather: activations from the token rows;
+// merge: the multi-launch GEMMs' tile list (token blocks staged: exactly the tile's, up to three),
+// else the single-launch forward's (at most two token blocks staged for every tile)
+static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kloop, bool gather, bool rows_too,
+                        bool merge) {
+    const int ml = merge ? 1 : 0;
+    const int n_mt = r.n_mt[ml];
+    const int *tiles = r.tiles[ml].data();
     const int S = p.T * p.k, K = swiglu ? p.H : p.I, N = swiglu ? 2 * p.I : p.H;
     const int sb = p.mx ? 32 : 16, nc = K / kKC, nb_n = N / kBN;
     const int w_pitch = p.tiled ? kKC / 2 : K / 2, w_step = p.tiled ? 32 * (kKC / 2) : kKC / 2;
     const int s_pitch = p.tiled ? kKC / sb : K / sb, s_step = p.tiled ? 32 * (kKC / sb) : kKC / sb;
     const int a_rows = gather ? p.T : S;
     const long long max_tiles = max_m_tiles(p);
-    if (r.n_mt > max_tiles) fail("tile count", r.n_mt, max_tiles);
-    for (int v = 0; v < r.n_mt * nb_n; ++v) {
-        const Tile t = tile_of(v, nb_n, r.offsets.data(), r.tiles.data(), r.n_mt);
-        if (!t.valid) fail("tile of a live block", v, r.n_mt * nb_n);
+    if (n_mt > max_tiles) fail("tile count", n_mt, max_tiles);
+    // every row of every expert in exactly one tile of each n-tile
+    std::vector<int> cover((size_t)S * nb_n, 0);
+    for (int v = 0; v < n_mt * nb_n; ++v) {
+        const Tile t = tile_of(v, nb_n, r.offsets.data(), tiles, n_mt, merge);
+        if (!t.valid || t.nt < 0 || t.nt >= nb_n || t.rows < 1) continue;
+        for (int i = 0; i < t.rows && t.row_begin + i < S; ++i) cover[(size_t)(t.row_begin + i) * nb_n + t.nt]++;
+    }
+    for (int row = 0; row < r.offsets[p.E]; ++row)
+        for (int nt = 0; nt < nb_n; ++nt)
+            if (cover[(size_t)row * nb_n + nt] != 1) fail("row covered by tiles", cover[(size_t)row * nb_n + nt], 1);
+    for (int v = 0; v < n_mt * nb_n; ++v) {
+        const Tile t = tile_of(v, nb_n, r.offsets.data(), tiles, n_mt, merge);
+        if (!t.valid) fail("tile of a live block", v, n_mt * nb_n);
         check_range("tile rows", t.row_begin, t.rows, (long long)r.offsets[t.e + 1]);
         if (t.rows < 1 || t.row_begin < r.offsets[t.e]) fail("tile rows", t.rows, t.row_begin);
+        if (t.rows > (merge ? kMaxRows : kBM)) fail("tile rows", t.rows, merge ? kMaxRows : kBM);
         if (t.nt < 0 || t.nt >= nb_n) fail("n-tile", t.nt, nb_n);
-        if (t.mt < 0 || t.mt >= r.n_mt) fail("m-tile", t.mt, r.n_mt);
-        for (int NTB = t.rows > 32 ? 2 : 1; NTB <= 2; ++NTB) {  // token blocks the kernel stages
+        if (t.mt < 0 || t.mt >= n_mt) fail("m-tile", t.mt, n_mt);
+        const int need = (t.rows + 31) / 32;
+        for (int NTB = need; NTB <= (merge ? need : 2); ++NTB) {  // token blocks the kernel stages
         // descriptors
         const long long w_rows = kloop ? (long long)p.E * N : N;
         const long long nW = w_rows * (K / 2), nWs = w_rows * (K / sb);
@@ -156,7 +184,7 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
                         fail("weight block rows", rl, il);
             // weight offsets depend only on (expert, n-tile): once per pair; offsets grow linearly with
             // the chunk, so its first and last chunk bound every other
-            if (t.mt != first_mt_of(r, t.e) || NTB != 2) continue;
+            if (t.mt != first_mt_of(r, ml, t.e) || NTB != need) continue;
             for (int lane = 0; lane < 64; ++lane)
                 for (int c : {0, nc - 1}) {
                     for (int i = 0; i < 4; ++i)
@@ -207,7 +235,7 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
                             kWSlot);
                 for (int tb = 0; tb < NTB; ++tb)
                     for (int buf = 0; buf < 2; ++buf)
-                        check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kBM * 2);
+                        check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kMaxRows * 2);
             }
             }
             for (int wave = 0; wave < 4; ++wave)
@@ -236,11 +264,13 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
 // weight staging, operand reads, the SwiGLU hand-over
 static void replay_lds() {
     for (bool mx : {false, true})
-        for (int NTB = 1; NTB <= 2; ++NTB) {
+        for (int NTB = 1; NTB <= 3; ++NTB) {
             for (int tid = 0; tid < kThreads; ++tid) {
                 for (int i = 0; i < NTB * 2; ++i) check_range("LDS activation write", lds_act(act_row(tid, i), act_gran(tid)), 16, kActBuf);
-                if (tid < NTB * 32)
-                    for (int buf = 0; buf < 2; ++buf) check_range("LDS scale write", 4 * lds_xs(buf, tid, 0), 8, 4 * 2 * kBM * 2);
+                if (tid < NTB * 32) {
+                    if (act_scale_row(tid) != tid) fail("activation scale row", act_scale_row(tid), tid);
+                    for (int buf = 0; buf < 2; ++buf) check_range("LDS scale write", 4 * lds_xs(buf, tid, 0), 8, 4 * 2 * kMaxRows * 2);
+                }
             }
             for (int lane = 0; lane < 64; ++lane) {
                 const int h = lane >> 5;
@@ -259,7 +289,7 @@ static void replay_lds() {
                                 kWSlot);
                     for (int tb = 0; tb < NTB; ++tb)
                         for (int buf = 0; buf < 2; ++buf)
-                            check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kBM * 2);
+                            check_range("LDS scale read", 4 * lds_xs(buf, tb * 32 + (lane & 31), q), 4, 4 * 2 * kMaxRows * 2);
                 }
                 for (int wu = 0; wu < 2; ++wu)
                     for (int tb = 0; tb < NTB; ++tb)
@@ -275,8 +305,10 @@ static void replay_fused_tails(const Problem &p, const Routing &r) {
     const long long max_tiles = max_m_tiles(p);
     constexpr int kLine = 32;  // counters one 128-byte line apart
     const long long n_counters = (max_tiles * n_cb + max_tiles) * kLine;
-    for (int v = 0; v < r.n_mt * nb1; ++v) {
-        const Tile t = tile_of(v, nb1, r.offsets.data(), r.tiles.data(), r.n_mt);
+    const int n_mt = r.n_mt[0];
+    const int *tiles = r.tiles[0].data();
+    for (int v = 0; v < n_mt * nb1; ++v) {
+        const Tile t = tile_of(v, nb1, r.offsets.data(), tiles, n_mt, false);
         const int cb = t.nt >> 1;
         check_range("re-quantisation counter", ((long long)t.mt * n_cb + cb) * kLine, 1, max_tiles * n_cb * kLine);
         check_range("ready counter", (max_tiles * n_cb + t.mt) * kLine, 1, n_counters);
@@ -293,9 +325,9 @@ static void replay_fused_tails(const Problem &p, const Routing &r) {
             }
     }
     // each 128-column block of h: exactly two GEMM1 tiles per m-tile
-    std::vector<int> pairs((size_t)r.n_mt * n_cb, 0);
-    for (int v = 0; v < r.n_mt * nb1; ++v) {
-        const Tile t = tile_of(v, nb1, r.offsets.data(), r.tiles.data(), r.n_mt);
+    std::vector<int> pairs((size_t)n_mt * n_cb, 0);
+    for (int v = 0; v < n_mt * nb1; ++v) {
+        const Tile t = tile_of(v, nb1, r.offsets.data(), tiles, n_mt, false);
         pairs[(size_t)t.mt * n_cb + (t.nt >> 1)]++;
     }
     for (int c : pairs)
@@ -345,7 +377,8 @@ static void replay_front_end(const Problem &p, const Routing &r, int threads) {
         check_range("slot_row store", s, 1, S);
     }
     check_range("offsets store", p.E, 1, p.E + 1);
-    check_range("tile list", (long long)r.n_mt * 2 - 1, 1, 2 * max_m_tiles(p));
+    check_range("tile list", (long long)r.n_mt[0] * 2 - 1, 1, 2 * max_m_tiles(p));
+    check_range("tile list", (long long)r.n_mt[1] * 2 - 1, 1, 2 * max_m_tiles(p));
 }
 
 int main() {
@@ -378,11 +411,15 @@ int main() {
             const bool fits = (long long)p.E * 2 * p.I * (p.H / 2) < (1ll << 31);
             const bool kloop_ok = p.H % 1024 == 0 && p.I % 1024 == 0 && fits;
             const bool rows_too = p.mx == p.tiled;  // once per shape and routing (two of the four formats)
-            for (bool kloop : {false, true}) {
+            // multi-launch GEMMs (merged tile list): one tile per workgroup, and the persistent form
+            // (T <= 32); the single-launch forward's GEMM phases (64-row tile list, two token blocks)
+            for (int form = 0; form < 3; ++form) {
+                const bool kloop = form > 0, merge = form < 2;
                 if (kloop && !kloop_ok) continue;
-                replay_gemm(p, r, true, kloop, true, rows_too);   // the forward: GEMM1 gathers through row_src
-                replay_gemm(p, r, true, kloop, false, rows_too);  // moe_grouped_ffn: GEMM1 on x_perm
-                replay_gemm(p, r, false, kloop, false, rows_too);
+                if (form == 1 && p.T > 32) continue;
+                replay_gemm(p, r, true, kloop, true, rows_too, merge);   // the forward: GEMM1 gathers through row_src
+                if (form < 2) replay_gemm(p, r, true, kloop, false, rows_too, merge);  // moe_grouped_ffn: GEMM1 on x_perm
+                replay_gemm(p, r, false, kloop, false, rows_too, merge);
             }
             const int S = p.T * p.k;
             if (kloop_ok && p.T <= 256 && S <= 2048 && rows_too) {

@@ -20,8 +20,8 @@ import oracle
 import token_permute_grouped_amd as tpg
 from moe_synth import CONFIGS, MoeConfig, generate
 from moe_synth.gen import w4a8_sweep_tokens
-from tests._gpu import DEV, DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, \
-    whole_tiles
+from tests._gpu import DEV, DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, merged_tile_rows, rel_err, \
+    to_dev, whole_tiles
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,10 @@ SMALL = {
     "w4_fused_t100_il_drop": MoeConfig("w4_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
     "w4_fused_e256": MoeConfig("w4_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8", swiglu_clamp=10.0),
+    # every expert 65..85 rows: one m-tile of three 32-row token blocks each (a remainder of at most
+    # 32 rows joins the expert's 64-row tile), one of them with a single extra row
+    "w4_merged_tiles": MoeConfig("w4_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8",
+                                 glu_interleave=32, swiglu_clamp=10.0, drop_p=0.05),
 }
 
 
@@ -169,6 +173,7 @@ def test_grouped_ffn_full_layer_sampled_rows():
         if off[e + 1] > off[e]:
             rows += [off[e], off[e + 1] - 1]
     rows = np.union1d(np.array(rows, dtype=np.int64), whole_tiles(off, 64))  # + two whole 64-row m-tiles
+    rows = np.union1d(rows, merged_tile_rows(off, 64))  # + a whole three-block (merged) m-tile
     expert = np.searchsorted(off, rows, side="right") - 1
     ref = oracle.ffn_rows(inp, row_src.cpu().numpy()[rows] // cfg.k, expert)
     err = rel_err(bf16_f64(bf16_host(y)[rows]), ref)

@@ -17,7 +17,8 @@ import oracle
 import token_permute_grouped_amd as tpg
 from moe_synth import CONFIGS, MoeConfig, generate
 from moe_synth.gen import w4a8_sweep_tokens
-from tests._gpu import DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, rel_err, to_dev, whole_tiles
+from tests._gpu import (DeviceProblem, assert_all_rows_written, bf16_f64, bf16_host, merged_tile_rows, rel_err, to_dev,
+                        whole_tiles)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +37,9 @@ SMALL = {
     "mx_fused_t100_il_drop": MoeConfig("mx_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8_mx",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
     "mx_fused_e256": MoeConfig("mx_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
+    # every expert 65..85 rows: one m-tile of three 32-row token blocks each
+    "mx_merged_tiles": MoeConfig("mx_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8_mx",
+                                 glu_interleave=32, swiglu_clamp=10.0, drop_p=0.05),
 }
 
 
@@ -126,7 +130,8 @@ def test_grouped_ffn_full_layer_sampled_rows():
         for e in range(inp["cfg"].E):
             if off[e + 1] > off[e]:
                 rows += [off[e], off[e + 1] - 1]
-        return np.union1d(np.array(rows, dtype=np.int64), whole_tiles(off, 64))  # + two whole 64-row m-tiles
+        rows = np.union1d(np.array(rows, dtype=np.int64), whole_tiles(off, 64))  # + two whole 64-row m-tiles
+        return np.union1d(rows, merged_tile_rows(off, 64))  # + a whole three-block (merged) m-tile
 
     err, got, R = _ffn_rows_err(inp, d, first_last)
     print(f"[gpu w4a8_mx] full layer: grouped FFN on the first and last row of every expert and two whole "

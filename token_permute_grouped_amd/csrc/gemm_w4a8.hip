@@ -17,13 +17,15 @@
 //   3. GEMM2: y = gs2_e * sum_kb hs[kb] * (h8 . w8), rounded to bf16
 //
 // The GEMMs stream packed weights, which is what bounds them at small token counts.
-// Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows and
-// 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every token of the
-// tile.  Weights are never shared between waves: each wave loads its rows with
-// line-coalesced loads (8 lanes per 128-byte line) three 256-wide K chunks ahead (four
-// register sets), transposes each chunk through its own LDS slot into the MFMA operand
-// layout (lane l: row l % 32, one contiguous 32-code run per 64-wide K step) and
-// dequantises it there.  Activations are shared by the four waves: each chunk of the
+// Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows (an
+// expert's last tile up to 96: the tile list lets a remainder of at most 32 rows join
+// the tile before it, so that it does not stream the expert's weights once more for a
+// few rows) and 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every
+// token of the tile.  Weights are never shared between waves: each wave loads its rows
+// with line-coalesced loads (8 lanes per 128-byte line) three 256-wide K chunks ahead
+// (four register sets; two ahead in three sets for three token blocks), transposes each
+// chunk through its own LDS slot into the MFMA operand layout (lane l: row l % 32, one
+// contiguous 32-code run per 64-wide K step) and dequantises it there.  Activations are shared by the four waves: each chunk of the
 // tile's token rows and its activation scales are loaded into registers two chunks
 // ahead and written to LDS one chunk ahead (two buffers, swizzled).  Every load is an
 // ordinary register load, so the compiler's own waits are exact: no wait drains the
@@ -69,7 +71,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-static_assert(w4::kBM == kGemmBMW4A8, "the tile holds at most two 32-token blocks");
+static_assert(w4::kBM == kGemmBMW4A8, "m-tiles of two 32-token blocks (three for an expert's merged last tile)");
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
 
@@ -150,10 +152,11 @@ struct WChunk {
 struct StaticSched {
     int v, stride, nb_n, n_mt;
     const int32_t *offsets, *tiles;
-    __device__ Tile first() { return w4::tile_of(v, nb_n, offsets, tiles, n_mt); }
+    bool merge;  // the tile list merges an expert's last partial tile of at most 32 rows
+    __device__ Tile first() { return w4::tile_of(v, nb_n, offsets, tiles, n_mt, merge); }
     __device__ Tile next() {
         v += stride;
-        return w4::tile_of(v, nb_n, offsets, tiles, n_mt);
+        return w4::tile_of(v, nb_n, offsets, tiles, n_mt, merge);
     }
     __device__ void before_act(const Tile &) {}
     __device__ void after_tile(const Tile &) {}
@@ -252,9 +255,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
         else
             w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * g.s_step, 0);
     };
-    unsigned char *const wl = wlds + wave * (2 * kWSlot);  // this wave's two staging slots
-    auto store_w = [&](const WChunk &w, int slot) {
-        unsigned char *d = wl + slot * kWSlot;
+    // this wave's staging slot: a chunk's weights are written after the wave's reads of the
+    // previous chunk's, and one wave's LDS accesses complete in order, so one slot serves
+    unsigned char *const wl = wlds + wave * kWSlot;
+    auto store_w = [&](const WChunk &w) {
+        unsigned char *d = wl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
         if constexpr (kMX)
@@ -282,8 +287,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
     auto compute = [&](int buf) {
         const unsigned char *ab = act + buf * kActBuf;
-        const unsigned char *wr = wl + buf * kWSlot + w4::lds_wread(lane);
-        const unsigned char *wsr = wl + buf * kWSlot + w4::lds_wsread(lane);
+        const unsigned char *wr = wl + w4::lds_wread(lane);
+        const unsigned char *wsr = wl + w4::lds_wsread(lane);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             float xs[NTB];
@@ -402,17 +407,21 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // It ends like a loop step (activations of the next chunk, then one weight set), so the
     // loads in flight at the loop head follow the same pattern on entry as on the back edge
     // and the compiler's waits there stay exact.
-    WChunk w[kNBuf];
+    // weight register sets: kNBuf, or one fewer for three token blocks (their accumulators take
+    // the registers)
+    constexpr int NBUF = NTB == 3 ? kNBuf - 1 : kNBuf;
+    static_assert(!kLoop || NBUF == kNBuf, "the persistent form rotates kNBuf sets across tiles");
+    WChunk w[NBUF];
     load_w(w[0], A, 0);
     sc.before_act(cur);
     finish_addr(A, cur);
     load_a(A, 0);
 #pragma unroll
-    for (int c = 1; c < kNBuf - 2; ++c) load_w(w[c], A, min(c, nc - 1));
+    for (int c = 1; c < NBUF - 2; ++c) load_w(w[c], A, min(c, nc - 1));
     store_a(0);
     load_a(A, min(1, nc - 1));
-    load_w(w[kNBuf - 2], A, min(kNBuf - 2, nc - 1));
-    store_w(w[0], 0);
+    load_w(w[NBUF - 2], A, min(NBUF - 2, nc - 1));
+    store_w(w[0]);
     lds_barrier();  // chunk 0 staged, scale table built
 
     for (;;) {
@@ -439,22 +448,25 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
         // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
         // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
         // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
-        // c + kNBuf - 1 (into the set of chunk c - 1).  Whole groups of four steps: a step past
+        // c + NBUF - 1 (into the set of chunk c - 1).  Whole groups of four steps: a step past
         // the last chunk (single-tile form with K / kKC not a multiple of four) skips only its
         // compute (which issues no memory loads), so every path through the loop issues the same
         // loads and the compiler's waits at the loop head see the regular pattern.
-        for (int c0 = 0; c0 < nc; c0 += kNBuf) {
+        for (int c0 = 0; c0 < nc; c0 += NBUF) {
 #pragma unroll
-            for (int sidx = 0; sidx < kNBuf; ++sidx) {
+            for (int sidx = 0; sidx < NBUF; ++sidx) {
                 const int c = c0 + sidx;
                 if (kLoop && sidx == 2 && c0 == 0 && go_on) finish_addr(B, nxt);
                 if (c < nc) compute(c & 1);
-                store_w(w[(sidx + 1) % kNBuf], (c + 1) & 1);
+                // the staging slot is rewritten below: keep these writes after the reads above
+                // (the lanes of the wave read each other's bytes; its LDS accesses run in order)
+                asm volatile("" ::: "memory");
+                store_w(w[(sidx + 1) % NBUF]);
                 store_a((c + 1) & 1);
-                const int ca = req(c + 2), cw = req(c + kNBuf - 1);
+                const int ca = req(c + 2), cw = req(c + NBUF - 1);
                 if (go_on && c + 2 == nc) sc.before_act(nxt);  // the next tile's first activation load
                 load_a(c + 2 < nc ? A : B, ca);
-                load_w(w[(sidx + kNBuf - 1) % kNBuf], c + kNBuf - 1 < nc ? A : B, cw);
+                load_w(w[(sidx + NBUF - 1) % NBUF], c + NBUF - 1 < nc ? A : B, cw);
                 lds_barrier();
             }
         }
@@ -474,20 +486,22 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
 #define TPG_W4A8_LDS                                                                                   \
     __shared__ __attribute__((aligned(1024))) unsigned char act[2 * kActBuf];                          \
     __shared__ u32x2 lut[256];                                                                         \
-    __shared__ float xsl[2 * kBM * 2]; /* activation scales of the staged chunks [buf][row][block] */ \
-    __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * 2 * kWSlot]; /* 2 slots per wave */ \
+    __shared__ float xsl[2 * w4::kMaxRows * 2]; /* activation scales of the staged chunks [buf][row][block] */ \
+    __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * kWSlot]; /* one slot per wave */ \
     if constexpr (!kMX) lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after a tile's first barrier */
 
-// one tile per workgroup; its token-block count from its own rows
+// one tile per workgroup; its token-block count (1 to 3) from its own rows
 template <bool kSwiGLU, bool kMX>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    StaticSched sc{(int)blockIdx.x, 0, g.N / kBN, n_tiles[0], offsets, tiles};
+    StaticSched sc{(int)blockIdx.x, 0, g.N / kBN, n_tiles[0], offsets, tiles, true};
     const Tile t = sc.first();
     if (!t.valid) return;
-    if (t.rows > 32)
+    if (t.rows > 2 * 32)
+        w4a8_tiles<kSwiGLU, kMX, 3, false>(g, sc, act, xsl, wlds, lut);
+    else if (t.rows > 32)
         w4a8_tiles<kSwiGLU, kMX, 2, false>(g, sc, act, xsl, wlds, lut);
     else
         w4a8_tiles<kSwiGLU, kMX, 1, false>(g, sc, act, xsl, wlds, lut);
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kern
     W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    StaticSched sc{(int)blockIdx.x, (int)gridDim.x, g.N / kBN, n_tiles[0], offsets, tiles};
+    StaticSched sc{(int)blockIdx.x, (int)gridDim.x, g.N / kBN, n_tiles[0], offsets, tiles, true};
     w4a8_tiles<kSwiGLU, kMX, 1, true>(g, sc, act, xsl, wlds, lut);
 }
 
@@ -750,8 +764,8 @@ struct FusedSched {
     }
     __device__ Tile decode(int it) {
         if (kG1 ? it >= n1 : (it < n1 || it >= n1 + n2)) return Tile{};
-        return kG1 ? w4::tile_of(it, 2 * f.I / kBN, f.offsets, f.tiles, n_mt)
-                   : w4::tile_of(it - n1, f.H / kBN, f.offsets, f.tiles, n_mt);
+        return kG1 ? w4::tile_of(it, 2 * f.I / kBN, f.offsets, f.tiles, n_mt, false)
+                   : w4::tile_of(it - n1, f.H / kBN, f.offsets, f.tiles, n_mt, false);
     }
     __device__ Tile first() {
         if (!st.have) {

@@ -126,7 +126,7 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
     int32_t *tiles = (int32_t *)(ws + L.tiles);
     int32_t *n_tiles = (int32_t *)(ws + L.n_tiles);
     const int64_t max_tiles = max_m_tiles(p);
-    int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), is_w4a8(&p), tiles, n_tiles, s));
+    int st = hip_status(launch_build_tiles(offsets, p.E, gemm_bm(p), tile_order(p), tiles, n_tiles, s));
     if (st) return st;
     if (is_w4a8(&p))
         return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, nullptr, offsets, tiles,
@@ -193,7 +193,7 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
     const bool small = n_slots(*p) <= kChunk && p->T <= 256;
     if ((st = mark(0))) return st;
     if (small) {
-        if ((st = hip_status(launch_frontend_small(logits, slot_drop, p->T, p->E, p->k, gemm_bm(*p), is_w4a8(p), topk_idx,
+        if ((st = hip_status(launch_frontend_small(logits, slot_drop, p->T, p->E, p->k, gemm_bm(*p), tile_order(*p), topk_idx,
                                                    topk_w, offsets, row_src, slot_row, tiles, n_tiles, s))))
             return st;
     } else if ((st = hip_status(launch_route_topk(logits, slot_drop, p->T, p->E, p->k, topk_idx, topk_w, s)))) {
@@ -202,7 +202,7 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
     if ((st = mark(1))) return st;
     // the tables' scan launch also writes the GEMM tile list
     if (!small && (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row,
-                                                 gemm_bm(*p), is_w4a8(p), tiles, n_tiles, s))))
+                                                 gemm_bm(*p), tile_order(*p), tiles, n_tiles, s))))
         return st;
     if ((st = mark(2))) return st;
     const bool fused = fused_gather(*p);

@@ -63,8 +63,11 @@ constexpr int kGemmBMW4A8 = 64;
 inline int64_t n_slots(const moe_problem &p) { return (int64_t)p.T * p.k; }
 inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1) / kChunk; }
 inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? kGemmBM : kGemmBMW4A8; }
-// upper bound of sum_e ceil(count_e / bm) over any routing
+// upper bound of sum_e ceil(count_e / bm) over any routing (also of the merged W4A8 tile count)
 inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + gemm_bm(p) - 1) / gemm_bm(p) + p.E; }
+// tile list order (build_tile_list's by_expert): bf16 full tiles first; W4A8 by expert, an expert's
+// last partial tile of at most 32 rows merged into the tile before it (a 96-row tile at most)
+inline int tile_order(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? 0 : 2; }
 
 WsLayout ws_layout(const moe_problem &p);
 
@@ -79,7 +82,7 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
 hipError_t launch_permute(const void *x, const float *x_scale, const int32_t *slot_row, int T, int k, int H,
                           int elem_bytes, void *x_perm, float *x_perm_scale, hipStream_t s);
 
-// GEMM m-tile list; by_expert: each expert's tiles together (W4A8), else full tiles first (bf16)
+// GEMM m-tile list in order by_expert (see build_tile_list and tile_order)
 hipError_t launch_build_tiles(const int32_t *offsets, int E, int bm, int by_expert, int32_t *tiles,
                               int32_t *n_tiles, hipStream_t s);
 

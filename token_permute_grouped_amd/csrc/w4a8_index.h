@@ -15,11 +15,13 @@ namespace tpg {
 namespace w4 {
 
 constexpr int kBM = 64;            // token rows per m-tile (2 blocks of 32)
+constexpr int kMaxRows = 96;       // rows of an expert's last m-tile when a remainder of at most 32
+                                   // rows joins it (3 blocks of 32)
 constexpr int kBN = 128;           // weight rows per workgroup (4 waves x 32)
 constexpr int kKC = 256;           // K per chunk
 constexpr int kNBuf = 4;           // weight register sets (weights kNBuf - 1 chunks ahead)
 constexpr int kThreads = 256;
-constexpr int kActBuf = kBM * kKC;  // bytes of one staged activation chunk (16 KB, two buffers)
+constexpr int kActBuf = kMaxRows * kKC;  // bytes of one staged activation chunk (24 KB, two buffers)
 // per-wave LDS staging of one chunk's weights in rows: 32 code rows of 128 bytes padded to 144
 // (so that 16 consecutive rows read at one column hit 16 distinct bank groups), then 32 scale
 // rows of 16 bytes
@@ -39,25 +41,35 @@ struct Tile {
 // n-tiles of one expert m-tile that run side by side (see tile_of)
 TPG_HD int tile_group(int nb_n) { return nb_n % 8 == 0 ? 8 : nb_n % 4 == 0 ? 4 : nb_n % 2 == 0 ? 2 : 1; }
 
+// m-tiles of an expert with cnt rows: kBM-row tiles, or with `merge` a last partial tile of at
+// most kBM / 2 rows joined to the tile before it (the tile list's by-expert merged form)
+TPG_HD int m_tiles(int cnt, bool merge) {
+    if (!merge) return (cnt + kBM - 1) / kBM;
+    if (cnt <= 0) return 0;
+    const int m = cnt / kBM + (cnt % kBM > kBM / 2 ? 1 : 0);
+    return m > 0 ? m : 1;
+}
+
 // Virtual block v -> tile.  The tile list holds each expert's m-tiles together.  Expert e's
 // blocks are [first * nb_n, (first + nm) * nb_n); they run in units of G n-tiles, the nm
 // m-tiles of an n-tile G blocks apart: with G = 8 those land on one XCD (block b runs on XCD
 // b mod 8, and the persistent grid's stride is a multiple of 8) at the same time, so the
-// weights an expert's second m-tile streams are L2 hits.
-TPG_HD Tile tile_of(int v, int nb_n, const int32_t *offsets, const int32_t *tiles, int n_mt) {
+// weights an expert's second m-tile streams are L2 hits.  An expert's last m-tile runs to the
+// expert's last row (up to kMaxRows rows with `merge`).
+TPG_HD Tile tile_of(int v, int nb_n, const int32_t *offsets, const int32_t *tiles, int n_mt, bool merge) {
     Tile t{};
     const int tq = v / nb_n;  // a tile of the expert this block works for
     t.valid = tq < n_mt;
     if (!t.valid) return t;
     t.e = tiles[2 * tq];
     const int first = tq - tiles[2 * tq + 1] / kBM;
-    const int nm = (offsets[t.e + 1] - offsets[t.e] + kBM - 1) / kBM;
+    const int nm = m_tiles(offsets[t.e + 1] - offsets[t.e], merge);
     const int G = tile_group(nb_n);
     const int r = v - first * nb_n, unit = nm * G;
     t.mt = first + (r % unit) / G;
     t.nt = (r / unit) * G + (r % unit) % G;
     t.row_begin = offsets[t.e] + tiles[2 * t.mt + 1];
-    t.rows = imin(kBM, offsets[t.e + 1] - t.row_begin);
+    t.rows = t.mt == first + nm - 1 ? offsets[t.e + 1] - t.row_begin : kBM;
     return t;
 }
 
@@ -88,11 +100,11 @@ TPG_HD int w_scale_bytes(int sb) { return kKC / sb / 2; }
 
 // Activation staging: thread tid stages granule tid % 16 (16 bytes) of tile rows tid / 16 + 16 i
 // (i < 2 NTB), and thread tid < 32 NTB the chunk's two activation scales of tile row
-// min(tid, kBM - 1).  Row rr of the source (the token row when gathering, else the row within the
+// min(tid, kMaxRows - 1).  Row rr of the source (the token row when gathering, else the row within the
 // descriptor): bytes rr * K + g * 16 (+ c * kKC for chunk c), scales rr * (K/128) * 4 (+ c * 8).
 TPG_HD int act_row(int tid, int i) { return (tid >> 4) + 16 * i; }
 TPG_HD int act_gran(int tid) { return tid & 15; }
-TPG_HD int act_scale_row(int tid) { return imin(tid, kBM - 1); }
+TPG_HD int act_scale_row(int tid) { return imin(tid, kMaxRows - 1); }
 TPG_HD uint32_t a_off(int rr, int K, int g) { return (uint32_t)(rr * K + g * 16); }
 TPG_HD uint32_t s_off(int rr, int K) { return (uint32_t)(rr * (K / 128) * 4); }
 // offset given to a row past the tile's live rows: beyond every descriptor, so it reads zero
@@ -109,8 +121,8 @@ TPG_HD int lds_wscale(int lane, bool mx) { return kWScales + (lane >> 1) * 16 + 
 // dword at - 4 h + 4 q for MXFP4)
 TPG_HD int lds_wread(int lane) { return (lane & 31) * kWRow + (lane >> 5) * 32; }
 TPG_HD int lds_wsread(int lane) { return kWScales + (lane & 31) * 16 + (lane >> 5) * 4; }
-// activation scale of tile row r, block q of the chunk (float index into [2][kBM][2])
-TPG_HD int lds_xs(int buf, int r, int q) { return buf * (kBM * 2) + r * 2 + q; }
+// activation scale of tile row r, block q of the chunk (float index into [2][kMaxRows][2])
+TPG_HD int lds_xs(int buf, int r, int q) { return buf * (kMaxRows * 2) + r * 2 + q; }
 // SwiGLU hand-over: accumulator v of token block tb of up wave 2 + wu, lane l (float index)
 TPG_HD int lds_xch(int wu, int NTB, int tb, int v, int lane) { return ((wu * NTB + tb) * 16 + v) * 64 + lane; }
 // activation granules of lane half h in 64-K step (q, t) of a chunk: the fp8 operand's bytes
