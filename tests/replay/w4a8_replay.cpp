@@ -107,17 +107,21 @@ static Routing make_routing(const Problem &p, int mode, Rng &rng) {
     // the tile lists of the W4A8 GEMMs: each expert's 64-row m-tiles together ([0], the
     // single-launch forward's), and the same with a last remainder of 1..32 rows (after at least
     // one full tile) left to the tile before it ([1], the multi-launch GEMMs')
+    // (the merged list puts the experts whose last tile is a merged one first)
     for (int merge = 0; merge < 2; ++merge) {
-        for (int e = 0; e < p.E; ++e) {
-            const int cnt = r.offsets[e + 1] - r.offsets[e];
-            int n = (cnt + kBM - 1) / kBM;
-            if (merge && cnt > kBM && cnt % kBM >= 1 && cnt % kBM <= kBM / 2) --n;
-            if (n != m_tiles(cnt, merge == 1)) fail("m-tiles of an expert", n, m_tiles(cnt, merge == 1));
-            for (int m = 0; m < n; ++m) {
-                r.tiles[merge].push_back(e);
-                r.tiles[merge].push_back(m * kBM);
+        for (int section = 0; section < 2; ++section)
+            for (int e = 0; e < p.E; ++e) {
+                const int cnt = r.offsets[e + 1] - r.offsets[e];
+                int n = (cnt + kBM - 1) / kBM;
+                const bool merged_last = merge && cnt > kBM && cnt % kBM >= 1 && cnt % kBM <= kBM / 2;
+                if (merged_last) --n;
+                if (section == 0 && n != m_tiles(cnt, merge == 1)) fail("m-tiles of an expert", n, m_tiles(cnt, merge == 1));
+                if ((section == 0) != merged_last) continue;
+                for (int m = 0; m < n; ++m) {
+                    r.tiles[merge].push_back(e);
+                    r.tiles[merge].push_back(m * kBM);
+                }
             }
-        }
         r.n_mt[merge] = (int)r.tiles[merge].size() / 2;
     }
     return r;
