@@ -264,6 +264,42 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
     }
 }
 
+// GEMM1 split in two K halves (NVFP4 at decode sizes, one tile per workgroup): each half's chunk
+// range, its partial-sum stores [2 halves][gate, up][S][I] and the re-quantisation's reads of them
+static bool split_gemm1(const Problem &p) {
+    const long long experts = p.E < (long long)p.T * p.k ? p.E : (long long)p.T * p.k;
+    return !p.mx && experts * (2LL * p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
+}
+static void replay_split(const Problem &p, const Routing &r) {
+    const int S = p.T * p.k, nb_n = 2 * p.I / kBN, nc = p.H / kKC;
+    const long long stride = (long long)S * p.I, n_part = 4 * stride;
+    if (nc % 2 != 0) fail("K chunks of a split GEMM1", nc, 2);
+    for (int v = 0; v < r.n_mt[1] * nb_n * 2; ++v) {
+        const Tile t = tile_of(v >> 1, nb_n, r.offsets.data(), r.tiles[1].data(), r.n_mt[1], true);
+        if (!t.valid) continue;
+        if (t.rows > 32) fail("rows of a split tile", t.rows, 32);
+        const int h = v & 1, c_first = h * (nc / 2), c_last = c_first + nc / 2 - 1;
+        if (c_first < 0 || c_last >= nc) fail("chunk of a K half", c_last, nc);
+        for (int wave = 0; wave < 4; ++wave)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int tok = lane & 31;
+                if (tok >= t.rows) continue;
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int col = h_col(t.nt, wave & 1, g4, lane);
+                    if (col + 4 > p.I) fail("partial column", col + 4, p.I);
+                    check_range("partial store",
+                                ((2LL * h + (wave >> 1)) * stride + (long long)(t.row_begin + tok) * p.I + col) * 4, 16,
+                                n_part * 4);
+                }
+            }
+    }
+    // the re-quantisation: row < offsets[E], lane's two columns of block b, in all four planes
+    for (int row = 0; row < r.offsets[p.E]; ++row)
+        for (int b = 0; b < p.I / 128; ++b)
+            for (int pl = 0; pl < 4; ++pl)
+                check_range("partial read", (pl * stride + (long long)row * p.I + b * 128 + 2 * 63) * 4, 8, n_part * 4);
+}
+
 // every LDS access of the tile pipeline (the same for every tile): activation and scale staging,
 // weight staging, operand reads, the SwiGLU hand-over
 static void replay_lds() {
@@ -395,7 +431,8 @@ int main() {
             for (bool tiled : {false, true}) probs.push_back({T, 7168, 2048, 32, 8, mx, tiled});
     // the small W4A8 GPU cases (K multiples of 256)
     const int small[][5] = {{64, 256, 256, 8, 2}, {1, 256, 256, 4, 4}, {100, 512, 512, 6, 3}, {300, 768, 768, 5, 2},
-                            {90, 512, 256, 4, 2}, {32, 1024, 1024, 64, 8}, {30, 512, 512, 6, 3}, {16, 1024, 1024, 32, 8}};
+                            {90, 512, 256, 4, 2}, {32, 1024, 1024, 64, 8}, {30, 512, 512, 6, 3}, {16, 1024, 1024, 32, 8},
+                            {1, 1024, 512, 8, 4}, {2, 1024, 1024, 4, 2}, {200, 512, 512, 5, 2}};
     for (auto &c : small)
         for (bool mx : {false, true}) probs.push_back({c[0], c[1], c[2], c[3], c[4], mx, false});
     // random shapes: E up to 256, k up to 32, up to 2048 slots, H, I multiples of 1024
@@ -425,6 +462,7 @@ int main() {
                 if (form < 2) replay_gemm(p, r, true, kloop, false, rows_too, merge);  // moe_grouped_ffn: GEMM1 on x_perm
                 replay_gemm(p, r, false, kloop, false, rows_too, merge);
             }
+            if (split_gemm1(p)) replay_split(p, r);
             const int S = p.T * p.k;
             if (kloop_ok && p.T <= 256 && S <= 2048 && rows_too) {
                 replay_fused_tails(p, r);

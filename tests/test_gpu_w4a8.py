@@ -42,6 +42,10 @@ SMALL = {
     "w4_fused_t100_il_drop": MoeConfig("w4_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
     "w4_fused_e256": MoeConfig("w4_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8", swiglu_clamp=10.0),
+    # one token, K = 1024: GEMM1 split in two K halves (two workgroups per tile, partial sums added by
+    # the re-quantisation)
+    "w4_one_token_split": MoeConfig("w4_one_token_split", T=1, H=1024, I=512, E=8, k=4, prec="w4a8",
+                                    swiglu_clamp=10.0),
     # every expert 65..85 rows: one m-tile of three 32-row token blocks each (a remainder of at most
     # 32 rows joins the expert's 64-row tile), one of them with a single extra row
     "w4_merged_tiles": MoeConfig("w4_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8",

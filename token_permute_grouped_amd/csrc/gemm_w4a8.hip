@@ -15,6 +15,10 @@
 //   1. GEMM1 + clamped SwiGLU: h = silu(g) * u in fp32, g, u = gs1_e * sum_kb xs[kb] * (x8 . w8)
 //   2. re-quantisation of h per (row, 128 columns): s = amax/448 (1 if 0), q = e4m3(h / s)
 //   3. GEMM2: y = gs2_e * sum_kb hs[kb] * (h8 . w8), rounded to bf16
+// For NVFP4 at decode sizes (w4a8_split_gemm1) GEMM1 runs two workgroups per tile, one per K
+// half, writing raw partial sums, and launch 2 adds the halves and applies gs1 and the SwiGLU
+// first (requant_swiglu_fp8_kernel): a CU then holds two workgroups' waves, one of which
+// dequantises while the other waits on its loads.
 //
 // The GEMMs stream packed weights, which is what bounds them at small token counts.
 // Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows (an
@@ -134,7 +138,11 @@ struct W4Args {
     const float *Wgs;    // [E] global scales
     int K, N, I, il, E;
     float clamp;
-    float *Hout;         // GEMM1: h fp32 [S][I]
+    float *Hout;         // GEMM1: h fp32 [S][I]; with split, the partial sums [2 halves][gate, up][S][I]
+    int split;           // GEMM1: 1 = one tile per workgroup, workgroup b sums K half b % 2 of tile b / 2 and
+                         // writes its partial sums; 2 = each workgroup sums both halves apart and adds them
+                         // at the end (the same arithmetic in one workgroup)
+    int64_t part_stride;  // with split: S * I (elements between the four partial-sum planes)
     uint16_t *Yout;      // GEMM2: y bf16 [S][ldy]
     int ldy;
 };
@@ -168,13 +176,17 @@ struct StaticSched {
 // tile pays for a prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at
 // the same register set and buffer phase).  sc.before_act(t) runs (uniformly, in every thread)
 // before the first activation load of tile t, sc.after_tile(t) after t's output is written.
-template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched>
+template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched, int kSplit = 0>
 __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned char *act, float *xsl,
                                            unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = g.K, kb_n = K / 128;
-    const int nc = K / kKC;
+    // kSplit (GEMM1 only, the value of g.split): 1 = this workgroup sums K half blockIdx.x % 2 and
+    // writes its partial sums; 2 = the two K halves are summed apart and added at the end
+    static_assert(kSplit == 0 || (kSwiGLU && NTB == 1), "K splits serve GEMM1 at decode sizes");
+    const int nc = (kSplit == 1 ? K / 2 : K) / kKC;               // chunks this workgroup sums
+    const int kc0 = kSplit == 1 ? (int)(blockIdx.x & 1) * nc : 0;  // its first chunk
     const int sg = w4::act_gran(tid);
     const int srow = w4::act_scale_row(tid);
     constexpr int kSB = kMX ? 32 : 16;  // K values per weight block scale
@@ -249,11 +261,12 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     Rs rs;
     auto load_w = [&](WChunk &w, const Addr &a, int c) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], c * g.w_step, 0);
+        for (int i = 0; i < 4; ++i)
+            w.c[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, a.woff[i], (kc0 + c) * g.w_step, 0);
         if constexpr (kMX)
-            w.s = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs.Ws, a.wsoff, c * g.s_step, 0), 0u};
+            w.s = u32x2{__builtin_amdgcn_raw_buffer_load_b32(rs.Ws, a.wsoff, (kc0 + c) * g.s_step, 0), 0u};
         else
-            w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, c * g.s_step, 0);
+            w.s = __builtin_amdgcn_raw_buffer_load_b64(rs.Ws, a.wsoff, (kc0 + c) * g.s_step, 0);
     };
     // this wave's staging slot: a chunk's weights are written after the wave's reads of the
     // previous chunk's, and one wave's LDS accesses complete in order, so one slot serves
@@ -271,8 +284,9 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     u32x2 ars;
     auto load_a = [&](const Addr &a, int c) {
 #pragma unroll
-        for (int i = 0; i < NTB * 2; ++i) ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, a.aoff[i], c * kKC, 0);
-        ars = __builtin_amdgcn_raw_buffer_load_b64(rs.S, a.soff, c * 8, 0);
+        for (int i = 0; i < NTB * 2; ++i)
+            ar[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, a.aoff[i], (kc0 + c) * kKC, 0);
+        ars = __builtin_amdgcn_raw_buffer_load_b64(rs.S, a.soff, (kc0 + c) * 8, 0);
     };
     auto store_a = [&](int buf) {
         unsigned char *dst = act + buf * kActBuf;
@@ -282,6 +296,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     };
 
     f32x16 acc[NTB];
+    f32x16 acc_lo[kSplit == 2 ? NTB : 1];  // the first K half's sum
 
     // lane (row r = l % 32, half h = l / 32) of 64-K step (q, t) takes code bytes
     // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
@@ -347,7 +362,24 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // through (an activation buffer no chunk still needs).
     auto epilogue = [&](const Tile &t, float *xch) {
         const float gs = g.Wgs[t.e];
-        if (kSwiGLU) {
+        if (kSplit == 1) {
+            // raw partial sums of this K half (no global scale, no SwiGLU: requant_swiglu_fp8_kernel
+            // adds the halves and applies both): gate waves to plane 2 half, up waves to 2 half + 1,
+            // at the h column each accumulator belongs to
+            float *plane = g.Hout + (int64_t)(2 * (int)(blockIdx.x & 1) + (wave >> 1)) * g.part_stride;
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                const int tok = tb * 32 + (lane & 31);
+                if (tok >= t.rows) continue;
+                float *prow = plane + (int64_t)(t.row_begin + tok) * g.I;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c0 = w4::h_col(t.nt, wave & 1, g4, lane);
+                    *(f32x4 *)(prow + c0) = f32x4{acc[tb][g4 * 4], acc[tb][g4 * 4 + 1], acc[tb][g4 * 4 + 2],
+                                                  acc[tb][g4 * 4 + 3]};
+                }
+            }
+        } else if (kSwiGLU) {
             if (wave >= 2)
 #pragma unroll
                 for (int tb = 0; tb < NTB; ++tb)
@@ -457,6 +489,14 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
             for (int sidx = 0; sidx < NBUF; ++sidx) {
                 const int c = c0 + sidx;
                 if (kLoop && sidx == 2 && c0 == 0 && go_on) finish_addr(B, nxt);
+                if (kSplit == 2 && c == nc / 2) {
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) {
+                        acc_lo[tb] = acc[tb];
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[tb][v] = 0.f;
+                    }
+                }
                 if (c < nc) compute(c & 1);
                 // the staging slot is rewritten below: keep these writes after the reads above
                 // (the lanes of the wave read each other's bytes; its LDS accesses run in order)
@@ -472,6 +512,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
         }
         // every wave has passed the last chunk's barrier; buffer nc % 2 holds the next tile's
         // first chunk (kLoop: nc is even), so the exchange uses the other one
+        if (kSplit == 2)
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[tb][v] = acc_lo[tb][v] + acc[tb][v];
         epilogue(cur, (float *)(act + ((nc + 1) & 1) * kActBuf));
         sc.after_tile(cur);
         if (!go_on) break;
@@ -496,10 +541,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
-    StaticSched sc{(int)blockIdx.x, 0, g.N / kBN, n_tiles[0], offsets, tiles, true};
+    StaticSched sc{g.split == 1 ? (int)(blockIdx.x >> 1) : (int)blockIdx.x, 0, g.N / kBN, n_tiles[0], offsets, tiles,
+                   true};
     const Tile t = sc.first();
     if (!t.valid) return;
-    if (t.rows > 2 * 32)
+    if (kSwiGLU && g.split == 1)  // decode sizes: rows of at most 32
+        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, kSwiGLU ? 1 : 0>(g, sc, act, xsl, wlds, lut);
+    else if (t.rows > 2 * 32)
         w4a8_tiles<kSwiGLU, kMX, 3, false>(g, sc, act, xsl, wlds, lut);
     else if (t.rows > 32)
         w4a8_tiles<kSwiGLU, kMX, 2, false>(g, sc, act, xsl, wlds, lut);
@@ -858,7 +906,7 @@ __device__ void fused_combine(const FusedArgs &f, int *rows_s, float *w_s) {
     }
 }
 
-template <bool kMX, int NTB>
+template <bool kMX, int NTB, bool kHalves = false>
 __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedArgs f) {
     TPG_W4A8_LDS
     __shared__ int word, n_mt_s;
@@ -913,7 +961,7 @@ __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedAr
     const int n1 = n_mt * (2 * f.I / kBN), n2 = n_mt * (f.H / kBN);
     {
         FusedSched<true> sc{f, st, &word, n_mt, n1, n2};
-        w4a8_tiles<true, kMX, NTB, true>(f.g1, sc, act, xsl, wlds, lut);
+        w4a8_tiles<true, kMX, NTB, true, FusedSched<true>, kHalves ? 2 : 0>(f.g1, sc, act, xsl, wlds, lut);
     }
     {
         FusedSched<false> sc{f, st, &word, n_mt, n1, n2};
@@ -952,6 +1000,51 @@ __global__ __launch_bounds__(256) void requant_fp8_kernel(const float *__restric
     const uint32_t q = to_fp8x2<false>(v.x / s, v.y / s, 0u);
     *(uint16_t *)(h8 + row * I + b * 128 + 2 * lane) = (uint16_t)(q & 0xffffu);
     if (lane == 0) hs[row * nb + b] = s;
+}
+
+// GEMM1 split in two K halves: h = silu(g) * u from the halves' partial sums
+// (part [2 halves][gate, up][S][I]; g = gs_e * (gate half 0 + gate half 1), u likewise, clamped,
+// then the same SwiGLU expression as the GEMM1 epilogue), then re-quantised as by
+// requant_fp8_kernel.  One wave per (row, 128 columns).
+__global__ __launch_bounds__(256) void requant_swiglu_fp8_kernel(const float *__restrict__ part, int64_t stride,
+                                                                 const int32_t *__restrict__ offsets, int E, int I,
+                                                                 const float *__restrict__ gs1, float clamp,
+                                                                 uint8_t *__restrict__ h8, float *__restrict__ hs) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nb = I / 128;
+    const int64_t row = item / nb;
+    const int b = (int)(item % nb);
+    if (row >= offsets[E]) return;
+    int lo = 0, hi = E - 1;  // the expert of the row: the last e with offsets[e] <= row
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offsets[mid] <= row) lo = mid;
+        else hi = mid - 1;
+    }
+    const float gs = gs1[lo];
+    const int64_t o = row * I + b * 128 + 2 * lane;
+    const f32x2 g0 = *(const f32x2 *)(part + o), u0 = *(const f32x2 *)(part + stride + o);
+    const f32x2 g1 = *(const f32x2 *)(part + 2 * stride + o), u1 = *(const f32x2 *)(part + 3 * stride + o);
+    float h[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float gv = gs * (g0[j] + g1[j]);
+        float uv = gs * (u0[j] + u1[j]);
+        if (clamp > 0.f) {
+            gv = fminf(fmaxf(gv, -clamp), clamp);
+            uv = fminf(fmaxf(uv, -clamp), clamp);
+        }
+        h[j] = gv / (1.0f + expf(-gv)) * uv;
+    }
+    float m = fmaxf(fabsf(h[0]), fabsf(h[1]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float sc = m / 448.0f;
+    if (sc == 0.0f) sc = 1.0f;
+    const uint32_t q = to_fp8x2<false>(h[0] / sc, h[1] / sc, 0u);
+    *(uint16_t *)(h8 + o) = (uint16_t)(q & 0xffffu);
+    if (lane == 0) hs[row * nb + b] = sc;
 }
 
 // the dequant of every (e2m1 code, e4m3 scale s) pair through the GEMMs' device routine:
@@ -1058,11 +1151,22 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     g1.clamp = p.swiglu_clamp;
     g1.Hout = h32;
     set_layout(g1, H, mx, w.w4_layout);
-    launch_w4a8_gemm<true>(mx, l1, g1, offsets, tiles, n_tiles, s);
+    const bool split = w4a8_split_gemm1(p);
+    if (split) {  // two workgroups per tile, one per K half, one tile each (rows of at most 32)
+        g1.split = 1;
+        g1.part_stride = (int64_t)S * I;
+        launch_w4a8_gemm<true>(mx, W4Launch{2 * max_tiles * (2 * I / kBN), false}, g1, offsets, tiles, n_tiles, s);
+    } else {
+        launch_w4a8_gemm<true>(mx, l1, g1, offsets, tiles, n_tiles, s);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t items = n_slots(p) * (I / 128);
-    hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
+    if (split)
+        hipLaunchKernelGGL(requant_swiglu_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, (int64_t)S * I,
+                           offsets, p.E, I, w.w1_gscale, p.swiglu_clamp, h8, hs);
+    else
+        hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     W4Args g2{};
@@ -1124,6 +1228,9 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     f.H = p.H;
     f.I = p.I;
     W4Args &g1 = f.g1;
+    // where the multi-launch GEMM1 splits K in two workgroups, sum the halves apart here too, so that
+    // the output stays bitwise the default forward's
+    g1.split = w4a8_split_gemm1(p) ? 2 : 0;
     g1.A8 = x;
     g1.As = x_scale;
     g1.row_src = row_src;
@@ -1162,10 +1269,12 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const bool one_block = p.T <= 32;  // every m-tile fits one 32-row token block
+    const bool halves = g1.split == 2;  // NVFP4 with T <= 32 only (one token block)
     const void *fn = mx ? (one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
                                      : (const void *)forward_small_w4a8_kernel<true, 2>)
-                        : (one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
-                                     : (const void *)forward_small_w4a8_kernel<false, 2>);
+                        : (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true>
+                           : one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
+                                       : (const void *)forward_small_w4a8_kernel<false, 2>);
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
     if (err != hipSuccess) return err;
     const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
@@ -1175,7 +1284,9 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
         else
             hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 2>), dim3(grid), dim3(kThreads), 0, s, f);
     } else {
-        if (one_block)
+        if (halves)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, true>), dim3(grid), dim3(kThreads), 0, s, f);
+        else if (one_block)
             hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, f);
         else
             hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, f);

@@ -78,7 +78,7 @@ WsLayout ws_layout(const moe_problem &p) {
     L.h_scale = o;
     if (is_w4a8(&p)) o = align256(o + S * (size_t)(p.I / 128) * 4);
     L.h32 = o;
-    if (is_w4a8(&p)) o = align256(o + S * (size_t)p.I * 4);
+    if (is_w4a8(&p)) o = align256(o + S * (size_t)p.I * 4 * (w4a8_split_gemm1(p) ? 4 : 1));
     L.ffn_end = o;
     L.topk_idx = o;
     o = align256(o + S * 4);

@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP translation units of libtpg_moe.so.
 // Every kernel is written for gfx950 (CDNA4, wave64).
 #pragma once
+#include <algorithm>
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -42,7 +43,8 @@ struct WsLayout {
     size_t n_tiles;       // int32 [4]              grouped GEMMs: tile count, full-tile count
     size_t h;             // bf16 [S][I]  or (W4A8) fp8 [S][I]
     size_t h_scale;       // W4A8: fp32 [S][I/128]
-    size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation)
+    size_t h32;           // W4A8: fp32 [S][I] (SwiGLU output before re-quantisation); with the GEMM1
+                          // K split, its partial sums [2 halves][gate, up][S][I]
     size_t topk_idx;      // forward only: int32 [T][k]
     size_t topk_w;        // forward only: fp32 [T][k]
     size_t offsets;       // forward only: int32 [E+1]
@@ -65,6 +67,14 @@ inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1)
 inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? kGemmBM : kGemmBMW4A8; }
 // upper bound of sum_e ceil(count_e / bm) over any routing (also of the merged W4A8 tile count)
 inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + gemm_bm(p) - 1) / gemm_bm(p) + p.E; }
+// W4A8 GEMM1 split in two halves of K (two workgroups per tile): NVFP4 weights, at most 256 GEMM1
+// tiles whatever the routing (each tile then streams its weights on a CU of its own, one wave per
+// SIMD, and the dequant goes unhidden), K a multiple of 512.  Deterministic: the halves' partial
+// sums are added by the re-quantisation (h32 holds the four partial planes: 4 x S x I floats).
+inline bool w4a8_split_gemm1(const moe_problem &p) {
+    const int64_t experts = std::min<int64_t>(p.E, (int64_t)p.T * p.k);
+    return p.prec == MOE_PREC_W4A8 && experts * (2 * (int64_t)p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
+}
 // tile list order (build_tile_list's by_expert): bf16 full tiles first; W4A8 by expert, an expert's
 // last partial tile of at most 32 rows merged into the tile before it (a 96-row tile at most)
 inline int tile_order(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? 0 : 2; }
