@@ -29,9 +29,10 @@
 // with line-coalesced loads (8 lanes per 128-byte line) three 256-wide K chunks ahead
 // (four register sets; two ahead in three sets for three token blocks), transposes each
 // chunk through its own LDS slot into the MFMA operand layout (lane l: row l % 32, one
-// contiguous 32-code run per 64-wide K step) and dequantises it there.  Activations are shared by the four waves: each chunk of the
-// tile's token rows and its activation scales are loaded into registers two chunks
-// ahead and written to LDS one chunk ahead (two buffers, swizzled).  Every load is an
+// contiguous 32-code run per 64-wide K step) and dequantises it there.  Activations are
+// shared by the four waves: each chunk of the tile's token rows and its activation scales
+// are loaded into registers two chunks ahead and written to LDS one chunk ahead (two
+// buffers, swizzled).  Every load is an
 // ordinary register load, so the compiler's own waits are exact: no wait drains the
 // weight prefetch, and the chunk barriers carry no memory fence.  In the forward the
 // first GEMM reads its rows straight from the token rows through row_src (the gather
@@ -1073,8 +1074,9 @@ namespace {
 // persistent: two workgroups per CU (the kernel's occupancy) walk the virtual blocks with the
 // grid as stride and prefetch each next tile's first chunks under the current one's last
 // steps (W4A8 layer, T = 16: 223 -> 214 us per forward).  Above 32 tokens a persistent
-// kernel would have to fix two token blocks for every tile (most tiles then hold under 32
-// rows at T = 64) and measured slower; there and for other K, one tile per workgroup.
+// kernel would have to fix the token-block count for every tile (most tiles then hold under 32
+// rows at T = 64) and measured slower; there and for other K, one tile per workgroup (and
+// for NVFP4 at decode sizes, two per tile, see w4a8_split_gemm1).
 struct W4Launch {
     int64_t grid;
     bool persistent;
