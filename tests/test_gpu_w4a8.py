@@ -50,6 +50,12 @@ SMALL = {
     # 32 rows joins the expert's 64-row tile), one of them with a single extra row
     "w4_merged_tiles": MoeConfig("w4_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8",
                                  glu_interleave=32, swiglu_clamp=10.0, drop_p=0.05),
+    # k = E: every expert holds exactly T rows; 96 = the largest merged tile (three full token
+    # blocks), 97 = a full 64-row tile and a 33-row one
+    "w4_all_experts_96": MoeConfig("w4_all_experts_96", T=96, H=512, I=256, E=4, k=4, prec="w4a8",
+                                     swiglu_clamp=10.0),
+    "w4_all_experts_97": MoeConfig("w4_all_experts_97", T=97, H=512, I=256, E=4, k=4, prec="w4a8",
+                                     swiglu_clamp=10.0),
 }
 
 

@@ -40,6 +40,12 @@ SMALL = {
     # every expert 65..85 rows: one m-tile of three 32-row token blocks each
     "mx_merged_tiles": MoeConfig("mx_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8_mx",
                                  glu_interleave=32, swiglu_clamp=10.0, drop_p=0.05),
+    # k = E: every expert holds exactly T rows; 96 = the largest merged tile (three full token
+    # blocks), 97 = a full 64-row tile and a 33-row one
+    "mx_all_experts_96": MoeConfig("mx_all_experts_96", T=96, H=512, I=256, E=4, k=4, prec="w4a8_mx",
+                                     swiglu_clamp=10.0),
+    "mx_all_experts_97": MoeConfig("mx_all_experts_97", T=97, H=512, I=256, E=4, k=4, prec="w4a8_mx",
+                                     swiglu_clamp=10.0),
 }
 
 
