@@ -191,6 +191,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-launch", action="store_true",
                     help="W4A8 workloads: the whole forward in one launch (MOE_FLAG_SINGLE_LAUNCH)")
+    ap.add_argument("--scatter-y", action="store_true",
+                    help="GEMM2 stores its rows in slot order and the combine reads them so (MOE_FLAG_SCATTER_Y)")
     ap.add_argument("--configs", choices=("all", "none"), default="all",
                     help="with the default workload, also report every other configuration (fewer steps each)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -299,8 +301,10 @@ def measure(cfg, args, detail, inp=None):
 
     w4 = cfg.prec != "bf16"
     mx = cfg.prec == "w4a8_mx"
+    flags = (tpg.MOE_FLAG_SINGLE_LAUNCH if getattr(args, "single_launch", False) else
+             tpg.MOE_FLAG_SCATTER_Y if getattr(args, "scatter_y", False) else 0)
     p = tpg.make_problem(cfg.T, cfg.H, cfg.I, cfg.E, cfg.k, tpg.PRECISIONS[cfg.prec], cfg.glu_interleave,
-                         cfg.swiglu_clamp, tpg.MOE_FLAG_SINGLE_LAUNCH if getattr(args, "single_launch", False) else 0)
+                         cfg.swiglu_clamp, flags)
     d = {k: dt(inp.get(k)) for k in ("logits", "slot_drop", "x", "x_scale", "w1", "w1_bscale", "w1_gscale", "w2",
                                       "w2_bscale", "w2_gscale")}
     layout = tpg.MOE_W4_LAYOUT_ROWS
@@ -480,8 +484,9 @@ def measure(cfg, args, detail, inp=None):
                       "grouped_gemm_w4a8_kernel<false>)",
             "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(a / PEAK_HBM_GBS, 4),
-            # the counters were taken on the default launches (not the single-launch kernel)
-            "traffic": (None if getattr(args, "single_launch", False) else
+            # the counters were taken on the default launches (not the single-launch kernel, nor
+            # GEMM2 storing in slot order)
+            "traffic": (None if flags else
                         measured_traffic(["gemm1_swiglu", "requant", "gemm2"], cfg.name, T, args.seed)),
             "algorithmic_per_launch": f"{ffn_bytes} bytes ({n_exp} experts' packed weights {w_bytes} B "
                                       f"+ activations {act_bytes} B)",
@@ -526,6 +531,8 @@ def measure(cfg, args, detail, inp=None):
         "graph_ms_per_step": round(graph_ms, 4),  # median replay of one captured forward
         "graph_cold_ms_per_step": round(graph_cold_ms, 4),  # the same, caches flushed before each
         "weight_layout": (args.w4_layout if w4 else "rows"),
+        # order of GEMM2's y rows: expert-major, or slot order (MOE_FLAG_SCATTER_Y)
+        "y_order": "slot" if flags == tpg.MOE_FLAG_SCATTER_Y else "expert",
         "roofline": roofline,
         "cpu_baseline": None,
     }

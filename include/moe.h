@@ -104,7 +104,7 @@ typedef struct moe_problem {
      * activation ("ClampedSwiGLU" in Megatron-LM PR #5984's log; the clamped
      * SwiGLU of the FlashInfer fused kernel). */
     float swiglu_clamp;
-    /* 0 or MOE_FLAG_SINGLE_LAUNCH (moe_forward only). */
+    /* 0, MOE_FLAG_SINGLE_LAUNCH or MOE_FLAG_SCATTER_Y (moe_forward only; one at a time). */
     int32_t flags;
 } moe_problem;
 
@@ -117,6 +117,18 @@ typedef struct moe_problem {
  * workspace, which the kernel resets itself (graph replay works); every wait is bounded.  On
  * this library's kernels it is slower than the default path, which stays the default. */
 #define MOE_FLAG_SINGLE_LAUNCH 1
+
+/* moe_forward stores GEMM2's output rows in slot order instead of expert order: row r of the
+ * expert-major order goes to row row_src[r] = t*k + j of the workspace's y buffer (dropped
+ * slots' rows stay unwritten), and the combine reads a token's k rows as one contiguous run.
+ * This is the second kernel of the FlashInfer split family ("[SM90] Add W4A8 MegaMoE support",
+ * the commit that adds the BN128 split family: the second GEMM with a contiguous scatter), and
+ * the unpermute folded into the producer as Megatron-LM "add permute fusion into hybrid ep"
+ * folds it.  Any precision; not with MOE_FLAG_SINGLE_LAUNCH (MOE_ERR_UNSUPPORTED).  Bitwise the
+ * same output as the default forward (the same rows, summed in the same order).  On MI355X the
+ * combine gains 2-5 % from it and GEMM2's scattered row stores lose about as much (whole
+ * forward within noise on the bf16 and W4A8 layers), so the default stays the expert order. */
+#define MOE_FLAG_SCATTER_Y 2
 
 /* Expert weights (device pointers, borrowed).  bf16: only w1 and w2 are used.
  * w4a8: w1 uint8 [E][2I][H/2], w1_bscale uint8 [E][2I][H/16], w1_gscale fp32 [E];

@@ -162,6 +162,18 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
     for (int row = 0; row < r.offsets[p.E]; ++row)
         for (int nt = 0; nt < nb_n; ++nt)
             if (cover[(size_t)row * nb_n + nt] != 1) fail("row covered by tiles", cover[(size_t)row * nb_n + nt], 1);
+    if (!swiglu) {
+        // scatter epilogue (MOE_FLAG_SCATTER_Y): row r of the expert-major order goes to y row
+        // row_src[r]; over the live rows these are the live slots, each exactly once
+        std::vector<int> hit(S, 0);
+        for (int row = 0; row < r.offsets[p.E]; ++row) {
+            const int s = r.row_src[row];
+            check_range("scatter destination row", s, 1, S);
+            if (s >= 0 && s < S) hit[s]++;
+        }
+        for (int s = 0; s < S; ++s)
+            if (hit[s] != (r.slot_row[s] >= 0 ? 1 : 0)) fail("scatter rows per slot", hit[s], r.slot_row[s] >= 0);
+    }
     for (int v = 0; v < n_mt * nb_n; ++v) {
         const Tile t = tile_of(v, nb_n, r.offsets.data(), tiles, n_mt, merge);
         if (!t.valid) fail("tile of a live block", v, n_mt * nb_n);
@@ -256,6 +268,8 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
                             const int col = y_col(t.nt, wave, g4, lane);
                             if (col + 4 > N) fail("y column", col + 4, N);
                             check_range("y store", ((long long)(t.row_begin + tok) * p.H + col) * 2, 8, (long long)S * p.H * 2);
+                            check_range("y scatter store", ((long long)r.row_src[t.row_begin + tok] * p.H + col) * 2, 8,
+                                        (long long)S * p.H * 2);
                         }
                     }
                 }

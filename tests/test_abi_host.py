@@ -51,7 +51,8 @@ def _p(**kw):
     (dict(swiglu_clamp=float("nan")), tpg.MOE_ERR_UNSUPPORTED),
     (dict(prec=1, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=1, I=384), tpg.MOE_ERR_SHAPE),
     (dict(prec=2, H=384), tpg.MOE_ERR_SHAPE), (dict(prec=2, I=384), tpg.MOE_ERR_SHAPE), (dict(prec=3), tpg.MOE_ERR_UNSUPPORTED),
-    (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE), (dict(flags=2), tpg.MOE_ERR_UNSUPPORTED),
+    (dict(H=65536, I=8192), tpg.MOE_ERR_SHAPE), (dict(flags=4), tpg.MOE_ERR_UNSUPPORTED),
+    (dict(flags=3), tpg.MOE_ERR_UNSUPPORTED), (dict(flags=-1), tpg.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_problems_are_rejected_by_every_entry_point(kw, status):
     lib = tpg.load()
@@ -200,6 +201,17 @@ def test_single_launch_flag_needs_an_eligible_problem():
         assert n > 0
         assert lib.moe_forward(FAKE, None, FAKE, FAKE, w, ctypes.byref(pr), FAKE, FAKE, n, None) == \
             tpg.MOE_ERR_UNSUPPORTED, kw
+
+
+def test_scatter_flag_is_accepted_alone_by_every_precision():
+    """MOE_FLAG_SCATTER_Y passes the problem check for every precision (the workspace is sized the
+    same); with MOE_FLAG_SINGLE_LAUNCH beside it the problem is refused"""
+    for prec in (tpg.MOE_PREC_BF16, tpg.MOE_PREC_W4A8, tpg.MOE_PREC_W4A8_MX):
+        plain = _p(prec=prec, H=1024, I=1024)
+        scat = _p(prec=prec, H=1024, I=1024, flags=tpg.MOE_FLAG_SCATTER_Y)
+        assert tpg.moe_workspace_bytes(scat) == tpg.moe_workspace_bytes(plain) > 0
+        both = _p(prec=prec, H=1024, I=1024, flags=tpg.MOE_FLAG_SCATTER_Y | tpg.MOE_FLAG_SINGLE_LAUNCH)
+        assert tpg.moe_workspace_bytes(both) == 0
 
 
 def test_noalloc_refuses_problems_beyond_its_scratch_on_the_host():

@@ -41,6 +41,7 @@ class MoeError(RuntimeError):
 
 
 MOE_FLAG_SINGLE_LAUNCH = 1
+MOE_FLAG_SCATTER_Y = 2
 
 
 class Problem(ctypes.Structure):

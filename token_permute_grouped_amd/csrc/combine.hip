@@ -1,4 +1,6 @@
-// Unpermute + combine: out[t] = bf16( sum_j w[t][j] * y_perm[slot_row[t*k+j]] ).
+// Unpermute + combine: out[t] = bf16( sum_j w[t][j] * y_perm[slot_row[t*k+j]] ), or with the
+// scatter epilogue's layout (GEMM2 stored every row at its slot) y[t*k+j] for the slots with
+// slot_row[t*k+j] >= 0: a token's k rows are then one contiguous run.
 //
 // The top-k reduction that ends the fused MoE of FlashInfer "[SM90] Add W4A8
 // MegaMoE support", with the unpermute folded in as Megatron-LM "add permute
@@ -36,7 +38,8 @@ constexpr int kThreads = 512;
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4 *__restrict__ y_perm,
                                                            const int32_t *__restrict__ slot_row,
                                                            const float *__restrict__ topk_w, int T, int k,
-                                                           int row_vec, uint4 *__restrict__ out) {
+                                                           int row_vec, bool slot_order,
+                                                           uint4 *__restrict__ out) {
     const int64_t t = blockIdx.x;
     const int32_t *rows = slot_row + t * k;  // uniform: scalar loads
     const float *w = topk_w + t * k;
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4 *__restri
             for (int q = 0; q < 8; ++q) {
                 const int j = j0 + q;
                 const int32_t r = j < k ? rows[j] : -1;
-                const uint4 *yr = y_perm + (int64_t)r * row_vec;
+                const uint4 *yr = y_perm + (slot_order ? t * k + j : (int64_t)r) * row_vec;
                 v[0][q] = r >= 0 ? load_once(yr + c0) : make_uint4(0, 0, 0, 0);
                 v[1][q] = (r >= 0 && two) ? load_once(yr + c1) : make_uint4(0, 0, 0, 0);
             }
@@ -71,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint4 *__restri
 }
 
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,
-                          uint16_t *out, hipStream_t s) {
+                          bool slot_order, uint16_t *out, hipStream_t s) {
     const int row_vec = H / 8;
     // one 16-byte chunk per thread (two above 512 chunks): as many threads as the row has chunks
     const int threads = std::min(kThreads, std::max(64, (row_vec + 63) / 64 * 64));
     hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(threads), 0, s, (const uint4 *)y_perm, slot_row, topk_w, T, k,
-                       row_vec, (uint4 *)out);
+                       row_vec, slot_order, (uint4 *)out);
     return hipGetLastError();
 }
 

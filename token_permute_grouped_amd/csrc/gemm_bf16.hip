@@ -176,7 +176,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
     const int32_t *__restrict__ tiles,     // [2 * n_tiles]: expert, first row within the expert
     const int32_t *__restrict__ n_tiles,   // [1]
     int K, int N, int I, int il, float clamp,
-    uint16_t *__restrict__ C, int ldc) {   // [S][ldc]
+    uint16_t *__restrict__ C, int ldc,     // [S][ldc]
+    const int32_t *__restrict__ row_dst) { // NULL, or [S]: row r of the tile order is stored to row row_dst[r] of C
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kBBase + kBStages * kBStage];  // 160 KB
 
     // ---- tile of this workgroup: band of m-tiles, XCD rectangle within the band, tile within it
@@ -506,7 +507,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_bf16_kernel(
         for (int r0 = wave * kRowsPerOp; r0 < kBM; r0 += kWaves * kRowsPerOp) {
             const int tr = r0 + sr;
             if (tr < rows)
-                *(u32x4 *)(C + (int64_t)(row_begin + tr) * ldc + c0) = *(const u32x4 *)(lds + cofs(tr, sc));
+                *(u32x4 *)(C + (int64_t)(row_dst ? row_dst[row_begin + tr] : row_begin + tr) * ldc + c0) =
+                    *(const u32x4 *)(lds + cofs(tr, sc));
         }
     }
 }
@@ -515,12 +517,12 @@ namespace {
 template <bool kSwiGLU>
 hipError_t launch(const uint16_t *A, const int32_t *row_src, int gather_k, int a_rows, const uint16_t *W,
                   const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int K,
-                  int N, int I, int il, float clamp, uint16_t *C, int ldc, hipStream_t s) {
+                  int N, int I, int il, float clamp, uint16_t *C, int ldc, const int32_t *row_dst, hipStream_t s) {
     const int nb_n = (N + kBN - 1) / kBN;
     const TileMap tm = tile_map(nb_n);
     const int64_t blocks = (max_tiles + tm.gm - 1) / tm.gm * tm.per_band;
     hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kSwiGLU>, dim3(blocks), dim3(kThreads), 0, s, A, row_src, gather_k,
-                       a_rows, W, offsets, tiles, n_tiles, K, N, I, il, clamp, C, ldc);
+                       a_rows, W, offsets, tiles, n_tiles, K, N, I, il, clamp, C, ldc, row_dst);
     return hipGetLastError();
 }
 }  // namespace
@@ -529,7 +531,7 @@ hipError_t launch_gemm1_swiglu_bf16(const uint16_t *x_perm, const uint16_t *w1, 
                                     const int32_t *tiles, const int32_t *n_tiles, int64_t max_tiles, int H, int I,
                                     int glu_interleave, float clamp, uint16_t *h, hipStream_t s) {
     return launch<true>(x_perm, nullptr, 1, 0, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave,
-                        clamp, h, I, s);
+                        clamp, h, I, nullptr, s);
 }
 
 hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row_src, int T, int k,
@@ -538,13 +540,14 @@ hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row
                                            int glu_interleave, float clamp, uint16_t *h, hipStream_t s) {
     if (!gather_fits(T, H)) return hipErrorInvalidValue;
     return launch<true>(x, row_src, k, T, w1, offsets, tiles, n_tiles, max_tiles, H, 2 * I, I, glu_interleave, clamp,
-                        h, I, s);
+                        h, I, nullptr, s);
 }
 
 hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
-                             hipStream_t s) {
-    return launch<false>(h, nullptr, 1, 0, w2, offsets, tiles, n_tiles, max_tiles, I, H, I, 0, 0.0f, y_perm, H, s);
+                             const int32_t *row_dst, hipStream_t s) {
+    return launch<false>(h, nullptr, 1, 0, w2, offsets, tiles, n_tiles, max_tiles, I, H, I, 0, 0.0f, y_perm, H, row_dst,
+                         s);
 }
 
 }  // namespace tpg

@@ -146,6 +146,7 @@ struct W4Args {
     int64_t part_stride;  // with split: S * I (elements between the four partial-sum planes)
     uint16_t *Yout;      // GEMM2: y bf16 [S][ldy]
     int ldy;
+    const int32_t *row_dst;  // GEMM2: NULL, or [S]: row r of the tile order goes to y row row_dst[r]
 };
 
 // weights of one 256-wide K chunk as one lane loads them (line-coalesced): 16 code bytes of
@@ -159,6 +160,7 @@ struct WChunk {
 // Tile order of the multi-launch GEMMs: virtual blocks v0, v0 + stride, ... (the persistent
 // form), or v0 alone.  No waits and nothing to signal.
 struct StaticSched {
+    static constexpr bool kRowDst = true;  // GEMM2 honours W4Args::row_dst
     int v, stride, nb_n, n_mt;
     const int32_t *offsets, *tiles;
     bool merge;  // the tile list merges an expert's last partial tile of at most 32 rows
@@ -417,7 +419,9 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
             for (int tb = 0; tb < NTB; ++tb) {
                 const int tok = tb * 32 + (lane & 31);
                 if (tok >= t.rows) continue;
-                uint16_t *yrow = g.Yout + (int64_t)(t.row_begin + tok) * g.ldy;
+                const int yr = t.row_begin + tok;
+                const int32_t *row_dst = Sched::kRowDst ? g.row_dst : nullptr;
+                uint16_t *yrow = g.Yout + (int64_t)(row_dst ? row_dst[yr] : yr) * g.ldy;
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int c0 = w4::y_col(t.nt, wave, g4, lane);
@@ -796,6 +800,7 @@ struct FusedState {
 
 template <bool kG1>
 struct FusedSched {
+    static constexpr bool kRowDst = false;  // the single-launch forward keeps the expert order
     const FusedArgs &f;
     FusedState &st;
     int *word;  // workgroup-shared int
@@ -1129,7 +1134,8 @@ void set_layout(W4Args &g, int K, bool mx, int layout) {
 hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
                                    const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
                                    int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
-                                   uint8_t *h8, float *hs, uint16_t *y_perm, hipStream_t s) {
+                                   uint8_t *h8, float *hs, uint16_t *y_perm, const int32_t *row_dst,
+                                   hipStream_t s) {
     const int H = p.H, I = p.I;
     if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
     const int S = (int)n_slots(p);
@@ -1185,6 +1191,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     g2.E = p.E;
     g2.Yout = y_perm;
     g2.ldy = H;
+    g2.row_dst = row_dst;
     set_layout(g2, I, mx, w.w4_layout);
     launch_w4a8_gemm<false>(mx, l2, g2, offsets, tiles, n_tiles, s);
     return hipGetLastError();

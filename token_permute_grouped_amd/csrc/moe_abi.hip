@@ -34,7 +34,9 @@ int check_problem(const moe_problem *p) {
     if (p->prec != MOE_PREC_BF16 && (p->H % 256 != 0 || p->I % 256 != 0)) return MOE_ERR_SHAPE;
     if (p->glu_interleave != 0 && p->glu_interleave != 32) return MOE_ERR_UNSUPPORTED;
     if (!(p->swiglu_clamp >= 0.0f) || p->swiglu_clamp > 3.0e38f) return MOE_ERR_UNSUPPORTED;  // also rejects NaN
-    if (p->flags != 0 && p->flags != MOE_FLAG_SINGLE_LAUNCH) return MOE_ERR_UNSUPPORTED;
+    // one flag at a time (the single-launch kernel keeps the expert-order y rows)
+    if (p->flags != 0 && p->flags != MOE_FLAG_SINGLE_LAUNCH && p->flags != MOE_FLAG_SCATTER_Y)
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -132,13 +134,13 @@ int run_grouped_ffn(const void *x_perm, const float *x_perm_scale, const int32_t
         return hip_status(launch_grouped_ffn_w4a8((const uint8_t *)x_perm, x_perm_scale, nullptr, offsets, tiles,
                                                   n_tiles, max_tiles, w, p, (float *)(ws + L.h32),
                                                   (uint8_t *)(ws + L.h), (float *)(ws + L.h_scale),
-                                                  (uint16_t *)y_perm, s));
+                                                  (uint16_t *)y_perm, nullptr, s));
     uint16_t *h = (uint16_t *)(ws + L.h);
     st = hip_status(launch_gemm1_swiglu_bf16((const uint16_t *)x_perm, (const uint16_t *)w.w1, offsets, tiles,
                                              n_tiles, max_tiles, p.H, p.I, p.glu_interleave, p.swiglu_clamp, h, s));
     if (st) return st;
     return hip_status(launch_gemm2_bf16(h, (const uint16_t *)w.w2, offsets, tiles, n_tiles, max_tiles, p.H, p.I,
-                                        (uint16_t *)y_perm, s));
+                                        (uint16_t *)y_perm, nullptr, s));
 }
 
 int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,
@@ -206,6 +208,9 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         return st;
     if ((st = mark(2))) return st;
     const bool fused = fused_gather(*p);
+    // scatter epilogue: GEMM2 stores row r at its slot row_src[r], the combine reads slot order
+    const bool scatter = (p->flags & MOE_FLAG_SCATTER_Y) != 0;
+    const int32_t *row_dst = scatter ? row_src : nullptr;
     if (!fused && (st = hip_status(launch_permute(x, w4 ? x_scale : nullptr, slot_row, p->T, p->k, p->H, w4 ? 1 : 2,
                                                   x_perm, x_perm_scale, s))))
         return st;
@@ -216,7 +221,8 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         const float *as = fused ? x_scale : x_perm_scale;
         if ((st = hip_status(launch_grouped_ffn_w4a8(a8, as, fused ? row_src : nullptr, offsets, tiles, n_tiles,
                                                      max_tiles, *w, *p, (float *)(b + L.h32), (uint8_t *)(b + L.h),
-                                                     (float *)(b + L.h_scale), (uint16_t *)y_perm, s))))
+                                                     (float *)(b + L.h_scale), (uint16_t *)y_perm, row_dst,
+                                                     s))))
             return st;
         if ((st = mark(5))) return st;
     } else {
@@ -233,11 +239,11 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         if (st) return st;
         if ((st = mark(5))) return st;
         if ((st = hip_status(launch_gemm2_bf16(h, (const uint16_t *)w->w2, offsets, tiles, n_tiles, max_tiles, p->H,
-                                               p->I, (uint16_t *)y_perm, s))))
+                                               p->I, (uint16_t *)y_perm, row_dst, s))))
             return st;
     }
     if ((st = mark(6))) return st;
-    if ((st = hip_status(launch_combine((const uint16_t *)y_perm, slot_row, topk_w, p->T, p->k, p->H,
+    if ((st = hip_status(launch_combine((const uint16_t *)y_perm, slot_row, topk_w, p->T, p->k, p->H, scatter,
                                         (uint16_t *)out, s))))
         return st;
     return mark(7);
@@ -340,8 +346,8 @@ int moe_unpermute_combine(const void *y_perm, const int32_t *slot_row, const flo
     if (st) return st;
     if (p->T == 0) return MOE_OK;
     if (!y_perm || !slot_row || !topk_w || !out) return MOE_ERR_NULL;
-    return hip_status(launch_combine((const uint16_t *)y_perm, slot_row, topk_w, p->T, p->k, p->H, (uint16_t *)out,
-                                     stream));
+    return hip_status(launch_combine((const uint16_t *)y_perm, slot_row, topk_w, p->T, p->k, p->H, false,
+                                     (uint16_t *)out, stream));
 }
 
 int moe_forward(const float *logits, const uint8_t *slot_drop, const void *x, const float *x_scale,

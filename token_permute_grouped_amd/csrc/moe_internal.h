@@ -119,19 +119,25 @@ hipError_t launch_gemm1_swiglu_gather_bf16(const uint16_t *x, const int32_t *row
                                            const int32_t *n_tiles, int64_t max_tiles, int H, int I,
                                            int glu_interleave, float clamp, uint16_t *h, hipStream_t s);
 
+// row_dst NULL: y row r in the expert-major order; else y row row_dst[r] (the scatter epilogue:
+// row_src as row_dst puts every row at its slot t*k + j)
 hipError_t launch_gemm2_bf16(const uint16_t *h, const uint16_t *w2, const int32_t *offsets, const int32_t *tiles,
                              const int32_t *n_tiles, int64_t max_tiles, int H, int I, uint16_t *y_perm,
-                             hipStream_t s);
+                             const int32_t *row_dst, hipStream_t s);
 
 // row_src NULL: x_perm / x_perm_scale are the expert-ordered rows; else x / x_scale token rows
-// read through row_src (the gather fused into GEMM1; needs gather_fits_fp8(T, H))
+// read through row_src (the gather fused into GEMM1; needs gather_fits_fp8(T, H)).  row_dst as
+// for launch_gemm2_bf16.
 hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_scale, const int32_t *row_src,
                                    const int32_t *offsets, const int32_t *tiles, const int32_t *n_tiles,
                                    int64_t max_tiles, const moe_weights &w, const moe_problem &p, float *h32,
-                                   uint8_t *h8, float *hs, uint16_t *y_perm, hipStream_t s);
+                                   uint8_t *h8, float *hs, uint16_t *y_perm, const int32_t *row_dst,
+                                   hipStream_t s);
 
+// slot_order false: slot s = t*k + j reads y row slot_row[s]; true: y row s (the scatter
+// epilogue's layout).  Either way a slot with slot_row[s] < 0 is dropped.
 hipError_t launch_combine(const uint16_t *y_perm, const int32_t *slot_row, const float *topk_w, int T, int k, int H,
-                          uint16_t *out, hipStream_t s);
+                          bool slot_order, uint16_t *out, hipStream_t s);
 
 // The whole W4A8 forward in one launch (up to 256 tokens and 2048 slots, H and I multiples of
 // 1024, every byte offset below 2^31): routing, tables, both GEMMs with the SwiGLU and the
