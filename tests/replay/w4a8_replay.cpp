@@ -282,7 +282,7 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
 // range, its partial-sum stores [2 halves][gate, up][S][I] and the re-quantisation's reads of them
 static bool split_gemm1(const Problem &p) {
     const long long experts = p.E < (long long)p.T * p.k ? p.E : (long long)p.T * p.k;
-    return !p.mx && experts * (2LL * p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
+    return experts * (2LL * p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
 }
 static void replay_split(const Problem &p, const Routing &r) {
     const int S = p.T * p.k, nb_n = 2 * p.I / kBN, nc = p.H / kKC;

@@ -27,8 +27,9 @@ CASES = [
     MoeConfig("graph_w4a8_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8", swiglu_clamp=10.0),
     MoeConfig("graph_w4a8_mx_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
     MoeConfig("graph_w4a8_mx", T=64, H=512, I=256, E=8, k=2, prec="w4a8_mx", swiglu_clamp=10.0),
-    # one token, NVFP4: GEMM1 split in two K halves (partial sums added by the re-quantisation)
+    # one token: GEMM1 split in two K halves (partial sums added by the re-quantisation), both formats
     MoeConfig("graph_w4a8_t1_split", T=1, H=1024, I=1024, E=8, k=4, prec="w4a8", swiglu_clamp=10.0),
+    MoeConfig("graph_w4a8_mx_t1_split", T=1, H=1024, I=1024, E=8, k=4, prec="w4a8_mx", swiglu_clamp=10.0),
     # three-block (merged) m-tiles: every expert holds 65..85 rows
     MoeConfig("graph_w4a8_merged", T=200, H=512, I=512, E=5, k=2, prec="w4a8", glu_interleave=32, swiglu_clamp=10.0,
               drop_p=0.05),
@@ -42,7 +43,7 @@ def _eager(d: DeviceProblem):
     return bf16_host(d.forward())
 
 
-SINGLE = {"graph_w4a8_persistent", "graph_w4a8_mx_fused_t100", "graph_w4a8_t1_split"}  # also with MOE_FLAG_SINGLE_LAUNCH
+SINGLE = {"graph_w4a8_persistent", "graph_w4a8_mx_fused_t100", "graph_w4a8_t1_split", "graph_w4a8_mx_t1_split"}  # also with MOE_FLAG_SINGLE_LAUNCH
 
 
 @pytest.mark.parametrize("cfg,flags", [(c, 0) for c in CASES]

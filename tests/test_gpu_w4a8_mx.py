@@ -37,6 +37,10 @@ SMALL = {
     "mx_fused_t100_il_drop": MoeConfig("mx_fused_t100_il_drop", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8_mx",
                                        glu_interleave=32, swiglu_clamp=10.0, drop_p=0.1),
     "mx_fused_e256": MoeConfig("mx_fused_e256", T=40, H=1024, I=2048, E=256, k=8, prec="w4a8_mx", swiglu_clamp=10.0),
+    # one token, K a multiple of 512: GEMM1 split in two K halves (two workgroups per tile, partial
+    # sums added by the re-quantisation); interleaved W1 and a dropped slot
+    "mx_one_token_split": MoeConfig("mx_one_token_split", T=1, H=1024, I=1024, E=8, k=4, prec="w4a8_mx",
+                                    glu_interleave=32, swiglu_clamp=10.0, drop_p=0.25),
     # every expert 65..85 rows: one m-tile of three 32-row token blocks each
     "mx_merged_tiles": MoeConfig("mx_merged_tiles", T=200, H=512, I=512, E=5, k=2, prec="w4a8_mx",
                                  glu_interleave=32, swiglu_clamp=10.0, drop_p=0.05),
@@ -166,7 +170,7 @@ def test_scales_outside_the_fp8_decoder_range_stay_exact(lo, hi):
     assert err <= W4A8_BAR
 
 
-@pytest.mark.parametrize("case", ["mx_persistent_il_drop", "mx_fused_t100_il_drop", "mx_fused_e256"]
+@pytest.mark.parametrize("case", ["mx_persistent_il_drop", "mx_fused_t100_il_drop", "mx_fused_e256", "mx_one_token_split"]
                          + [f"T{T}" for T in w4a8_sweep_tokens()])
 def test_single_launch_forward_equals_default(case):
     """MOE_FLAG_SINGLE_LAUNCH with MXFP4 weights: bitwise the default multi-launch forward"""

@@ -15,10 +15,10 @@
 //   1. GEMM1 + clamped SwiGLU: h = silu(g) * u in fp32, g, u = gs1_e * sum_kb xs[kb] * (x8 . w8)
 //   2. re-quantisation of h per (row, 128 columns): s = amax/448 (1 if 0), q = e4m3(h / s)
 //   3. GEMM2: y = gs2_e * sum_kb hs[kb] * (h8 . w8), rounded to bf16
-// For NVFP4 at decode sizes (w4a8_split_gemm1) GEMM1 runs two workgroups per tile, one per K
-// half, writing raw partial sums, and launch 2 adds the halves and applies gs1 and the SwiGLU
-// first (requant_swiglu_fp8_kernel): a CU then holds two workgroups' waves, one of which
-// dequantises while the other waits on its loads.
+// At decode sizes (w4a8_split_gemm1) GEMM1 runs two workgroups per tile, one per K half,
+// writing raw partial sums, and launch 2 adds the halves and applies gs1 and the SwiGLU first
+// (requant_swiglu_fp8_kernel): a CU then holds two workgroups' waves, one of which computes
+// (NVFP4: dequantises) while the other waits on its loads, and twice the weight bytes in flight.
 //
 // The GEMMs stream packed weights, which is what bounds them at small token counts.
 // Tiling.  A workgroup (4 waves) owns one expert m-tile of up to 64 token rows (an
@@ -1091,7 +1091,7 @@ namespace {
 // steps (W4A8 layer, T = 16: 223 -> 214 us per forward).  Above 32 tokens a persistent
 // kernel would have to fix the token-block count for every tile (most tiles then hold under 32
 // rows at T = 64) and measured slower; there and for other K, one tile per workgroup (and
-// for NVFP4 at decode sizes, two per tile, see w4a8_split_gemm1).
+// at decode sizes, two per tile, see w4a8_split_gemm1).
 struct W4Launch {
     int64_t grid;
     bool persistent;
@@ -1288,9 +1288,10 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const bool one_block = p.T <= 32;  // every m-tile fits one 32-row token block
-    const bool halves = g1.split == 2;  // NVFP4 with T <= 32 only (one token block)
-    const void *fn = mx ? (one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
-                                     : (const void *)forward_small_w4a8_kernel<true, 2>)
+    const bool halves = g1.split == 2;  // T <= 32 only (one token block)
+    const void *fn = mx ? (halves ? (const void *)forward_small_w4a8_kernel<true, 1, true>
+                           : one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
+                                       : (const void *)forward_small_w4a8_kernel<true, 2>)
                         : (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true>
                            : one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
                                        : (const void *)forward_small_w4a8_kernel<false, 2>);
@@ -1298,7 +1299,9 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     if (err != hipSuccess) return err;
     const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
     if (mx) {
-        if (one_block)
+        if (halves)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1, true>), dim3(grid), dim3(kThreads), 0, s, f);
+        else if (one_block)
             hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, f);
         else
             hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 2>), dim3(grid), dim3(kThreads), 0, s, f);

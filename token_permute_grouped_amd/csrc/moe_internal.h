@@ -67,13 +67,14 @@ inline int64_t n_chunks(const moe_problem &p) { return (n_slots(p) + kChunk - 1)
 inline int gemm_bm(const moe_problem &p) { return p.prec == MOE_PREC_BF16 ? kGemmBM : kGemmBMW4A8; }
 // upper bound of sum_e ceil(count_e / bm) over any routing (also of the merged W4A8 tile count)
 inline int64_t max_m_tiles(const moe_problem &p) { return (n_slots(p) + gemm_bm(p) - 1) / gemm_bm(p) + p.E; }
-// W4A8 GEMM1 split in two halves of K (two workgroups per tile): NVFP4 weights, at most 256 GEMM1
-// tiles whatever the routing (each tile then streams its weights on a CU of its own, one wave per
-// SIMD, and the dequant goes unhidden), K a multiple of 512.  Deterministic: the halves' partial
-// sums are added by the re-quantisation (h32 holds the four partial planes: 4 x S x I floats).
+// W4A8 GEMM1 split in two halves of K (two workgroups per tile): at most 256 GEMM1 tiles whatever
+// the routing (each tile would otherwise stream its weights on a CU of its own, one wave per SIMD,
+// with the NVFP4 dequant unhidden and few bytes in flight), K a multiple of 512.  Deterministic:
+// the halves' partial sums are added by the re-quantisation (h32 holds the four partial planes:
+// 4 x S x I floats).
 inline bool w4a8_split_gemm1(const moe_problem &p) {
     const int64_t experts = std::min<int64_t>(p.E, (int64_t)p.T * p.k);
-    return p.prec == MOE_PREC_W4A8 && experts * (2 * (int64_t)p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
+    return p.prec != MOE_PREC_BF16 && experts * (2 * (int64_t)p.I / 128) <= 256 && p.H % 512 == 0 && p.T <= 32;
 }
 // tile list order (build_tile_list's by_expert): bf16 full tiles first; W4A8 by expert, an expert's
 // last partial tile of at most 32 rows merged into the tile before it (a 96-row tile at most)
