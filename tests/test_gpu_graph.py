@@ -46,9 +46,14 @@ def _eager(d: DeviceProblem):
 SINGLE = {"graph_w4a8_persistent", "graph_w4a8_mx_fused_t100", "graph_w4a8_t1_split", "graph_w4a8_mx_t1_split"}  # also with MOE_FLAG_SINGLE_LAUNCH
 
 
+SCATTER = {"graph_bf16_il_drop", "graph_w4a8_persistent", "graph_w4a8_merged"}  # also with MOE_FLAG_SCATTER_Y
+FLAG_IDS = {0: "default", tpg.MOE_FLAG_SINGLE_LAUNCH: "single_launch", tpg.MOE_FLAG_SCATTER_Y: "scatter_y"}
+
+
 @pytest.mark.parametrize("cfg,flags", [(c, 0) for c in CASES]
-                         + [(c, tpg.MOE_FLAG_SINGLE_LAUNCH) for c in CASES if c.name in SINGLE],
-                         ids=lambda v: v.name if isinstance(v, MoeConfig) else ("single_launch" if v else "default"))
+                         + [(c, tpg.MOE_FLAG_SINGLE_LAUNCH) for c in CASES if c.name in SINGLE]
+                         + [(c, tpg.MOE_FLAG_SCATTER_Y) for c in CASES if c.name in SCATTER],
+                         ids=lambda v: v.name if isinstance(v, MoeConfig) else FLAG_IDS[v])
 def test_forward_graph_replay(cfg, flags):
     print(f"[gpu graph] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec} flags={flags}",
           flush=True)

@@ -26,6 +26,8 @@ CASES = [
               drop_p=0.1),
     CONFIGS["w4a8"].with_tokens(4),  # also run with MOE_FLAG_SINGLE_LAUNCH below
 ]
+# flags of call i (the scatter epilogue on two calls, the single launch on the last)
+FLAGS = {1: tpg.MOE_FLAG_SCATTER_Y, 4: tpg.MOE_FLAG_SCATTER_Y, len(CASES) - 1: tpg.MOE_FLAG_SINGLE_LAUNCH}
 
 
 def _noalloc(d: DeviceProblem):
@@ -37,10 +39,10 @@ def _noalloc(d: DeviceProblem):
 
 def test_noalloc_forward_equals_forward_on_calls_in_a_row():
     for i, cfg in enumerate(CASES):
-        print(f"[no-alloc] call {i}: {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec}",
-              flush=True)
+        print(f"[no-alloc] call {i}: {cfg.name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec} "
+              f"flags={FLAGS.get(i, 0)}", flush=True)
         inp = generate(cfg, seed=i)
-        d = DeviceProblem(inp, tpg.MOE_FLAG_SINGLE_LAUNCH if i == len(CASES) - 1 else 0)
+        d = DeviceProblem(inp, FLAGS.get(i, 0))
         assert tpg.moe_workspace_bytes(d.p) <= tpg.MOE_NOALLOC_SCRATCH_BYTES
         a = bf16_host(_noalloc(d))
         b = bf16_host(d.forward())
