@@ -139,7 +139,8 @@ typedef struct moe_problem {
  * MOE_W4_LAYOUT_TILED, the same bytes regrouped by moe_w4a8_tile_weights so that
  * the GEMMs stream every 32-row, 256-wide piece as one contiguous run (the
  * FlashInfer Usage section likewise prepares weights once with a transform
- * function).  Both give bitwise the same results. */
+ * function), NVFP4 codes also reordered within each 4-byte group so that the
+ * in-kernel dequant yields K order directly.  Both give bitwise the same results. */
 enum { MOE_W4_LAYOUT_ROWS = 0, MOE_W4_LAYOUT_TILED = 1 };
 typedef struct moe_weights {
     const void *w1;
@@ -288,7 +289,10 @@ int moe_w4a8_dequant_table(uint8_t *out8, hipStream_t stream);
  * row r < 32,
  *   codes_tiled [e][b][c][r][0..127]    = codes [e][32 b + r][128 c .. 128 c + 127]
  *   bscale_tiled[e][b][c][r][0..256/bs) = bscale[e][32 b + r][(256/bs) c ..]
- * (the same array sizes).  Device pointers; the outputs must not overlap the inputs;
+ * (the same array sizes); for MOE_PREC_W4A8 each 4-byte group of codes_tiled, which holds
+ * the codes of 8 consecutive K positions k0..k0+7, stores k0 + i in the low nibble and
+ * k0 + 4 + i in the high nibble of its byte i (the row-major bytes hold k0 + 2i and
+ * k0 + 2i + 1).  MXFP4 codes keep the row-major packing.  Device pointers; the outputs must not overlap the inputs;
  * enqueued on `stream`.  Call it once per matrix (W1: N = 2I, K = H; W2: N = H, K =
  * I) when the weights are loaded. */
 int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled,

@@ -1,9 +1,10 @@
 """GPU checks of the tiled W4A8 weight layout (MOE_W4_LAYOUT_TILED).
 
 moe_w4a8_tile_weights must regroup the bytes exactly as include/moe.h defines (compared
-with a numpy regrouping of the same arrays, bit for bit), and a forward or grouped FFN on
-tiled weights must give bitwise the output of the same call on row-major weights (the
-GEMMs see the same values in the same order; only their addresses change).
+with a numpy regrouping of the same arrays, bit for bit, NVFP4 nibbles included), and a
+forward or grouped FFN on tiled weights must give bitwise the output of the same call on
+row-major weights (the GEMMs see the same values in the same order; only their addresses,
+and for NVFP4 the dequant's path to K order, change).
 """
 from __future__ import annotations
 
@@ -18,13 +19,25 @@ from tests._gpu import DEV, DeviceProblem, bf16_host, to_dev
 pytestmark = pytest.mark.gpu
 
 
+def split_nibbles_host(codes: np.ndarray) -> np.ndarray:
+    """NVFP4 codes of every 4-byte group (byte i = codes 2i, 2i + 1, low nibble first) regrouped so
+    that byte i holds codes i (low nibble) and i + 4 (high nibble)"""
+    g = codes.reshape(-1, 4)
+    k = np.stack([g & 15, g >> 4], axis=-1).reshape(-1, 8)  # the eight codes in K order
+    return (k[:, :4] | (k[:, 4:] << 4)).astype(np.uint8).reshape(codes.shape)
+
+
 def tile_host(codes: np.ndarray, bscale: np.ndarray, bs: int):
-    """the layout's definition: [e][b][c][r][bytes] from row-major [e][32 b + r][bytes of piece c]"""
+    """the layout's definition: [e][b][c][r][bytes] from row-major [e][32 b + r][bytes of piece c],
+    NVFP4 codes (bs = 16) with their nibbles regrouped per 4-byte group"""
     E, N, Kh = codes.shape
     nc = Kh // 128
     c = codes.reshape(E, N // 32, 32, nc, 128).transpose(0, 1, 3, 2, 4)
     s = bscale.reshape(E, N // 32, 32, nc, 256 // bs).transpose(0, 1, 3, 2, 4)
-    return np.ascontiguousarray(c).reshape(codes.shape), np.ascontiguousarray(s).reshape(bscale.shape)
+    c = np.ascontiguousarray(c).reshape(codes.shape)
+    if bs == 16:
+        c = split_nibbles_host(c)
+    return c, np.ascontiguousarray(s).reshape(bscale.shape)
 
 
 def tile_device(codes: torch.Tensor, bscale: torch.Tensor, prec: int):
@@ -59,6 +72,12 @@ CASES = {
                                glu_interleave=32, swiglu_clamp=10.0),
     "mx_persistent": MoeConfig("mx_persistent", T=16, H=1024, I=1024, E=32, k=8, prec="w4a8_mx",
                                swiglu_clamp=10.0),
+    # one token: GEMM1 in two K halves (the dequant of the tiled nibble order in the split form)
+    "nv_one_token_split": MoeConfig("nv_one_token_split", T=1, H=1024, I=1024, E=8, k=4, prec="w4a8",
+                                    glu_interleave=32, swiglu_clamp=10.0, drop_p=0.25),
+    # two token blocks per tile in the single-launch forward
+    "nv_fused_t100": MoeConfig("nv_fused_t100", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8", swiglu_clamp=10.0,
+                               drop_p=0.1),
 }
 
 
@@ -99,3 +118,16 @@ def test_full_layer_forward_on_tiled_weights_equals_row_major(wl, T):
     a, b = bf16_host(rows.forward()), bf16_host(tiled.forward())
     torch.cuda.synchronize()
     assert (a == b).all()
+
+
+@pytest.mark.parametrize("name", ["nv_persistent", "nv_one_token_split", "nv_fused_t100", "mx_persistent"])
+def test_single_launch_forward_on_tiled_weights_equals_row_major(name):
+    """the single-launch kernel on tiled weights (for NVFP4 its dequant of the tiled nibble order, in
+    the one-block, two-block and K-halves forms) against the default forward on row-major weights"""
+    cfg = CASES[name]
+    print(f"[gpu w4 layout] single launch {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} {cfg.prec}",
+          flush=True)
+    inp = generate(cfg, seed=0)
+    rows, tiled = DeviceProblem(inp), _tiled_problem(inp)
+    tiled.p.flags = tpg.MOE_FLAG_SINGLE_LAUNCH
+    assert (bf16_host(rows.forward()) == bf16_host(tiled.forward())).all()

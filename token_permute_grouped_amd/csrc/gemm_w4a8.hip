@@ -99,14 +99,18 @@ __device__ __forceinline__ u32x2 scaled_e2m1_table(uint32_t sc) {
     return t;
 }
 
-// eight e2m1 codes (low nibble first) -> eight e4m3 codes, through the table t of their
-// block scale.  v_perm_b32 selector bytes 0..3 pick bytes of the second source, 4..7 of
-// the first.
+// eight e2m1 codes -> eight e4m3 codes, through the table t of their block scale.  kSplit
+// false: the codes are packed low nibble first (byte i holds codes 2i and 2i + 1); true: the
+// tiled layout's NVFP4 order (byte i holds codes i and i + 4), whose low and high nibbles
+// already give the outputs in K order.  v_perm_b32 selector bytes 0..3 pick bytes of the
+// second source, 4..7 of the first.
+template <bool kSplit = false>
 __device__ __forceinline__ u32x2 dequant8(uint32_t x, u32x2 t) {
-    const uint32_t me = __builtin_amdgcn_perm(t.y, t.x, x & 0x07070707u);         // codes 0, 2, 4, 6
-    const uint32_t mo = __builtin_amdgcn_perm(t.y, t.x, (x >> 4) & 0x07070707u);  // codes 1, 3, 5, 7
+    const uint32_t me = __builtin_amdgcn_perm(t.y, t.x, x & 0x07070707u);         // low nibbles
+    const uint32_t mo = __builtin_amdgcn_perm(t.y, t.x, (x >> 4) & 0x07070707u);  // high nibbles
     const uint32_t ve = me ^ ((x << 4) & 0x80808080u);
     const uint32_t vo = mo ^ (x & 0x80808080u);
+    if constexpr (kSplit) return u32x2{ve, vo};
     return u32x2{__builtin_amdgcn_perm(vo, ve, 0x05010400u), __builtin_amdgcn_perm(vo, ve, 0x07030602u)};
 }
 
@@ -188,7 +192,7 @@ struct StaticSched {
 // tile pays for a prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at
 // the same register set and buffer phase).  sc.before_act(t) runs (uniformly, in every thread)
 // before the first activation load of tile t, sc.after_tile(t) after t's output is written.
-template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched, int kSplit = 0>
+template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched, int kSplit = 0, bool kNib = false>
 __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned char *act, float *xsl,
                                            unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -342,8 +346,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                 } else {
                     const uint32_t sc = sq >> (16 * t);
                     const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
-                    const u32x2 d0 = dequant8(cw.x, t0), d1 = dequant8(cw.y, t0);
-                    const u32x2 d2 = dequant8(cw.z, t1), d3 = dequant8(cw.w, t1);
+                    const u32x2 d0 = dequant8<kNib>(cw.x, t0), d1 = dequant8<kNib>(cw.y, t0);
+                    const u32x2 d2 = dequant8<kNib>(cw.z, t1), d3 = dequant8<kNib>(cw.w, t1);
                     wa = i32x8{(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y, (int)d2.x, (int)d2.y, (int)d3.x, (int)d3.y};
                 }
                 // activation granules (16 K each) of this lane's 32 fp8 bytes.  Both operands fp8: one
@@ -550,8 +554,9 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * kWSlot]; /* one slot per wave */ \
     if constexpr (!kMX) lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after a tile's first barrier */
 
-// one tile per workgroup; its token-block count (1 to 3) from its own rows
-template <bool kSwiGLU, bool kMX>
+// one tile per workgroup; its token-block count (1 to 3) from its own rows.  kNib: NVFP4 codes in
+// the tiled layout's nibble order
+template <bool kSwiGLU, bool kMX, bool kNib>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
@@ -561,23 +566,23 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
     const Tile t = sc.first();
     if (!t.valid) return;
     if (kSwiGLU && g.split == 1)  // decode sizes: rows of at most 32
-        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, kSwiGLU ? 1 : 0>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, kSwiGLU ? 1 : 0, kNib>(g, sc, act, xsl, wlds, lut);
     else if (t.rows > 2 * 32)
-        w4a8_tiles<kSwiGLU, kMX, 3, false>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 3, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
     else if (t.rows > 32)
-        w4a8_tiles<kSwiGLU, kMX, 2, false>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 2, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
     else
-        w4a8_tiles<kSwiGLU, kMX, 1, false>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
 }
 
 // persistent (at most 32 rows per tile): workgroup b takes virtual blocks b, b + gridDim.x, ...
-template <bool kSwiGLU, bool kMX>
+template <bool kSwiGLU, bool kMX, bool kNib>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kernel(
     W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
     StaticSched sc{(int)blockIdx.x, (int)gridDim.x, g.N / kBN, n_tiles[0], offsets, tiles, true};
-    w4a8_tiles<kSwiGLU, kMX, 1, true>(g, sc, act, xsl, wlds, lut);
+    w4a8_tiles<kSwiGLU, kMX, 1, true, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
 }
 
 // ---------------------------------------------------------------- single-launch small-token forward
@@ -922,7 +927,7 @@ __device__ void fused_combine(const FusedArgs &f, int *rows_s, float *w_s) {
     }
 }
 
-template <bool kMX, int NTB, bool kHalves = false>
+template <bool kMX, int NTB, bool kHalves = false, bool kNib = false>
 __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedArgs f) {
     TPG_W4A8_LDS
     __shared__ int word, n_mt_s;
@@ -977,11 +982,11 @@ __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedAr
     const int n1 = n_mt * (2 * f.I / kBN), n2 = n_mt * (f.H / kBN);
     {
         FusedSched<true> sc{f, st, &word, n_mt, n1, n2};
-        w4a8_tiles<true, kMX, NTB, true, FusedSched<true>, kHalves ? 2 : 0>(f.g1, sc, act, xsl, wlds, lut);
+        w4a8_tiles<true, kMX, NTB, true, FusedSched<true>, kHalves ? 2 : 0, kNib>(f.g1, sc, act, xsl, wlds, lut);
     }
     {
         FusedSched<false> sc{f, st, &word, n_mt, n1, n2};
-        w4a8_tiles<false, kMX, NTB, true>(f.g2, sc, act, xsl, wlds, lut);
+        w4a8_tiles<false, kMX, NTB, true, FusedSched<false>, 0, kNib>(f.g2, sc, act, xsl, wlds, lut);
     }
     // every workgroup's GEMM2 rows are written before any combine reads them
     publish_and_count(&sy->gemm_done, &word);
@@ -1109,23 +1114,26 @@ W4Launch w4_launch(int64_t max_tiles, int N, int K, int E, int a_rows, int T) {
     return {std::min<int64_t>(blocks, 2 * (int64_t)n_cu), true};
 }
 
-template <bool kSwiGLU, bool kMX>
+template <bool kSwiGLU, bool kMX, bool kNib>
 void launch_w4a8_gemm_as(const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
                          const int32_t *n_tiles, hipStream_t s) {
     if (l.persistent)
-        hipLaunchKernelGGL((grouped_gemm_w4a8_persistent_kernel<kSwiGLU, kMX>), dim3(l.grid), dim3(kThreads), 0, s, g,
+        hipLaunchKernelGGL((grouped_gemm_w4a8_persistent_kernel<kSwiGLU, kMX, kNib>), dim3(l.grid), dim3(kThreads), 0,
+                           s, g, offsets, tiles, n_tiles);
+    else
+        hipLaunchKernelGGL((grouped_gemm_w4a8_kernel<kSwiGLU, kMX, kNib>), dim3(l.grid), dim3(kThreads), 0, s, g,
                            offsets, tiles, n_tiles);
-    else
-        hipLaunchKernelGGL((grouped_gemm_w4a8_kernel<kSwiGLU, kMX>), dim3(l.grid), dim3(kThreads), 0, s, g, offsets,
-                           tiles, n_tiles);
 }
+// nib: NVFP4 codes in the tiled layout's nibble order (never with MXFP4)
 template <bool kSwiGLU>
-void launch_w4a8_gemm(bool mx, const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
-                      const int32_t *n_tiles, hipStream_t s) {
+void launch_w4a8_gemm(bool mx, bool nib, const W4Launch &l, const W4Args &g, const int32_t *offsets,
+                      const int32_t *tiles, const int32_t *n_tiles, hipStream_t s) {
     if (mx)
-        launch_w4a8_gemm_as<kSwiGLU, true>(l, g, offsets, tiles, n_tiles, s);
+        launch_w4a8_gemm_as<kSwiGLU, true, false>(l, g, offsets, tiles, n_tiles, s);
+    else if (nib)
+        launch_w4a8_gemm_as<kSwiGLU, false, true>(l, g, offsets, tiles, n_tiles, s);
     else
-        launch_w4a8_gemm_as<kSwiGLU, false>(l, g, offsets, tiles, n_tiles, s);
+        launch_w4a8_gemm_as<kSwiGLU, false, false>(l, g, offsets, tiles, n_tiles, s);
 }
 }  // namespace
 
@@ -1150,6 +1158,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
     const int S = (int)n_slots(p);
     const bool mx = p.prec == MOE_PREC_W4A8_MX;
+    const bool nib = !mx && w.w4_layout == MOE_W4_LAYOUT_TILED;  // NVFP4 codes in the tiled nibble order
     const W4Launch l1 = w4_launch(max_tiles, 2 * I, H, p.E, row_src ? p.T : S, p.T),
                    l2 = w4_launch(max_tiles, H, I, p.E, S, p.T);
     W4Args g1{};
@@ -1173,9 +1182,10 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     if (split) {  // two workgroups per tile, one per K half, one tile each (rows of at most 32)
         g1.split = 1;
         g1.part_stride = (int64_t)S * I;
-        launch_w4a8_gemm<true>(mx, W4Launch{2 * max_tiles * (2 * I / kBN), false}, g1, offsets, tiles, n_tiles, s);
+        launch_w4a8_gemm<true>(mx, nib, W4Launch{2 * max_tiles * (2 * I / kBN), false}, g1, offsets, tiles, n_tiles,
+                               s);
     } else {
-        launch_w4a8_gemm<true>(mx, l1, g1, offsets, tiles, n_tiles, s);
+        launch_w4a8_gemm<true>(mx, nib, l1, g1, offsets, tiles, n_tiles, s);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1203,7 +1213,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     g2.ldy = H;
     g2.row_dst = row_dst;
     set_layout(g2, I, mx, w.w4_layout);
-    launch_w4a8_gemm<false>(mx, l2, g2, offsets, tiles, n_tiles, s);
+    launch_w4a8_gemm<false>(mx, nib, l2, g2, offsets, tiles, n_tiles, s);
     return hipGetLastError();
 }
 
@@ -1222,6 +1232,7 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
                                      uint16_t *out, hipStream_t s) {
     if (!forward_small_w4a8_fits(p)) return hipErrorInvalidValue;
     const bool mx = p.prec == MOE_PREC_W4A8_MX;
+    const bool nib = !mx && w.w4_layout == MOE_W4_LAYOUT_TILED;  // NVFP4 codes in the tiled nibble order
     const int S = (int)n_slots(p);
     FusedArgs f{};
     f.logits = logits;
@@ -1292,9 +1303,12 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     const void *fn = mx ? (halves ? (const void *)forward_small_w4a8_kernel<true, 1, true>
                            : one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
                                        : (const void *)forward_small_w4a8_kernel<true, 2>)
-                        : (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true>
-                           : one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
-                                       : (const void *)forward_small_w4a8_kernel<false, 2>);
+                   : nib ? (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true, true>
+                            : one_block ? (const void *)forward_small_w4a8_kernel<false, 1, false, true>
+                                        : (const void *)forward_small_w4a8_kernel<false, 2, false, true>)
+                         : (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true>
+                            : one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
+                                        : (const void *)forward_small_w4a8_kernel<false, 2>);
     err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
     if (err != hipSuccess) return err;
     const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
@@ -1305,6 +1319,13 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
             hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, f);
         else
             hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 2>), dim3(grid), dim3(kThreads), 0, s, f);
+    } else if (nib) {
+        if (halves)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, true, true>), dim3(grid), dim3(kThreads), 0, s, f);
+        else if (one_block)
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, false, true>), dim3(grid), dim3(kThreads), 0, s, f);
+        else
+            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 2, false, true>), dim3(grid), dim3(kThreads), 0, s, f);
     } else {
         if (halves)
             hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, true>), dim3(grid), dim3(kThreads), 0, s, f);
@@ -1316,12 +1337,22 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     return hipGetLastError();
 }
 
+// NVFP4 codes in the tiled layout: the eight codes of a dword, packed low nibble first (byte i
+// holds codes 2i and 2i + 1), regrouped so that byte i holds codes i and i + 4; the dequant then
+// yields its fp8 bytes in K order without an interleave
+__device__ __forceinline__ uint32_t split_nibbles(uint32_t x) {
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 0, 2, 4, 6 / 1, 3, 5, 7
+    const uint32_t first = __builtin_amdgcn_perm(hi, lo, 0x05010400u);   // codes 0, 1, 2, 3
+    const uint32_t second = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4, 5, 6, 7
+    return first | (second << 4);
+}
+
 // MOE_W4_LAYOUT_TILED from row-major codes and block scales: one thread per destination unit
 // (16 code bytes, or 8 scale bytes); destination unit d of a 32-row block's 256-wide piece c
-// holds row r, bytes 16 j (8 j) of that row's piece
+// holds row r, bytes 16 j (8 j) of that row's piece (NVFP4 codes with split_nibbles applied)
 __global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
                                                            int64_t units, int unit_bytes, int piece_units,
-                                                           int row_bytes, int n_pieces) {
+                                                           int row_bytes, int n_pieces, bool split) {
     const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (d >= units) return;
     const int j = (int)(d % piece_units);
@@ -1329,9 +1360,11 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t *__rest
     const int64_t c = (d / (piece_units * 32)) % n_pieces;
     const int64_t blk = d / ((int64_t)piece_units * 32 * n_pieces);  // expert * (N / 32) + block
     const int64_t from = (blk * 32 + r) * row_bytes + c * (piece_units * unit_bytes) + j * unit_bytes;
-    if (unit_bytes == 16)
-        *(uint4 *)(dst + d * 16) = *(const uint4 *)(src + from);
-    else
+    if (unit_bytes == 16) {
+        uint4 v = *(const uint4 *)(src + from);
+        if (split) v = make_uint4(split_nibbles(v.x), split_nibbles(v.y), split_nibbles(v.z), split_nibbles(v.w));
+        *(uint4 *)(dst + d * 16) = v;
+    } else
         *(uint2 *)(dst + d * 8) = *(const uint2 *)(src + from);
 }
 
@@ -1342,11 +1375,11 @@ hipError_t launch_tile_weights(const uint8_t *codes, const uint8_t *bscale, uint
     const int64_t cu = rows * (K / 2) / 16;      // 16-byte code units
     const int64_t su = rows * (K / sb) / 8;      // 8-byte scale units
     hipLaunchKernelGGL(tile_weights_kernel, dim3((cu + 255) / 256), dim3(256), 0, s, codes, codes_tiled, cu, 16,
-                       (kKC / 2) / 16, K / 2, n_pieces);
+                       (kKC / 2) / 16, K / 2, n_pieces, !mx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(tile_weights_kernel, dim3((su + 255) / 256), dim3(256), 0, s, bscale, bscale_tiled, su, 8,
-                       (kKC / sb) / 8, K / sb, n_pieces);
+                       (kKC / sb) / 8, K / sb, n_pieces, false);
     return hipGetLastError();
 }
 
