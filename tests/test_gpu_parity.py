@@ -304,3 +304,28 @@ def test_zero_tokens_is_a_no_op():
     tpg.moe_unpermute_combine(None, None, None, p, out)
     torch.cuda.synchronize()
     assert (out.cpu() == 7).all()
+
+
+def test_forward_at_the_gather_offset_limit():
+    """T*H*2 = 2^31 bytes of x: the rows no longer fit one buffer descriptor's 31-bit offsets, so the
+    forward gathers them with the separate permute kernel instead of inside GEMM1; sampled tokens
+    against the oracle, every token row written, and bitwise the step-by-step entry points"""
+    cfg = MoeConfig("gather_limit", T=32768, H=32768, I=128, E=2, k=1)
+    print(f"[gpu parity] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    inp = generate(cfg, seed=7)
+    d = DeviceProblem(inp)
+    out_dev = d.forward()
+    tokens = np.unique(np.concatenate([np.random.default_rng(7).integers(0, cfg.T, 14), [0, cfg.T - 1]]))
+    ref = oracle.moe_forward(inp, tokens)
+    out = bf16_host(out_dev)
+    err = rel_err(bf16_f64(out[tokens]), ref)
+    print(f"[gpu parity] {cfg.name}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}", flush=True)
+    assert err <= BF16_BAR
+    assert_all_rows_written(out_dev, cfg.T, float(np.abs(ref).max()), f"{cfg.name} forward out")
+    del out_dev
+    idx, w = d.route()
+    offsets, row_src, slot_row, x_perm, _ = d.permute(idx)
+    y = d.grouped_ffn(x_perm, None, offsets)
+    del x_perm
+    steps = bf16_host(d.combine(y, slot_row, w))
+    assert (steps == out).all()

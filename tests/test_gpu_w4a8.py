@@ -248,3 +248,28 @@ def test_forward_deterministic_and_workspace_reuse():
     c = bf16_host(d.forward())
     assert (a == b).all() and (a == c).all()
 
+
+
+def test_forward_at_the_gather_offset_limit():
+    """T*H = 2^31 fp8 bytes of x: the forward gathers the rows and their scales with the separate
+    permute kernel instead of inside GEMM1; sampled tokens against the oracle, every token row
+    written, and bitwise the step-by-step entry points"""
+    cfg = MoeConfig("w4_gather_limit", T=65536, H=32768, I=256, E=2, k=1, prec="w4a8", swiglu_clamp=10.0)
+    print(f"[gpu w4a8] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    inp = generate(cfg, seed=7)
+    d = DeviceProblem(inp)
+    out_dev = d.forward()
+    tokens = np.unique(np.concatenate([np.random.default_rng(7).integers(0, cfg.T, 14), [0, cfg.T - 1]]))
+    ref = oracle.moe_forward(inp, tokens)
+    out = bf16_host(out_dev)
+    err = rel_err(bf16_f64(out[tokens]), ref)
+    print(f"[gpu w4a8] {cfg.name}: forward on {tokens.size} tokens, max|err|/max|ref| = {err:.3e}", flush=True)
+    assert err <= W4A8_BAR
+    assert_all_rows_written(out_dev, cfg.T, float(np.abs(ref).max()), f"{cfg.name} forward out")
+    del out_dev
+    idx, w = d.route()
+    offsets, row_src, slot_row, x_perm, x_perm_scale = d.permute(idx)
+    y = d.grouped_ffn(x_perm, x_perm_scale, offsets)
+    del x_perm
+    steps = bf16_host(d.combine(y, slot_row, w))
+    assert (steps == out).all()
