@@ -447,7 +447,7 @@ int main() {
     const int small[][5] = {{64, 256, 256, 8, 2}, {1, 256, 256, 4, 4}, {100, 512, 512, 6, 3}, {300, 768, 768, 5, 2},
                             {90, 512, 256, 4, 2}, {32, 1024, 1024, 64, 8}, {30, 512, 512, 6, 3}, {16, 1024, 1024, 32, 8},
                             {1, 1024, 512, 8, 4}, {2, 1024, 1024, 4, 2}, {200, 512, 512, 5, 2}, {96, 512, 256, 4, 4},
-                            {97, 512, 256, 4, 4}};
+                            {97, 512, 256, 4, 4}, {16, 65536, 1024, 4, 2}, {65536, 32768, 256, 2, 1}};
     for (auto &c : small)
         for (bool mx : {false, true}) probs.push_back({c[0], c[1], c[2], c[3], c[4], mx, false});
     // random shapes: E up to 256, k up to 32, up to 2048 slots, H, I multiples of 1024

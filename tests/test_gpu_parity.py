@@ -329,3 +329,18 @@ def test_forward_at_the_gather_offset_limit():
     del x_perm
     steps = bf16_host(d.combine(y, slot_row, w))
     assert (steps == out).all()
+
+
+def test_forward_at_the_largest_hidden_size():
+    """H = 65536, the largest the boundary accepts: 1024 K stages in GEMM1 and 256 n-tiles in GEMM2;
+    every token against the oracle and every token row written"""
+    cfg = MoeConfig("max_h", T=64, H=65536, I=1024, E=2, k=2)
+    print(f"[gpu parity] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    inp = generate(cfg, seed=8)
+    d = DeviceProblem(inp)
+    out_dev = d.forward()
+    ref = oracle.moe_forward(inp)
+    err = rel_err(bf16_f64(bf16_host(out_dev)), ref)
+    print(f"[gpu parity] {cfg.name}: forward, max|err|/max|ref| = {err:.3e}", flush=True)
+    assert err <= BF16_BAR
+    assert_all_rows_written(out_dev, cfg.T, float(np.abs(ref).max()), f"{cfg.name} forward out")

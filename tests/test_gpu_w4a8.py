@@ -273,3 +273,19 @@ def test_forward_at_the_gather_offset_limit():
     del x_perm
     steps = bf16_host(d.combine(y, slot_row, w))
     assert (steps == out).all()
+
+
+@pytest.mark.parametrize("prec", ["w4a8", "w4a8_mx"])
+def test_forward_at_the_largest_hidden_size(prec):
+    """H = 65536, the largest the boundary accepts: 256 K chunks in GEMM1 (the persistent form: sixteen tokens,
+    so every tile holds one token block) and 512 n-tiles in GEMM2; every token against the oracle and every token row written"""
+    cfg = MoeConfig(f"{prec}_max_h", T=16, H=65536, I=1024, E=4, k=2, prec=prec, swiglu_clamp=10.0)
+    print(f"[gpu w4a8] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}", flush=True)
+    inp = generate(cfg, seed=8)
+    d = DeviceProblem(inp)
+    out_dev = d.forward()
+    ref = oracle.moe_forward(inp)
+    err = rel_err(bf16_f64(bf16_host(out_dev)), ref)
+    print(f"[gpu w4a8] {cfg.name}: forward, max|err|/max|ref| = {err:.3e}", flush=True)
+    assert err <= W4A8_BAR
+    assert_all_rows_written(out_dev, cfg.T, float(np.abs(ref).max()), f"{cfg.name} forward out")
