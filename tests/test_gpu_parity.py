@@ -39,6 +39,7 @@ SMALL_CASES = {
     "clamped": MoeConfig("clamped", T=150, H=384, I=256, E=8, k=3, swiglu_clamp=1.0),
     "ragged_tiles": MoeConfig("ragged_tiles", T=700, H=256, I=640, E=5, k=2),
     "wide_k": MoeConfig("wide_k", T=40, H=128, I=128, E=128, k=64),          # k above 32: 16 slots per lane
+    "all_experts": MoeConfig("all_experts", T=8, H=128, I=128, E=256, k=256),  # k = E = 256: every expert, 8 rows each
 }
 FULL = ["mid", "skewed", "ep_share"]
 
