@@ -47,7 +47,10 @@
 // e4m3 codes of the eight e2m1 magnitudes times that scale (rounded to nearest even,
 // saturating at +-448; the products are exact in fp32).  Eight packed codes (one
 // dword, low nibble first) then become eight e4m3 bytes with two v_perm_b32 table
-// selects, a sign xor and two v_perm_b32 interleaves.
+// selects, a sign xor and two v_perm_b32 interleaves; in the tiled layout the codes
+// of a dword are stored so that the table selects already give K order (no
+// interleave).  Weight loads are non-temporal: a call reads each weight byte about
+// once.
 //
 // Operand layout of v_mfma_*_32x32x64_f8f6f4 (checked on the device): lane l holds
 // row l % 32 and the 32 consecutive K bytes starting at 32 * (l / 32); the output
