@@ -233,6 +233,14 @@ def test_forward_matches_oracle(name):
     MoeConfig("front_t256", T=256, H=128, I=128, E=64, k=4),             # 256 tokens: four passes
     MoeConfig("front_t100_odd", T=100, H=128, I=256, E=12, k=3),         # last pass partly empty
     MoeConfig("front_wide_k", T=8, H=128, I=128, E=256, k=100, drop_p=0.1),  # k above 32 in the front end
+    # just past the bound (1024 slots): the separate launches, two table chunks
+    MoeConfig("front_1025", T=205, H=128, I=128, E=16, k=5),              # one slot in the second chunk
+    MoeConfig("front_1500_drop", T=250, H=128, I=256, E=12, k=6, drop_p=0.1),
+    MoeConfig("front_2048", T=256, H=128, I=128, E=32, k=8),
+    MoeConfig("front_k16", T=128, H=256, I=128, E=64, k=16, glu_interleave=32),
+    MoeConfig("front_2050", T=205, H=128, I=128, E=16, k=10),
+    MoeConfig("front_w4_2048", T=256, H=512, I=512, E=32, k=8, prec="w4a8", swiglu_clamp=10.0, drop_p=0.02),
+    MoeConfig("front_mx_1536", T=192, H=512, I=512, E=16, k=8, prec="w4a8_mx"),
 ], ids=lambda c: c.name)
 def test_forward_small_front_end_matches_separate_steps(cfg):
     """up to 1024 slots and 256 tokens the forward routes, builds the tables and the tile

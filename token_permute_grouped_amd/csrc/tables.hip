@@ -262,6 +262,7 @@ hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, 
                                  int by_expert, int32_t *topk_idx, float *topk_w, int32_t *offsets,
                                  int32_t *row_src, int32_t *slot_row, int32_t *tiles, int32_t *n_tiles,
                                  hipStream_t s) {
+    if (T > 256 || (int64_t)T * k > kChunk) return hipErrorInvalidValue;  // the LDS tables' sizes
     hipLaunchKernelGGL(frontend_small_kernel, dim3(1), dim3(kChunk), 0, s, logits, slot_drop, T, E, k, bm, by_expert,
                        topk_idx, topk_w, offsets, row_src, slot_row, tiles, n_tiles);
     return hipGetLastError();
