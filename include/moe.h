@@ -137,10 +137,11 @@ typedef struct moe_problem {
  * w4_layout (W4A8 and W4A8_MX only) says how the codes and block scales of each
  * matrix are stored: MOE_W4_LAYOUT_ROWS, the row-major arrays above, or
  * MOE_W4_LAYOUT_TILED, the same bytes regrouped by moe_w4a8_tile_weights so that
- * the GEMMs stream every 32-row, 256-wide piece as one contiguous run (the
- * FlashInfer Usage section likewise prepares weights once with a transform
- * function), NVFP4 codes also reordered within each 4-byte group so that the
- * in-kernel dequant yields K order directly.  Both give bitwise the same results. */
+ * the GEMMs stream every 32-row, 256-wide piece as one contiguous run already in their
+ * matrix instructions' operand order (the FlashInfer Usage section likewise prepares
+ * weights once with a transform function), NVFP4 codes also reordered within each 4-byte
+ * group so that the in-kernel dequant yields K order directly.  Both give bitwise the same
+ * results. */
 enum { MOE_W4_LAYOUT_ROWS = 0, MOE_W4_LAYOUT_TILED = 1 };
 typedef struct moe_weights {
     const void *w1;
@@ -285,14 +286,18 @@ int moe_w4a8_dequant_table(uint8_t *out8, hipStream_t stream);
 /* W4A8 weight preparation: one matrix stack of E experts with N rows and K columns
  * (N a multiple of 32, K of 256), row-major codes uint8 [E][N][K/2] and block scales
  * uint8 [E][N][K/bs] (bs = 16 for MOE_PREC_W4A8, 32 for MOE_PREC_W4A8_MX), rewritten
- * into MOE_W4_LAYOUT_TILED: for every expert e, 32-row block b, 256-wide K piece c and
- * row r < 32,
- *   codes_tiled [e][b][c][r][0..127]    = codes [e][32 b + r][128 c .. 128 c + 127]
- *   bscale_tiled[e][b][c][r][0..256/bs) = bscale[e][32 b + r][(256/bs) c ..]
- * (the same array sizes); for MOE_PREC_W4A8 each 4-byte group of codes_tiled, which holds
- * the codes of 8 consecutive K positions k0..k0+7, stores k0 + i in the low nibble and
- * k0 + 4 + i in the high nibble of its byte i (the row-major bytes hold k0 + 2i and
- * k0 + 2i + 1).  MXFP4 codes keep the row-major packing.  Device pointers; the outputs must not overlap the inputs;
+ * into MOE_W4_LAYOUT_TILED: every expert e's 32-row block b and 256-wide K piece c is one
+ * contiguous run (4096 code bytes at codes_tiled + ((e N/32 + b) K/256 + c) 4096, and
+ * 32 x 256/bs scale bytes at the same piece index times that size in bscale_tiled), stored in
+ * the order in which the GEMMs' matrix instructions take it: with row r < 32, the 16-byte
+ * granule g < 8 of the row's 128 code bytes of the piece, q = g / 4, h = (g / 2) % 2,
+ * t = g % 2, sits at byte 1024 (2 q + t) + 16 (32 h + r) of the piece's codes; scale byte j of
+ * the row's piece sits, for MOE_PREC_W4A8 (16 per row; j = 8 q + 4 h + u, u < 4), at byte
+ * 8 (32 h + r) + 4 q + u, and for MOE_PREC_W4A8_MX (8 per row; j = 4 q + 2 h + u, u < 2) at
+ * byte 4 (32 h + r) + 2 q + u (the same array sizes).  For MOE_PREC_W4A8 each 4-byte group
+ * of codes, which holds the codes of 8 consecutive K positions k0..k0+7, also stores k0 + i in
+ * the low nibble and k0 + 4 + i in the high nibble of its byte i (the row-major bytes hold
+ * k0 + 2i and k0 + 2i + 1).  MXFP4 codes keep the row-major packing.  Device pointers; the outputs must not overlap the inputs;
  * enqueued on `stream`.  Call it once per matrix (W1: N = 2I, K = H; W2: N = H, K =
  * I) when the weights are loaded. */
 int moe_w4a8_tile_weights(const void *codes, const void *bscale, void *codes_tiled, void *bscale_tiled,

@@ -204,9 +204,12 @@ static void replay_gemm(const Problem &p, const Routing &r, bool swiglu, bool kl
             for (int lane = 0; lane < 64; ++lane)
                 for (int c : {0, nc - 1}) {
                     for (int i = 0; i < 4; ++i)
-                        check_load("weight codes", w_code_off(blk, K, lane, i, w_pitch), (uint32_t)(c * w_step), 16, nW);
-                    check_load("weight scales", w_scale_off(blk, K, sb, lane, s_pitch), (uint32_t)(c * s_step),
-                               w_scale_bytes(sb), nWs);
+                        check_load("weight codes",
+                                   p.tiled ? w_code_off_tiled(blk, K, lane, i) : w_code_off(blk, K, lane, i, w_pitch),
+                                   (uint32_t)(c * w_step), 16, nW);
+                    check_load("weight scales",
+                               p.tiled ? w_scale_off_tiled(blk, K, sb, lane) : w_scale_off(blk, K, sb, lane, s_pitch),
+                               (uint32_t)(c * s_step), w_scale_bytes(sb), nWs);
                 }
         }
         if (!rows_too) continue;  // the row addressing does not depend on the weight format or layout
@@ -330,6 +333,17 @@ static void replay_lds() {
                 const int h = lane >> 5;
                 for (int i = 0; i < 4; ++i) check_range("LDS weight write", lds_wcode(lane, i), 16, kWScales);
                 check_range("LDS weight scale write", lds_wscale(lane, mx), mx ? 4 : 8, kWSlot);
+                // tiled NVFP4 weights staged through the slot: the same slot bytes, written from the
+                // operand-order registers, must be the bytes the operand reads take
+                for (int i = 0; i < 4; ++i) {
+                    check_range("LDS tiled weight write", lds_wcode_tiled(lane, i), 16, kWScales);
+                    if (lds_wcode_tiled(lane, i) != lds_wread(lane) + 64 * (i >> 1) + 16 * (i & 1))
+                        fail("LDS tiled weight position", lane, i);
+                }
+                for (int q = 0; q < 2; ++q) {
+                    check_range("LDS tiled scale write", lds_wscale_tiled(lane, q), 4, kWSlot);
+                    if (lds_wscale_tiled(lane, q) != lds_wsread(lane) + 8 * q) fail("LDS tiled scale position", lane, q);
+                }
                 for (int q = 0; q < 2; ++q) {
                     for (int tt = 0; tt < 2; ++tt) {
                         check_range("LDS weight read", lds_wread(lane) + 64 * q + 16 * tt, 16, kWScales);
@@ -351,6 +365,55 @@ static void replay_lds() {
                             check_range("LDS hand-over", 4 * lds_xch(wu, NTB, tb, v16, lane), 4, kActBuf);
             }
         }
+}
+
+// the tiled layout: its code granules and scale bytes fill each piece exactly once, and a lane's
+// loads of a chunk (codes of step i = 2 q + t, its scale bytes) are the bytes its operands take:
+// row l % 32, code granule 4 q + 2 h + t (h = l / 32), scale bytes 8 q + 4 h + 2 t, +1 (NVFP4) or
+// 4 q + 2 h + t (MXFP4)
+static void replay_tiled_layout() {
+    std::vector<int> seen(256, 0);
+    for (int r = 0; r < 32; ++r)
+        for (int g = 0; g < 8; ++g) {
+            const int pos = tiled_code_pos(r, g);
+            check_range("tiled code granule", pos, 16, 4096);
+            if (pos % 16 != 0) fail("tiled code granule alignment", pos, 16);
+            else if (pos >= 0 && pos < 4096) seen[pos / 16]++;
+        }
+    for (int u = 0; u < 256; ++u)
+        if (seen[u] != 1) fail("tiled code granule use", seen[u], 1);
+    for (int lane = 0; lane < 64; ++lane)
+        for (int i = 0; i < 4; ++i) {
+            const int q = i >> 1, t = i & 1, h = lane >> 5;
+            if ((int)w_code_off_tiled(0, kKC, lane, i) != tiled_code_pos(lane & 31, 4 * q + 2 * h + t))
+                fail("tiled code load", lane, i);
+        }
+    for (bool mx : {false, true}) {
+        const int sb = mx ? 32 : 16, per = kKC / sb;
+        std::vector<int> used(32 * per, 0);
+        for (int r = 0; r < 32; ++r)
+            for (int j = 0; j < per; ++j) {
+                const int pos = tiled_scale_pos(r, j, mx);
+                check_range("tiled scale byte", pos, 1, 32 * per);
+                if (pos >= 0 && pos < 32 * per) used[pos]++;
+            }
+        for (int u = 0; u < 32 * per; ++u)
+            if (used[u] != 1) fail("tiled scale byte use", used[u], 1);
+        for (int lane = 0; lane < 64; ++lane) {
+            const int r = lane & 31, h = lane >> 5, base = (int)w_scale_off_tiled(0, kKC, sb, lane);
+            check_range("tiled scale load", base, w_scale_bytes(sb), 32 * per);
+            for (int q = 0; q < 2; ++q)
+                for (int t = 0; t < 2; ++t) {
+                    if (mx) {
+                        if (base + 2 * q + t != tiled_scale_pos(r, 4 * q + 2 * h + t, true)) fail("tiled MX scale", lane, q);
+                    } else {
+                        for (int u = 0; u < 2; ++u)
+                            if (base + 4 * q + 2 * t + u != tiled_scale_pos(r, 8 * q + 4 * h + 2 * t + u, false))
+                                fail("tiled NV scale", lane, q);
+                    }
+                }
+        }
+    }
 }
 
 // the single-launch forward's counters, re-quantisation and combine
@@ -438,6 +501,8 @@ static void replay_front_end(const Problem &p, const Routing &r, int threads) {
 int main() {
     g_case = "LDS";
     replay_lds();
+    g_case = "tiled layout";
+    replay_tiled_layout();
     Rng rng{12345};
     std::vector<Problem> probs;
     for (int T : {1, 2, 4, 8, 16, 32, 64, 128, 256})

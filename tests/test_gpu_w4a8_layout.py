@@ -28,16 +28,35 @@ def split_nibbles_host(codes: np.ndarray) -> np.ndarray:
 
 
 def tile_host(codes: np.ndarray, bscale: np.ndarray, bs: int):
-    """the layout's definition: [e][b][c][r][bytes] from row-major [e][32 b + r][bytes of piece c],
-    NVFP4 codes (bs = 16) with their nibbles regrouped per 4-byte group"""
+    """the layout's definition (include/moe.h), element by element: every 32-row block's 256-wide
+    piece is one run; code granule g of row r at 1024 (2 q + t) + 16 (32 h + r) with g = 4 q + 2 h
+    + t; scale byte j of row r at 8 (32 h + r) + 4 q + u (j = 8 q + 4 h + u, NVFP4) or 4 (32 h + r)
+    + 2 q + u (j = 4 q + 2 h + u, MXFP4); NVFP4 codes (bs = 16) with their nibbles regrouped per
+    4-byte group"""
     E, N, Kh = codes.shape
-    nc = Kh // 128
-    c = codes.reshape(E, N // 32, 32, nc, 128).transpose(0, 1, 3, 2, 4)
-    s = bscale.reshape(E, N // 32, 32, nc, 256 // bs).transpose(0, 1, 3, 2, 4)
-    c = np.ascontiguousarray(c).reshape(codes.shape)
-    if bs == 16:
-        c = split_nibbles_host(c)
-    return c, np.ascontiguousarray(s).reshape(bscale.shape)
+    nc, per = Kh // 128, 256 // bs
+    src_c = split_nibbles_host(codes) if bs == 16 else codes
+    out_c = np.zeros(E * N * Kh, dtype=np.uint8)
+    out_s = np.zeros(bscale.size, dtype=np.uint8)
+    for e in range(E):
+        for row in range(N):
+            blk, r = e * (N // 32) + row // 32, row % 32
+            for c in range(nc):
+                piece = (blk * nc + c) * 4096
+                for g in range(8):
+                    q, h, t = g // 4, (g // 2) % 2, g % 2
+                    d = piece + 1024 * (2 * q + t) + 16 * (32 * h + r)
+                    out_c[d:d + 16] = src_c[e, row, 128 * c + 16 * g:128 * c + 16 * g + 16]
+                spiece = (blk * nc + c) * 32 * per
+                for j in range(per):
+                    if bs == 16:
+                        q, h, u = j // 8, (j // 4) % 2, j % 4
+                        d = 8 * (32 * h + r) + 4 * q + u
+                    else:
+                        q, h, u = j // 4, (j // 2) % 2, j % 2
+                        d = 4 * (32 * h + r) + 2 * q + u
+                    out_s[spiece + d] = bscale[e, row, per * c + j]
+    return out_c.reshape(codes.shape), out_s.reshape(bscale.shape)
 
 
 def tile_device(codes: torch.Tensor, bscale: torch.Tensor, prec: int):

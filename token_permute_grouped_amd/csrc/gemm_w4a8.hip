@@ -195,7 +195,7 @@ struct StaticSched {
 // tile pays for a prologue (needs K / kKC to be a multiple of kNBuf, so that every tile starts at
 // the same register set and buffer phase).  sc.before_act(t) runs (uniformly, in every thread)
 // before the first activation load of tile t, sc.after_tile(t) after t's output is written.
-template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched, int kSplit = 0, bool kNib = false>
+template <bool kSwiGLU, bool kMX, int NTB, bool kLoop, class Sched, int kSplit = 0, bool kTiled = false>
 __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned char *act, float *xsl,
                                            unsigned char *wlds, const u32x2 *lut) {
     const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -210,6 +210,11 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     const int srow = w4::act_scale_row(tid);
     constexpr int kSB = kMX ? 32 : 16;  // K values per weight block scale
     const bool gather = g.row_src != nullptr;
+    // tiled weights go from the load registers straight into the matrix instructions, except
+    // NVFP4 with three token blocks: there the chunk's codes held until its compute, next to the
+    // dequant temporaries and 96 accumulators, would spill, so they are staged through the
+    // wave's LDS slot like row-major ones (at the slot positions of the same bytes)
+    constexpr bool kDirect = kTiled && (kMX || NTB < 3);
 
     // ---- addressing of one tile.  Weights: each wave streams its own 32 rows, in chunks of
     // 256 K (128 code bytes + 16 scale bytes per row); loads cover whole 128-byte lines (8 lanes
@@ -251,8 +256,9 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
         // a wave's 32 weight rows are one 32-row block of the matrix (weight_row(r) = weight_row(0) + r)
         const int blk = er + w4::weight_row(kSwiGLU, t.nt, wave, 0, g.I, g.il);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a.woff[i] = w4::w_code_off(blk, K, lane, i, g.w_pitch);
-        a.wsoff = w4::w_scale_off(blk, K, kSB, lane, g.s_pitch);
+        for (int i = 0; i < 4; ++i)
+            a.woff[i] = kTiled ? w4::w_code_off_tiled(blk, K, lane, i) : w4::w_code_off(blk, K, lane, i, g.w_pitch);
+        a.wsoff = kTiled ? w4::w_scale_off_tiled(blk, K, kSB, lane) : w4::w_scale_off(blk, K, kSB, lane, g.s_pitch);
 #pragma unroll
         for (int i = 0; i < NTB * 2 + 1; ++i) a.src[i] = 0;
         if (gather) {
@@ -293,12 +299,19 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     unsigned char *const wl = wlds + wave * kWSlot;
     auto store_w = [&](const WChunk &w) {
         unsigned char *d = wl;
+        if constexpr (kTiled) {  // NVFP4 only (kDirect otherwise)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
-        if constexpr (kMX)
-            *(uint32_t *)(d + w4::lds_wscale(lane, true)) = w.s.x;
-        else
-            *(u32x2 *)(d + w4::lds_wscale(lane, false)) = w.s;
+            for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode_tiled(lane, i)) = w.c[i];
+            *(uint32_t *)(d + w4::lds_wscale_tiled(lane, 0)) = w.s.x;
+            *(uint32_t *)(d + w4::lds_wscale_tiled(lane, 1)) = w.s.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
+            if constexpr (kMX)
+                *(uint32_t *)(d + w4::lds_wscale(lane, true)) = w.s.x;
+            else
+                *(u32x2 *)(d + w4::lds_wscale(lane, false)) = w.s;
+        }
     };
     u32x4 ar[NTB * 2];
     u32x2 ars;
@@ -319,8 +332,10 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     f32x16 acc_lo[kSplit == 2 ? NTB : 1];  // the first K half's sum
 
     // lane (row r = l % 32, half h = l / 32) of 64-K step (q, t) takes code bytes
-    // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1
-    auto compute = [&](int buf) {
+    // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1: from
+    // the wave's staging slot, or (kDirect) straight from the chunk's registers (code set
+    // 2 q + t; scale dword q (NVFP4), or halfword q (MXFP4))
+    auto compute = [&](int buf, const WChunk &wc) {
         const unsigned char *ab = act + buf * kActBuf;
         const unsigned char *wr = wl + w4::lds_wread(lane);
         const unsigned char *wsr = wl + w4::lds_wsread(lane);
@@ -336,11 +351,12 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                 for (int v = 0; v < 16; ++v) part[tb][v] = 0.f;
             // block scales of this lane's K runs: NVFP4 e4m3 bytes 8q + 4h + 2t, +1 (one per 16 K),
             // MXFP4 e8m0 byte 4q + 2h + t (one per 32 K)
-            const uint32_t sq = kMX ? *(const uint32_t *)(wsr - 4 * half + 4 * q) >> (16 * half)
-                                    : *(const uint32_t *)(wsr + 8 * q);
+            const uint32_t sq = kDirect ? (kMX ? wc.s.x >> (16 * q) : (q ? wc.s.y : wc.s.x))
+                                : kMX ? *(const uint32_t *)(wsr - 4 * half + 4 * q) >> (16 * half)
+                                      : *(const uint32_t *)(wsr + 8 * q);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {  // two 64-wide MFMA steps per 128-wide block
-                const u32x4 cw = *(const u32x4 *)(wr + 64 * q + 16 * t);
+                const u32x4 cw = kDirect ? wc.c[2 * q + t] : *(const u32x4 *)(wr + 64 * q + 16 * t);
                 i32x8 wa;
                 int wscale = 127;  // e8m0 1.0: the NVFP4 weights are dequantised to fp8 here
                 if constexpr (kMX) {  // the e2m1 codes are the MFMA's fp4 operand as they are
@@ -349,8 +365,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                 } else {
                     const uint32_t sc = sq >> (16 * t);
                     const u32x2 t0 = lut[sc & 0xffu], t1 = lut[(sc >> 8) & 0xffu];
-                    const u32x2 d0 = dequant8<kNib>(cw.x, t0), d1 = dequant8<kNib>(cw.y, t0);
-                    const u32x2 d2 = dequant8<kNib>(cw.z, t1), d3 = dequant8<kNib>(cw.w, t1);
+                    const u32x2 d0 = dequant8<kTiled>(cw.x, t0), d1 = dequant8<kTiled>(cw.y, t0);
+                    const u32x2 d2 = dequant8<kTiled>(cw.z, t1), d3 = dequant8<kTiled>(cw.w, t1);
                     wa = i32x8{(int)d0.x, (int)d0.y, (int)d1.x, (int)d1.y, (int)d2.x, (int)d2.y, (int)d3.x, (int)d3.y};
                 }
                 // activation granules (16 K each) of this lane's 32 fp8 bytes.  Both operands fp8: one
@@ -475,7 +491,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     store_a(0);
     load_a(A, min(1, nc - 1));
     load_w(w[NBUF - 2], A, min(NBUF - 2, nc - 1));
-    store_w(w[0]);
+    if constexpr (!kDirect) store_w(w[0]);
     lds_barrier();  // chunk 0 staged, scale table built
 
     for (;;) {
@@ -519,11 +535,13 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                         for (int v = 0; v < 16; ++v) acc[tb][v] = 0.f;
                     }
                 }
-                if (c < nc) compute(c & 1);
-                // the staging slot is rewritten below: keep these writes after the reads above
-                // (the lanes of the wave read each other's bytes; its LDS accesses run in order)
-                asm volatile("" ::: "memory");
-                store_w(w[(sidx + 1) % NBUF]);
+                if (c < nc) compute(c & 1, w[sidx]);
+                if constexpr (!kDirect) {
+                    // the staging slot is rewritten below: keep these writes after the reads above
+                    // (the lanes of the wave read each other's bytes; its LDS accesses run in order)
+                    asm volatile("" ::: "memory");
+                    store_w(w[(sidx + 1) % NBUF]);
+                }
                 store_a((c + 1) & 1);
                 const int ca = req(c + 2), cw = req(c + NBUF - 1);
                 if (go_on && c + 2 == nc) sc.before_act(nxt);  // the next tile's first activation load
@@ -557,9 +575,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     __shared__ __attribute__((aligned(16))) unsigned char wlds[4 * kWSlot]; /* one slot per wave */ \
     if constexpr (!kMX) lut[threadIdx.x] = scaled_e2m1_table(threadIdx.x); /* read after a tile's first barrier */
 
-// one tile per workgroup; its token-block count (1 to 3) from its own rows.  kNib: NVFP4 codes in
-// the tiled layout's nibble order
-template <bool kSwiGLU, bool kMX, bool kNib>
+
+template <bool kSwiGLU, bool kMX, bool kTiled>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g, const int32_t *__restrict__ offsets,
                                                                      const int32_t *__restrict__ tiles,
                                                                      const int32_t *__restrict__ n_tiles) {
@@ -569,23 +586,23 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_kernel(W4Args g
     const Tile t = sc.first();
     if (!t.valid) return;
     if (kSwiGLU && g.split == 1)  // decode sizes: rows of at most 32
-        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, kSwiGLU ? 1 : 0, kNib>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, kSwiGLU ? 1 : 0, kTiled>(g, sc, act, xsl, wlds, lut);
     else if (t.rows > 2 * 32)
-        w4a8_tiles<kSwiGLU, kMX, 3, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 3, false, StaticSched, 0, kTiled>(g, sc, act, xsl, wlds, lut);
     else if (t.rows > 32)
-        w4a8_tiles<kSwiGLU, kMX, 2, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 2, false, StaticSched, 0, kTiled>(g, sc, act, xsl, wlds, lut);
     else
-        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
+        w4a8_tiles<kSwiGLU, kMX, 1, false, StaticSched, 0, kTiled>(g, sc, act, xsl, wlds, lut);
 }
 
 // persistent (at most 32 rows per tile): workgroup b takes virtual blocks b, b + gridDim.x, ...
-template <bool kSwiGLU, bool kMX, bool kNib>
+template <bool kSwiGLU, bool kMX, bool kTiled>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_w4a8_persistent_kernel(
     W4Args g, const int32_t *__restrict__ offsets, const int32_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles) {
     TPG_W4A8_LDS
     StaticSched sc{(int)blockIdx.x, (int)gridDim.x, g.N / kBN, n_tiles[0], offsets, tiles, true};
-    w4a8_tiles<kSwiGLU, kMX, 1, true, StaticSched, 0, kNib>(g, sc, act, xsl, wlds, lut);
+    w4a8_tiles<kSwiGLU, kMX, 1, true, StaticSched, 0, kTiled>(g, sc, act, xsl, wlds, lut);
 }
 
 // ---------------------------------------------------------------- single-launch small-token forward
@@ -930,7 +947,7 @@ __device__ void fused_combine(const FusedArgs &f, int *rows_s, float *w_s) {
     }
 }
 
-template <bool kMX, int NTB, bool kHalves = false, bool kNib = false>
+template <bool kMX, int NTB, bool kHalves = false, bool kTiled = false>
 __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedArgs f) {
     TPG_W4A8_LDS
     __shared__ int word, n_mt_s;
@@ -985,11 +1002,11 @@ __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedAr
     const int n1 = n_mt * (2 * f.I / kBN), n2 = n_mt * (f.H / kBN);
     {
         FusedSched<true> sc{f, st, &word, n_mt, n1, n2};
-        w4a8_tiles<true, kMX, NTB, true, FusedSched<true>, kHalves ? 2 : 0, kNib>(f.g1, sc, act, xsl, wlds, lut);
+        w4a8_tiles<true, kMX, NTB, true, FusedSched<true>, kHalves ? 2 : 0, kTiled>(f.g1, sc, act, xsl, wlds, lut);
     }
     {
         FusedSched<false> sc{f, st, &word, n_mt, n1, n2};
-        w4a8_tiles<false, kMX, NTB, true, FusedSched<false>, 0, kNib>(f.g2, sc, act, xsl, wlds, lut);
+        w4a8_tiles<false, kMX, NTB, true, FusedSched<false>, 0, kTiled>(f.g2, sc, act, xsl, wlds, lut);
     }
     // every workgroup's GEMM2 rows are written before any combine reads them
     publish_and_count(&sy->gemm_done, &word);
@@ -1117,23 +1134,25 @@ W4Launch w4_launch(int64_t max_tiles, int N, int K, int E, int a_rows, int T) {
     return {std::min<int64_t>(blocks, 2 * (int64_t)n_cu), true};
 }
 
-template <bool kSwiGLU, bool kMX, bool kNib>
+template <bool kSwiGLU, bool kMX, bool kTiled>
 void launch_w4a8_gemm_as(const W4Launch &l, const W4Args &g, const int32_t *offsets, const int32_t *tiles,
                          const int32_t *n_tiles, hipStream_t s) {
     if (l.persistent)
-        hipLaunchKernelGGL((grouped_gemm_w4a8_persistent_kernel<kSwiGLU, kMX, kNib>), dim3(l.grid), dim3(kThreads), 0,
+        hipLaunchKernelGGL((grouped_gemm_w4a8_persistent_kernel<kSwiGLU, kMX, kTiled>), dim3(l.grid), dim3(kThreads), 0,
                            s, g, offsets, tiles, n_tiles);
     else
-        hipLaunchKernelGGL((grouped_gemm_w4a8_kernel<kSwiGLU, kMX, kNib>), dim3(l.grid), dim3(kThreads), 0, s, g,
+        hipLaunchKernelGGL((grouped_gemm_w4a8_kernel<kSwiGLU, kMX, kTiled>), dim3(l.grid), dim3(kThreads), 0, s, g,
                            offsets, tiles, n_tiles);
 }
-// nib: NVFP4 codes in the tiled layout's nibble order (never with MXFP4)
+// tiled: weights in MOE_W4_LAYOUT_TILED (operand order; NVFP4 codes in its nibble order)
 template <bool kSwiGLU>
-void launch_w4a8_gemm(bool mx, bool nib, const W4Launch &l, const W4Args &g, const int32_t *offsets,
+void launch_w4a8_gemm(bool mx, bool tiled, const W4Launch &l, const W4Args &g, const int32_t *offsets,
                       const int32_t *tiles, const int32_t *n_tiles, hipStream_t s) {
-    if (mx)
+    if (mx && tiled)
+        launch_w4a8_gemm_as<kSwiGLU, true, true>(l, g, offsets, tiles, n_tiles, s);
+    else if (mx)
         launch_w4a8_gemm_as<kSwiGLU, true, false>(l, g, offsets, tiles, n_tiles, s);
-    else if (nib)
+    else if (tiled)
         launch_w4a8_gemm_as<kSwiGLU, false, true>(l, g, offsets, tiles, n_tiles, s);
     else
         launch_w4a8_gemm_as<kSwiGLU, false, false>(l, g, offsets, tiles, n_tiles, s);
@@ -1161,7 +1180,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     if (row_src && !gather_fits_fp8(p.T, H)) return hipErrorInvalidValue;
     const int S = (int)n_slots(p);
     const bool mx = p.prec == MOE_PREC_W4A8_MX;
-    const bool nib = !mx && w.w4_layout == MOE_W4_LAYOUT_TILED;  // NVFP4 codes in the tiled nibble order
+    const bool tiled = w.w4_layout == MOE_W4_LAYOUT_TILED;
     const W4Launch l1 = w4_launch(max_tiles, 2 * I, H, p.E, row_src ? p.T : S, p.T),
                    l2 = w4_launch(max_tiles, H, I, p.E, S, p.T);
     W4Args g1{};
@@ -1185,10 +1204,10 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     if (split) {  // two workgroups per tile, one per K half, one tile each (rows of at most 32)
         g1.split = 1;
         g1.part_stride = (int64_t)S * I;
-        launch_w4a8_gemm<true>(mx, nib, W4Launch{2 * max_tiles * (2 * I / kBN), false}, g1, offsets, tiles, n_tiles,
+        launch_w4a8_gemm<true>(mx, tiled, W4Launch{2 * max_tiles * (2 * I / kBN), false}, g1, offsets, tiles, n_tiles,
                                s);
     } else {
-        launch_w4a8_gemm<true>(mx, nib, l1, g1, offsets, tiles, n_tiles, s);
+        launch_w4a8_gemm<true>(mx, tiled, l1, g1, offsets, tiles, n_tiles, s);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -1216,7 +1235,7 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
     g2.ldy = H;
     g2.row_dst = row_dst;
     set_layout(g2, I, mx, w.w4_layout);
-    launch_w4a8_gemm<false>(mx, nib, l2, g2, offsets, tiles, n_tiles, s);
+    launch_w4a8_gemm<false>(mx, tiled, l2, g2, offsets, tiles, n_tiles, s);
     return hipGetLastError();
 }
 
@@ -1227,6 +1246,28 @@ bool forward_small_w4a8_fits(const moe_problem &p) {
            (int64_t)p.E * p.H * (p.I / 2) <= lim && (int64_t)p.T * p.H <= lim && S * p.I <= lim;
 }
 
+namespace {
+// one kernel form: its grid is every workgroup resident at once (two per CU: the kernel's LDS and
+// register budget); the kernel does not depend on it, but idle waits are shortest then
+template <bool kMX, bool kTiled>
+hipError_t launch_forward_small_as(const FusedArgs &f, bool halves, bool one_block, int n_cu, hipStream_t s) {
+    const void *fn = halves      ? (const void *)forward_small_w4a8_kernel<kMX, 1, true, kTiled>
+                     : one_block ? (const void *)forward_small_w4a8_kernel<kMX, 1, false, kTiled>
+                                 : (const void *)forward_small_w4a8_kernel<kMX, 2, false, kTiled>;
+    int per_cu = 0;
+    const hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
+    if (err != hipSuccess) return err;
+    const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
+    if (halves)
+        hipLaunchKernelGGL((forward_small_w4a8_kernel<kMX, 1, true, kTiled>), dim3(grid), dim3(kThreads), 0, s, f);
+    else if (one_block)
+        hipLaunchKernelGGL((forward_small_w4a8_kernel<kMX, 1, false, kTiled>), dim3(grid), dim3(kThreads), 0, s, f);
+    else
+        hipLaunchKernelGGL((forward_small_w4a8_kernel<kMX, 2, false, kTiled>), dim3(grid), dim3(kThreads), 0, s, f);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_drop, const uint8_t *x,
                                      const float *x_scale, const moe_weights &w, const moe_problem &p,
                                      int64_t max_tiles, FusedSync *sync, int32_t *topk_idx, float *topk_w,
@@ -1235,7 +1276,7 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
                                      uint16_t *out, hipStream_t s) {
     if (!forward_small_w4a8_fits(p)) return hipErrorInvalidValue;
     const bool mx = p.prec == MOE_PREC_W4A8_MX;
-    const bool nib = !mx && w.w4_layout == MOE_W4_LAYOUT_TILED;  // NVFP4 codes in the tiled nibble order
+    const bool tiled = w.w4_layout == MOE_W4_LAYOUT_TILED;
     const int S = (int)n_slots(p);
     FusedArgs f{};
     f.logits = logits;
@@ -1295,49 +1336,16 @@ hipError_t launch_forward_small_w4a8(const float *logits, const uint8_t *slot_dr
     g2.Yout = y;
     g2.ldy = p.H;
     set_layout(g2, p.I, mx, w.w4_layout);
-    // every workgroup resident at once (two per CU: the kernel's LDS and register budget); the
-    // kernel does not depend on it, but idle waits are shortest then
-    int dev = 0, n_cu = 0, per_cu = 0;
+    int dev = 0, n_cu = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err == hipSuccess) err = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const bool one_block = p.T <= 32;  // every m-tile fits one 32-row token block
     const bool halves = g1.split == 2;  // T <= 32 only (one token block)
-    const void *fn = mx ? (halves ? (const void *)forward_small_w4a8_kernel<true, 1, true>
-                           : one_block ? (const void *)forward_small_w4a8_kernel<true, 1>
-                                       : (const void *)forward_small_w4a8_kernel<true, 2>)
-                   : nib ? (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true, true>
-                            : one_block ? (const void *)forward_small_w4a8_kernel<false, 1, false, true>
-                                        : (const void *)forward_small_w4a8_kernel<false, 2, false, true>)
-                         : (halves ? (const void *)forward_small_w4a8_kernel<false, 1, true>
-                            : one_block ? (const void *)forward_small_w4a8_kernel<false, 1>
-                                        : (const void *)forward_small_w4a8_kernel<false, 2>);
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
-    if (err != hipSuccess) return err;
-    const int grid = std::max(1, std::min(per_cu, 2) * n_cu);
-    if (mx) {
-        if (halves)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1, true>), dim3(grid), dim3(kThreads), 0, s, f);
-        else if (one_block)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, f);
-        else
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<true, 2>), dim3(grid), dim3(kThreads), 0, s, f);
-    } else if (nib) {
-        if (halves)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, true, true>), dim3(grid), dim3(kThreads), 0, s, f);
-        else if (one_block)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, false, true>), dim3(grid), dim3(kThreads), 0, s, f);
-        else
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 2, false, true>), dim3(grid), dim3(kThreads), 0, s, f);
-    } else {
-        if (halves)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1, true>), dim3(grid), dim3(kThreads), 0, s, f);
-        else if (one_block)
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, f);
-        else
-            hipLaunchKernelGGL((forward_small_w4a8_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, f);
-    }
-    return hipGetLastError();
+    if (mx && tiled) return launch_forward_small_as<true, true>(f, halves, one_block, n_cu, s);
+    if (mx) return launch_forward_small_as<true, false>(f, halves, one_block, n_cu, s);
+    if (tiled) return launch_forward_small_as<false, true>(f, halves, one_block, n_cu, s);
+    return launch_forward_small_as<false, false>(f, halves, one_block, n_cu, s);
 }
 
 // NVFP4 codes in the tiled layout: the eight codes of a dword, packed low nibble first (byte i
@@ -1350,39 +1358,50 @@ __device__ __forceinline__ uint32_t split_nibbles(uint32_t x) {
     return first | (second << 4);
 }
 
-// MOE_W4_LAYOUT_TILED from row-major codes and block scales: one thread per destination unit
-// (16 code bytes, or 8 scale bytes); destination unit d of a 32-row block's 256-wide piece c
-// holds row r, bytes 16 j (8 j) of that row's piece (NVFP4 codes with split_nibbles applied)
-__global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
-                                                           int64_t units, int unit_bytes, int piece_units,
-                                                           int row_bytes, int n_pieces, bool split) {
-    const int64_t d = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (d >= units) return;
-    const int j = (int)(d % piece_units);
-    const int r = (int)((d / piece_units) % 32);
-    const int64_t c = (d / (piece_units * 32)) % n_pieces;
-    const int64_t blk = d / ((int64_t)piece_units * 32 * n_pieces);  // expert * (N / 32) + block
-    const int64_t from = (blk * 32 + r) * row_bytes + c * (piece_units * unit_bytes) + j * unit_bytes;
-    if (unit_bytes == 16) {
-        uint4 v = *(const uint4 *)(src + from);
-        if (split) v = make_uint4(split_nibbles(v.x), split_nibbles(v.y), split_nibbles(v.z), split_nibbles(v.w));
-        *(uint4 *)(dst + d * 16) = v;
-    } else
-        *(uint2 *)(dst + d * 8) = *(const uint2 *)(src + from);
+// MOE_W4_LAYOUT_TILED from row-major codes: one thread per 16-byte granule g of row r's 256-wide
+// piece c in a 32-row block; it goes to w4::tiled_code_pos(r, g) of that piece (NVFP4 codes with
+// split_nibbles applied)
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                         int64_t units, int row_bytes, int n_pieces, bool split) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const int per_row = row_bytes / 16;
+    const int64_t row = u / per_row;  // expert * N + row of the matrix
+    const int gi = (int)(u % per_row), c = gi / 8, g = gi % 8;
+    const int64_t blk = row / 32;
+    const int r = (int)(row % 32);
+    uint4 v = *(const uint4 *)(src + u * 16);
+    if (split) v = make_uint4(split_nibbles(v.x), split_nibbles(v.y), split_nibbles(v.z), split_nibbles(v.w));
+    *(uint4 *)(dst + (blk * n_pieces + c) * 4096 + w4::tiled_code_pos(r, g)) = v;
+}
+
+// the block scales: one thread per row and piece (16 e4m3 bytes, or 8 e8m0 bytes); byte j goes to
+// w4::tiled_scale_pos(r, j, mx) of the piece's scales
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                          int64_t units, int n_pieces, bool mx) {
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    const int per = mx ? kKC / 32 : kKC / 16;  // scale bytes of one row's piece
+    const int64_t row = u / n_pieces;
+    const int c = (int)(u % n_pieces);
+    const int64_t blk = row / 32;
+    const int r = (int)(row % 32);
+    uint8_t *d = dst + (blk * n_pieces + c) * 32 * per;
+    for (int j = 0; j < per; ++j) d[w4::tiled_scale_pos(r, j, mx)] = src[u * per + j];
 }
 
 hipError_t launch_tile_weights(const uint8_t *codes, const uint8_t *bscale, uint8_t *codes_tiled,
                                uint8_t *bscale_tiled, int E, int N, int K, bool mx, hipStream_t s) {
-    const int sb = mx ? 32 : 16, n_pieces = K / kKC;
+    const int n_pieces = K / kKC;
     const int64_t rows = (int64_t)E * N;
-    const int64_t cu = rows * (K / 2) / 16;      // 16-byte code units
-    const int64_t su = rows * (K / sb) / 8;      // 8-byte scale units
-    hipLaunchKernelGGL(tile_weights_kernel, dim3((cu + 255) / 256), dim3(256), 0, s, codes, codes_tiled, cu, 16,
-                       (kKC / 2) / 16, K / 2, n_pieces, !mx);
+    const int64_t cu = rows * (K / 2) / 16;  // 16-byte code granules
+    const int64_t su = rows * n_pieces;      // row pieces of scales
+    hipLaunchKernelGGL(tile_codes_kernel, dim3((cu + 255) / 256), dim3(256), 0, s, codes, codes_tiled, cu, K / 2,
+                       n_pieces, !mx);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(tile_weights_kernel, dim3((su + 255) / 256), dim3(256), 0, s, bscale, bscale_tiled, su, 8,
-                       (kKC / sb) / 8, K / sb, n_pieces, false);
+    hipLaunchKernelGGL(tile_scales_kernel, dim3((su + 255) / 256), dim3(256), 0, s, bscale, bscale_tiled, su, n_pieces,
+                       mx);
     return hipGetLastError();
 }
 

@@ -98,6 +98,36 @@ TPG_HD uint32_t w_scale_off(int blk, int K, int sb, int lane, int s_pitch) {
 // bytes one lane's scale load of a chunk reads (8 e4m3 scales, or 4 e8m0 ones)
 TPG_HD int w_scale_bytes(int sb) { return kKC / sb / 2; }
 
+// The tiled layout stores each 32-row block's 256-wide piece in the matrix instruction's operand
+// order: lane l = 32 h + r (row r, half h) of 64-K step i = 2 q + t takes the 16 code bytes
+// [64 q + 32 h + 16 t, +16) of its row, so the piece is four 1 KB runs, one per step, each in
+// lane order; and the block scales of those codes in lane order (8 bytes per lane for NVFP4:
+// row bytes 4 h .. 4 h + 3 and 8 + 4 h .. 8 + 4 h + 3; 4 for MXFP4: row bytes 2 h, 2 h + 1,
+// 4 + 2 h, 5 + 2 h).  A wave then loads its operands with contiguous 16-byte (codes) and 8- or
+// 4-byte (scales) loads per lane, with no transposition through LDS.
+// Position within the piece of 16-byte code granule g of row r:
+TPG_HD int tiled_code_pos(int r, int g) {
+    const int q = g >> 2, h = (g >> 1) & 1, t = g & 1;
+    return (2 * q + t) * 1024 + (32 * h + r) * 16;
+}
+// Position within the piece's scales of scale byte j of row r (16 per row for NVFP4, 8 for MXFP4)
+TPG_HD int tiled_scale_pos(int r, int j, bool mx) {
+    if (mx) {  // j = 4 q + 2 h + u
+        const int q = j >> 2, h = (j >> 1) & 1, u = j & 1;
+        return (32 * h + r) * 4 + 2 * q + u;
+    }
+    const int q = j >> 3, h = (j >> 2) & 1, u = j & 3;  // j = 8 q + 4 h + u
+    return (32 * h + r) * 8 + 4 * q + u;
+}
+// Loads of one chunk from the tiled layout (chunk c adds c * 4096 for the codes, c * 32 times
+// the row's scale bytes per piece for the scales): lane l's codes of step i, its scales
+TPG_HD uint32_t w_code_off_tiled(int blk, int K, int lane, int i) {
+    return (uint32_t)(blk * (K / 2) + i * 1024 + lane * 16);
+}
+TPG_HD uint32_t w_scale_off_tiled(int blk, int K, int sb, int lane) {
+    return (uint32_t)(blk * (K / sb) + lane * w_scale_bytes(sb));
+}
+
 // Activation staging: thread tid stages granule tid % 16 (16 bytes) of tile rows tid / 16 + 16 i
 // (i < 2 NTB), and thread tid < 32 NTB the chunk's two activation scales of tile row
 // min(tid, kMaxRows - 1).  Row rr of the source (the token row when gathering, else the row within the
@@ -121,6 +151,14 @@ TPG_HD int lds_wscale(int lane, bool mx) { return kWScales + (lane >> 1) * 16 + 
 // dword at - 4 h + 4 q for MXFP4)
 TPG_HD int lds_wread(int lane) { return (lane & 31) * kWRow + (lane >> 5) * 32; }
 TPG_HD int lds_wsread(int lane) { return kWScales + (lane & 31) * 16 + (lane >> 5) * 4; }
+// a wave's staging slot for tiled weights (whose lane l holds the operand bytes of step i, see
+// tiled_code_pos): the same slot layout as above, so the operand reads are unchanged; code
+// register i of lane l goes to row l % 32, granule 4 (i / 2) + 2 (l / 32) + i % 2, and NVFP4
+// scale dword q to the row's bytes 8 q + 4 (l / 32)
+TPG_HD int lds_wcode_tiled(int lane, int i) {
+    return (lane & 31) * kWRow + (4 * (i >> 1) + 2 * (lane >> 5) + (i & 1)) * 16;
+}
+TPG_HD int lds_wscale_tiled(int lane, int q) { return kWScales + (lane & 31) * 16 + 8 * q + 4 * (lane >> 5); }
 // activation scale of tile row r, block q of the chunk (float index into [2][kMaxRows][2])
 TPG_HD int lds_xs(int buf, int r, int q) { return buf * (kMaxRows * 2) + r * 2 + q; }
 // SwiGLU hand-over: accumulator v of token block tb of up wave 2 + wu, lane l (float index)
