@@ -463,6 +463,23 @@ static void replay_fused_tails(const Problem &p, const Routing &r) {
 }
 
 // the front ends: routing rows, LDS ids and counts, tables and tile list
+// the single-workgroup tables kernel after the router (up to 2048 slots): slot s is thread
+// s % 1024 of pass s / 1024, its counter group pass * 16 + wave, counters [2 * 16][256]
+static void replay_tables_small(const Problem &p, const Routing &r) {
+    const int S = p.T * p.k;
+    if (S > 2048) fail("slots of the tables kernel", S, 2048);
+    for (int s = 0; s < S; ++s) {
+        const int x = r.idx[s];
+        const int g = (s / 1024) * 16 + (s % 1024) / 64;
+        if (x >= 0) {
+            check_range("LDS count", (long long)g * 256 + x, 1, 2LL * 16 * 256);
+            check_range("row_src store", r.slot_row[s], 1, S);
+        }
+        check_range("slot_row store", s, 1, S);
+    }
+    check_range("offsets store", p.E, 1, p.E + 1);
+}
+
 static void replay_front_end(const Problem &p, const Routing &r, int threads) {
     const int S = p.T * p.k, waves = threads / 64;
     const int sid_n = threads == 1024 ? 1024 : 2048;
@@ -549,6 +566,7 @@ int main() {
                 replay_front_end(p, r, 256);
             }
             if (S <= 1024 && p.T <= 256) replay_front_end(p, r, 1024);
+            if (S <= 2048) replay_tables_small(p, r);
         }
     std::printf("%zu problems x 4 routings: %ld index checks, %ld out of range, %ld loads ending exactly at their "
                 "buffer's end\n", probs.size(), g_checks, g_fail, g_exact_end);

@@ -202,7 +202,7 @@ int forward_impl(const float *logits, const uint8_t *slot_drop, const void *x, c
         return st;
     }
     if ((st = mark(1))) return st;
-    // the tables' scan launch also writes the GEMM tile list
+    // the tables' launches (the scan, or tables_small up to 2048 slots) also write the GEMM tile list
     if (!small && (st = hip_status(launch_tables(topk_idx, p->T, p->k, p->E, chunk_counts, offsets, row_src, slot_row,
                                                  gemm_bm(*p), tile_order(*p), tiles, n_tiles, s))))
         return st;

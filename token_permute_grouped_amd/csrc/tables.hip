@@ -19,7 +19,8 @@
 //
 // For up to kChunk slots the forward runs all of this (and the routing) in one workgroup
 // instead: frontend_small, with the expert ids kept in LDS between the steps.  At small
-// token counts the five launches it replaces cost more than their work.
+// token counts the five launches it replaces cost more than their work.  Up to 2048 slots the
+// three table launches are one (tables_small, after the router).
 #include <algorithm>
 
 #include "route_token.h"
@@ -190,6 +191,8 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t *__restr
 // Routing, tables and tile list of at most kChunk slots in one workgroup of 16 waves: the same
 // results as route_topk + chunk_hist + scan + rank + build_tiles.  Slot s is thread s.
 constexpr int kFrontWaves = kChunk / kWave;  // 16
+constexpr int kTablesPasses = 2;                        // tables_small_kernel: slots per thread
+constexpr int kTablesSlots = kTablesPasses * kChunk;    // its largest slot count (2048)
 __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
     const float *__restrict__ logits, const uint8_t *__restrict__ slot_drop, int T, int E, int k, int bm, int by_expert,
     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ offsets,
@@ -258,6 +261,82 @@ __global__ __launch_bounds__(kChunk) void frontend_small_kernel(
     build_tile_list(off, E, bm, by_expert, tiles, n_tiles, ws);
 }
 
+// Tables (and, given tiles, the tile list) of at most kTablesSlots slots in one workgroup of 16
+// waves, after the router: the same results as chunk_hist + scan + rank, in one launch instead
+// of three.  Slot s is thread s % kChunk of pass s / kChunk; the passes, and the waves within a
+// pass, take an expert's rows in slot order, so the order stays stable.  (Routing stays with
+// route_topk's many workgroups: routing 256 tokens inside one workgroup measured as slow as the
+// separate launches.)
+__global__ __launch_bounds__(kChunk) void tables_small_kernel(const int32_t *__restrict__ idx, int S, int E, int bm,
+                                                              int by_expert, int32_t *__restrict__ offsets,
+                                                              int32_t *__restrict__ row_src,
+                                                              int32_t *__restrict__ slot_row,
+                                                              int32_t *__restrict__ tiles,
+                                                              int32_t *__restrict__ n_tiles) {
+    __shared__ int cnt[kTablesPasses * kFrontWaves][256];  // per (pass, wave) counts, then bases
+    __shared__ int off[257];
+    __shared__ int ws[8];  // block prefix-sum scratch
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int x[kTablesPasses];
+#pragma unroll
+    for (int p = 0; p < kTablesPasses; ++p) {
+        const int slot = p * kChunk + tid;
+        x[p] = slot < S ? valid_id(idx[slot], E) : -1;
+    }
+    for (int i = tid; i < kTablesPasses * kFrontWaves * 256; i += kChunk) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kTablesPasses; ++p)
+        if (x[p] >= 0) atomicAdd(&cnt[p * kFrontWaves + w][x[p]], 1);
+    __syncthreads();
+
+    // per expert: exclusive bases over the (pass, wave) groups in slot order and the total;
+    // exclusive scan over experts
+    int tot = 0;
+    if (tid < 256)
+        for (int g = 0; g < kTablesPasses * kFrontWaves; ++g) {
+            const int v = cnt[g][tid];
+            cnt[g][tid] = tot;
+            tot += v;
+        }
+    int incl = tot, unused = 0, R_all, unused_total;
+    block_incl_sum256(incl, unused, ws, &R_all, &unused_total);
+    if (tid < E) {
+        off[tid] = incl - tot;
+        offsets[tid] = incl - tot;
+    }
+    if (tid == 0) {
+        off[E] = R_all;
+        offsets[E] = R_all;
+    }
+    __syncthreads();
+
+    // rank of the slot among equal ids of lower lanes of its pass: 9 ballots (one per bit of id+1)
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int R = off[E];
+#pragma unroll
+    for (int p = 0; p < kTablesPasses; ++p) {
+        const unsigned key = (unsigned)(x[p] + 1);
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+            const bool bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & lt);
+        const int slot = p * kChunk + tid;
+        if (slot < S) {
+            const int r = x[p] >= 0 ? off[x[p]] + cnt[p * kFrontWaves + w][x[p]] + rank : -1;
+            slot_row[slot] = r;
+            if (r >= 0) row_src[r] = slot;
+            if (slot >= R) row_src[slot] = -1;  // rows past the live count (r < R never lands here)
+        }
+    }
+    if (tiles == nullptr) return;  // uniform
+    build_tile_list(off, E, bm, by_expert, tiles, n_tiles, ws);
+}
+
 hipError_t launch_frontend_small(const float *logits, const uint8_t *slot_drop, int T, int E, int k, int bm,
                                  int by_expert, int32_t *topk_idx, float *topk_w, int32_t *offsets,
                                  int32_t *row_src, int32_t *slot_row, int32_t *tiles, int32_t *n_tiles,
@@ -272,6 +351,11 @@ hipError_t launch_tables(const int32_t *topk_idx, int T, int k, int E, int32_t *
                          int32_t *row_src, int32_t *slot_row, int bm, int by_expert, int32_t *tiles,
                          int32_t *n_tiles, hipStream_t s) {
     const int64_t S = (int64_t)T * k;
+    if (S <= kTablesSlots) {
+        hipLaunchKernelGGL(tables_small_kernel, dim3(1), dim3(kChunk), 0, s, topk_idx, (int)S, E, bm, by_expert, offsets,
+                           row_src, slot_row, tiles, n_tiles);
+        return hipGetLastError();
+    }
     const int64_t nch = (S + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(chunk_hist_kernel, dim3(nch), dim3(256), 0, s, topk_idx, S, E, chunk_counts);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, chunk_counts, nch, E, scan_parts(nch, E),
