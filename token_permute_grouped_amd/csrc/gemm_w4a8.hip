@@ -26,10 +26,16 @@
 // the tile before it, so that it does not stream the expert's weights once more for a
 // few rows) and 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every
 // token of the tile.  Weights are never shared between waves: each wave loads its rows
-// with line-coalesced loads (8 lanes per 128-byte line) three 256-wide K chunks ahead
-// (four register sets; two ahead in three sets for three token blocks), transposes each
-// chunk through its own LDS slot into the MFMA operand layout (lane l: row l % 32, one
-// contiguous 32-code run per 64-wide K step) and dequantises it there.  Activations are
+// three 256-wide K chunks ahead (four register sets; two ahead in three sets for three
+// token blocks).  Row-major weights come in line-coalesced loads (8 lanes per 128-byte
+// line) and each chunk is transposed through the wave's own LDS slot into the MFMA
+// operand layout (lane l: row l % 32, one contiguous 32-code run per 64-wide K step).
+// The tiled layout (moe_w4a8_tile_weights) already stores every 32-row, 256-wide piece
+// in that operand order, four 1 KB runs in lane order, so a wave's loads are contiguous
+// and land in the operand registers as they are (kTiled): no LDS transpose, and the
+// chunk is used where it is computed instead of a step earlier; NVFP4 with three token
+// blocks still stages it through the slot (registers).  NVFP4 codes are dequantised as
+// they are read.  Activations are
 // shared by the four waves: each chunk of the tile's token rows and its activation scales
 // are loaded into registers two chunks ahead and written to LDS one chunk ahead (two
 // buffers, swizzled).  Every load is an
