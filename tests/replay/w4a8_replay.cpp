@@ -333,17 +333,6 @@ static void replay_lds() {
                 const int h = lane >> 5;
                 for (int i = 0; i < 4; ++i) check_range("LDS weight write", lds_wcode(lane, i), 16, kWScales);
                 check_range("LDS weight scale write", lds_wscale(lane, mx), mx ? 4 : 8, kWSlot);
-                // tiled NVFP4 weights staged through the slot: the same slot bytes, written from the
-                // operand-order registers, must be the bytes the operand reads take
-                for (int i = 0; i < 4; ++i) {
-                    check_range("LDS tiled weight write", lds_wcode_tiled(lane, i), 16, kWScales);
-                    if (lds_wcode_tiled(lane, i) != lds_wread(lane) + 64 * (i >> 1) + 16 * (i & 1))
-                        fail("LDS tiled weight position", lane, i);
-                }
-                for (int q = 0; q < 2; ++q) {
-                    check_range("LDS tiled scale write", lds_wscale_tiled(lane, q), 4, kWSlot);
-                    if (lds_wscale_tiled(lane, q) != lds_wsread(lane) + 8 * q) fail("LDS tiled scale position", lane, q);
-                }
                 for (int q = 0; q < 2; ++q) {
                     for (int tt = 0; tt < 2; ++tt) {
                         check_range("LDS weight read", lds_wread(lane) + 64 * q + 16 * tt, 16, kWScales);

@@ -26,16 +26,15 @@
 // the tile before it, so that it does not stream the expert's weights once more for a
 // few rows) and 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every
 // token of the tile.  Weights are never shared between waves: each wave loads its rows
-// three 256-wide K chunks ahead (four register sets; two ahead in three sets for three
-// token blocks).  Row-major weights come in line-coalesced loads (8 lanes per 128-byte
-// line) and each chunk is transposed through the wave's own LDS slot into the MFMA
-// operand layout (lane l: row l % 32, one contiguous 32-code run per 64-wide K step).
-// The tiled layout (moe_w4a8_tile_weights) already stores every 32-row, 256-wide piece
-// in that operand order, four 1 KB runs in lane order, so a wave's loads are contiguous
-// and land in the operand registers as they are (kTiled): no LDS transpose, and the
-// chunk is used where it is computed instead of a step earlier; NVFP4 with three token
-// blocks still stages it through the slot (registers).  NVFP4 codes are dequantised as
-// they are read.  Activations are
+// into a ring of register sets, one 256-wide K chunk per set, as many chunks ahead as the
+// ring allows (four sets; for three token blocks, whose accumulators take registers, three,
+// or two with tiled weights).  Row-major weights come in line-coalesced loads (8 lanes per
+// 128-byte line) and each chunk is transposed, one step before its compute, through the
+// wave's own LDS slot into the MFMA operand layout (lane l: row l % 32, one contiguous
+// 32-code run per 64-wide K step).  The tiled layout (moe_w4a8_tile_weights) already
+// stores every 32-row, 256-wide piece in that operand order, four 1 KB runs in lane
+// order, so a wave's loads are contiguous and land in the operand registers as they are
+// (kTiled): no LDS transpose.  NVFP4 codes are dequantised as they are read.  Activations are
 // shared by the four waves: each chunk of the tile's token rows and its activation scales
 // are loaded into registers two chunks ahead and written to LDS one chunk ahead (two
 // buffers, swizzled).  Every load is an
@@ -216,11 +215,6 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     const int srow = w4::act_scale_row(tid);
     constexpr int kSB = kMX ? 32 : 16;  // K values per weight block scale
     const bool gather = g.row_src != nullptr;
-    // tiled weights go from the load registers straight into the matrix instructions, except
-    // NVFP4 with three token blocks: there the chunk's codes held until its compute, next to the
-    // dequant temporaries and 96 accumulators, would spill, so they are staged through the
-    // wave's LDS slot like row-major ones (at the slot positions of the same bytes)
-    constexpr bool kDirect = kTiled && (kMX || NTB < 3);
 
     // ---- addressing of one tile.  Weights: each wave streams its own 32 rows, in chunks of
     // 256 K (128 code bytes + 16 scale bytes per row); loads cover whole 128-byte lines (8 lanes
@@ -303,21 +297,14 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // this wave's staging slot: a chunk's weights are written after the wave's reads of the
     // previous chunk's, and one wave's LDS accesses complete in order, so one slot serves
     unsigned char *const wl = wlds + wave * kWSlot;
-    auto store_w = [&](const WChunk &w) {
+    auto store_w = [&](const WChunk &w) {  // row-major weights only
         unsigned char *d = wl;
-        if constexpr (kTiled) {  // NVFP4 only (kDirect otherwise)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode_tiled(lane, i)) = w.c[i];
-            *(uint32_t *)(d + w4::lds_wscale_tiled(lane, 0)) = w.s.x;
-            *(uint32_t *)(d + w4::lds_wscale_tiled(lane, 1)) = w.s.y;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
-            if constexpr (kMX)
-                *(uint32_t *)(d + w4::lds_wscale(lane, true)) = w.s.x;
-            else
-                *(u32x2 *)(d + w4::lds_wscale(lane, false)) = w.s;
-        }
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(d + w4::lds_wcode(lane, i)) = w.c[i];
+        if constexpr (kMX)
+            *(uint32_t *)(d + w4::lds_wscale(lane, true)) = w.s.x;
+        else
+            *(u32x2 *)(d + w4::lds_wscale(lane, false)) = w.s;
     };
     u32x4 ar[NTB * 2];
     u32x2 ars;
@@ -339,8 +326,8 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
 
     // lane (row r = l % 32, half h = l / 32) of 64-K step (q, t) takes code bytes
     // [64 q + 32 h + 16 t, +16) of its row and their two scale bytes 8 q + 4 h + 2 t, +1: from
-    // the wave's staging slot, or (kDirect) straight from the chunk's registers (code set
-    // 2 q + t; scale dword q (NVFP4), or halfword q (MXFP4))
+    // the wave's staging slot, or (tiled weights) straight from the chunk's registers (code
+    // set 2 q + t; scale dword q (NVFP4), or halfword q (MXFP4))
     auto compute = [&](int buf, const WChunk &wc) {
         const unsigned char *ab = act + buf * kActBuf;
         const unsigned char *wr = wl + w4::lds_wread(lane);
@@ -357,12 +344,12 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                 for (int v = 0; v < 16; ++v) part[tb][v] = 0.f;
             // block scales of this lane's K runs: NVFP4 e4m3 bytes 8q + 4h + 2t, +1 (one per 16 K),
             // MXFP4 e8m0 byte 4q + 2h + t (one per 32 K)
-            const uint32_t sq = kDirect ? (kMX ? wc.s.x >> (16 * q) : (q ? wc.s.y : wc.s.x))
+            const uint32_t sq = kTiled ? (kMX ? wc.s.x >> (16 * q) : (q ? wc.s.y : wc.s.x))
                                 : kMX ? *(const uint32_t *)(wsr - 4 * half + 4 * q) >> (16 * half)
                                       : *(const uint32_t *)(wsr + 8 * q);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {  // two 64-wide MFMA steps per 128-wide block
-                const u32x4 cw = kDirect ? wc.c[2 * q + t] : *(const u32x4 *)(wr + 64 * q + 16 * t);
+                const u32x4 cw = kTiled ? wc.c[2 * q + t] : *(const u32x4 *)(wr + 64 * q + 16 * t);
                 i32x8 wa;
                 int wscale = 127;  // e8m0 1.0: the NVFP4 weights are dequantised to fp8 here
                 if constexpr (kMX) {  // the e2m1 codes are the MFMA's fp4 operand as they are
@@ -483,9 +470,10 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // It ends like a loop step (activations of the next chunk, then one weight set), so the
     // loads in flight at the loop head follow the same pattern on entry as on the back edge
     // and the compiler's waits there stay exact.
-    // weight register sets: kNBuf, or one fewer for three token blocks (their accumulators take
-    // the registers)
-    constexpr int NBUF = NTB == 3 ? kNBuf - 1 : kNBuf;
+    // weight register sets: kNBuf; for three token blocks (their accumulators take the
+    // registers) one fewer, and with tiled weights, whose registers also hold the chunk being
+    // computed, two (three measured 2-5 % slower at T = 256, NVFP4 spilling)
+    constexpr int NBUF = NTB == 3 ? (kTiled ? 2 : kNBuf - 1) : kNBuf;
     static_assert(!kLoop || NBUF == kNBuf, "the persistent form rotates kNBuf sets across tiles");
     WChunk w[NBUF];
     load_w(w[0], A, 0);
@@ -497,7 +485,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     store_a(0);
     load_a(A, min(1, nc - 1));
     load_w(w[NBUF - 2], A, min(NBUF - 2, nc - 1));
-    if constexpr (!kDirect) store_w(w[0]);
+    if constexpr (!kTiled) store_w(w[0]);
     lds_barrier();  // chunk 0 staged, scale table built
 
     for (;;) {
@@ -542,7 +530,7 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
                     }
                 }
                 if (c < nc) compute(c & 1, w[sidx]);
-                if constexpr (!kDirect) {
+                if constexpr (!kTiled) {
                     // the staging slot is rewritten below: keep these writes after the reads above
                     // (the lanes of the wave read each other's bytes; its LDS accesses run in order)
                     asm volatile("" ::: "memory");

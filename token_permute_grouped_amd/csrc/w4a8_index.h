@@ -151,14 +151,6 @@ TPG_HD int lds_wscale(int lane, bool mx) { return kWScales + (lane >> 1) * 16 + 
 // dword at - 4 h + 4 q for MXFP4)
 TPG_HD int lds_wread(int lane) { return (lane & 31) * kWRow + (lane >> 5) * 32; }
 TPG_HD int lds_wsread(int lane) { return kWScales + (lane & 31) * 16 + (lane >> 5) * 4; }
-// a wave's staging slot for tiled weights (whose lane l holds the operand bytes of step i, see
-// tiled_code_pos): the same slot layout as above, so the operand reads are unchanged; code
-// register i of lane l goes to row l % 32, granule 4 (i / 2) + 2 (l / 32) + i % 2, and NVFP4
-// scale dword q to the row's bytes 8 q + 4 (l / 32)
-TPG_HD int lds_wcode_tiled(int lane, int i) {
-    return (lane & 31) * kWRow + (4 * (i >> 1) + 2 * (lane >> 5) + (i & 1)) * 16;
-}
-TPG_HD int lds_wscale_tiled(int lane, int q) { return kWScales + (lane & 31) * 16 + 8 * q + 4 * (lane >> 5); }
 // activation scale of tile row r, block q of the chunk (float index into [2][kMaxRows][2])
 TPG_HD int lds_xs(int buf, int r, int q) { return buf * (kMaxRows * 2) + r * 2 + q; }
 // SwiGLU hand-over: accumulator v of token block tb of up wave 2 + wu, lane l (float index)
