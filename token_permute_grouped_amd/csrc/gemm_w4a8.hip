@@ -27,8 +27,7 @@
 // few rows) and 128 weight rows; wave w owns 32 weight rows (one MFMA block) and every
 // token of the tile.  Weights are never shared between waves: each wave loads its rows
 // into a ring of register sets, one 256-wide K chunk per set, as many chunks ahead as the
-// ring allows (four sets; for three token blocks, whose accumulators take registers, three,
-// or two with tiled weights).  Row-major weights come in line-coalesced loads (8 lanes per
+// ring allows (four sets; fewer where measured faster, see NBUF).  Row-major weights come in line-coalesced loads (8 lanes per
 // 128-byte line) and each chunk is transposed, one step before its compute, through the
 // wave's own LDS slot into the MFMA operand layout (lane l: row l % 32, one contiguous
 // 32-code run per 64-wide K step).  The tiled layout (moe_w4a8_tile_weights) already
@@ -471,9 +470,14 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     // loads in flight at the loop head follow the same pattern on entry as on the back edge
     // and the compiler's waits there stay exact.
     // weight register sets: kNBuf; for three token blocks (their accumulators take the
-    // registers) one fewer, and with tiled weights, whose registers also hold the chunk being
-    // computed, two (three measured 2-5 % slower at T = 256, NVFP4 spilling)
-    constexpr int NBUF = NTB == 3 ? (kTiled ? 2 : kNBuf - 1) : kNBuf;
+    // registers) one fewer.  With tiled weights, whose registers also hold the chunk being
+    // computed, the measured best (W4A8 layer, each against the neighbouring counts): two for
+    // three token blocks (three: 2-5 % slower at T = 256, NVFP4 spilling), two for one token
+    // block outside the persistent form (the K-split GEMM1 at T = 1, one-block tiles above 32
+    // tokens: MXFP4 T = 1 -4 %, T = 64 -3 %; the persistent form keeps four: two made MXFP4
+    // T = 4 5 % and NVFP4 T = 16 2 % slower), four for two token blocks (three: 2 % slower at
+    // T = 128)
+    constexpr int NBUF = NTB == 3 ? (kTiled ? 2 : kNBuf - 1) : (NTB == 1 && kTiled && !kLoop) ? 2 : kNBuf;
     static_assert(!kLoop || NBUF == kNBuf, "the persistent form rotates kNBuf sets across tiles");
     WChunk w[NBUF];
     load_w(w[0], A, 0);
