@@ -129,7 +129,10 @@ def test_forward_and_grouped_ffn_on_tiled_weights_equal_row_major(name):
     assert (y_rows[:R] == y_tiled[:R]).all()
 
 
-@pytest.mark.parametrize("wl,T", [("w4a8", 1), ("w4a8", 256), ("w4a8_mx", 16), ("w4a8_mx", 256)])
+# every GEMM form on the full layer in both formats: the K-split GEMM1 (T = 1), the persistent
+# GEMMs (T = 16), one- and two-block tiles above 32 tokens (T = 64, 128), three-block tiles (T = 256)
+@pytest.mark.parametrize("wl,T", [("w4a8", 1), ("w4a8", 16), ("w4a8", 64), ("w4a8", 256), ("w4a8_mx", 1),
+                                  ("w4a8_mx", 16), ("w4a8_mx", 128), ("w4a8_mx", 256)])
 def test_full_layer_forward_on_tiled_weights_equals_row_major(wl, T):
     print(f"[gpu w4 layout] {wl} layer T={T}", flush=True)
     inp = generate(CONFIGS[wl], seed=0, T=T)
