@@ -138,6 +138,41 @@ def test_permute_tables_and_rows_bit_exact(name):
 
 # ----------------------------------------------------------------------------- combine
 
+# expert ids chosen directly (no routing) around the one-workgroup tables kernel's bound of 2048
+# slots: exactly 2048 and 2049 slots, every slot dropped, one hot expert, one expert, one slot
+TABLE_CASES = [
+    ("s2048_drops", 2048, 1, 64, "random"), ("s2049", 2049, 1, 64, "random"), ("s2048_k8", 256, 8, 256, "random"),
+    ("s1024_all_dropped", 512, 2, 16, "dropped"), ("s2048_one_hot", 1024, 2, 256, "hot"),
+    ("s1500_one_expert", 1500, 1, 1, "random"), ("s1", 1, 1, 4, "random"), ("s4100", 2050, 2, 33, "random"),
+]
+
+
+@pytest.mark.parametrize("case", TABLE_CASES, ids=[c[0] for c in TABLE_CASES])
+def test_tables_bit_exact_at_the_one_workgroup_bound(case):
+    name, T, k, E, mode = case
+    print(f"[gpu parity] tables {name}: T={T} k={k} E={E} {mode}", flush=True)
+    rng = np.random.default_rng(T * 31 + k * 7 + E)
+    if mode == "dropped":
+        idx = np.full((T, k), -1, np.int32)
+    elif mode == "hot":
+        idx = np.where(rng.random((T, k)) < 0.9, 5, rng.integers(0, E, (T, k))).astype(np.int32)
+    else:
+        idx = rng.integers(0, E, (T, k)).astype(np.int32)
+        idx[rng.random((T, k)) < 0.1] = -1  # dropped slots
+    cfg = MoeConfig(name, T=T, H=128, I=128, E=E, k=k)
+    inp = {"cfg": cfg, "logits": np.zeros((T, E), np.float32), "x": rng.integers(0, 1 << 16, (T, 128), dtype=np.uint16),
+           "w1": np.zeros((E, 256, 128), np.uint16), "w2": np.zeros((E, 128, 128), np.uint16)}
+    d = DeviceProblem(inp)
+    offsets, row_src, slot_row, x_perm, _ = d.permute(to_dev(idx))
+    torch.cuda.synchronize()
+    _, ref_off, ref_rs, ref_sr = oracle.tables(idx, E)
+    assert (offsets.cpu().numpy() == ref_off).all()
+    assert (row_src.cpu().numpy() == ref_rs).all()
+    assert (slot_row.cpu().numpy() == ref_sr).all()
+    R = int(ref_off[-1])
+    assert (x_perm.cpu().numpy().view(np.uint16)[:R] == inp["x"][ref_rs[:R] // k]).all()
+
+
 @pytest.mark.parametrize("name", ["tiny", "interleaved_drop", "max_experts", "mid"])
 def test_combine_matches_oracle(name):
     inp, d = workload(name)
