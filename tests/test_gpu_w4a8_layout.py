@@ -97,6 +97,14 @@ CASES = {
     # two token blocks per tile in the single-launch forward
     "nv_fused_t100": MoeConfig("nv_fused_t100", T=100, H=1024, I=1024, E=16, k=4, prec="w4a8", swiglu_clamp=10.0,
                                drop_p=0.1),
+    # above 128 tokens: two- and three-block tiles, with H = 4096 and 20-24 one-tile experts more
+    # tiles (640-768) than two workgroups per CU
+    "nv_t200_three_block": MoeConfig("nv_t200_three_block", T=200, H=512, I=1024, E=5, k=2, prec="w4a8",
+                                          swiglu_clamp=10.0, drop_p=0.05),
+    "mx_t256_h4096": MoeConfig("mx_t256_h4096", T=256, H=4096, I=1024, E=24, k=4, prec="w4a8_mx",
+                                    glu_interleave=32),
+    "nv_t200_h4096": MoeConfig("nv_t200_h4096", T=200, H=4096, I=1024, E=20, k=4, prec="w4a8",
+                                    swiglu_clamp=10.0, drop_p=0.1),
 }
 
 
