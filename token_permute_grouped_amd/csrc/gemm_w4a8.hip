@@ -216,9 +216,10 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
     const bool gather = g.row_src != nullptr;
 
     // ---- addressing of one tile.  Weights: each wave streams its own 32 rows, in chunks of
-    // 256 K (128 code bytes + 16 scale bytes per row); loads cover whole 128-byte lines (8 lanes
-    // per row), and the wave transposes each chunk through its own LDS slot into the MFMA
-    // operand layout.  Activations: thread t stages granule t % 16 of token rows t / 16 + 16 i,
+    // 256 K (128 code bytes + 16 scale bytes per row); row-major weights in loads that cover
+    // whole 128-byte lines (8 lanes per row), which the wave transposes through its own LDS slot
+    // into the MFMA operand layout, tiled weights in contiguous loads already in that layout (see
+    // w4::tiled_code_pos).  Activations: thread t stages granule t % 16 of token rows t / 16 + 16 i,
     // and thread r < 32 NTB the chunk's two activation scales of token row r.  Raw buffer
     // resources bound every read (rows past the tile's live rows read as zero), so every lane
     // issues the same unconditional loads and the compiler's wait counts stay exact.  With
@@ -511,20 +512,21 @@ __device__ __forceinline__ void w4a8_tiles(const W4Args &g, Sched &sc, unsigned 
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[tb][q] = 0.f;
 
-        // Chunk c computes from activation buffer c % 2 and this wave's weight slot c % 2, then
-        // stages the weights of chunk c + 1 (set (c + 1) % 4, loaded two steps ago) into the other
-        // slot (this wave last read it in chunk c - 1; a wave's LDS accesses stay in order) and
-        // the activations of chunk c + 1 into the other buffer (last read in chunk c - 1, before
-        // the previous barrier), loads the activations of chunk c + 2 and the weights of chunk
-        // c + NBUF - 1 (into the set of chunk c - 1).  Whole groups of four steps: a step past
-        // the last chunk (single-tile form with K / kKC not a multiple of four) skips only its
+        // Chunk c computes from activation buffer c % 2 and from its weights: this wave's LDS slot
+        // (row-major), or register set c % NBUF (tiled).  Then (row-major only) it stages the
+        // weights of chunk c + 1 into the slot (this wave read it just now; a wave's LDS accesses
+        // stay in order), stages the activations of chunk c + 1 into the other buffer (last read
+        // in chunk c - 1, before the previous barrier), loads the activations of chunk c + 2 and
+        // the weights of chunk c + NBUF - 1 (into the set of chunk c - 1).  Whole groups of NBUF
+        // steps: a step past the last chunk (single-tile form with K / kKC not a multiple of
+        // NBUF) skips only its
         // compute (which issues no memory loads), so every path through the loop issues the same
         // loads and the compiler's waits at the loop head see the regular pattern.
         for (int c0 = 0; c0 < nc; c0 += NBUF) {
 #pragma unroll
             for (int sidx = 0; sidx < NBUF; ++sidx) {
                 const int c = c0 + sidx;
-                if (kLoop && sidx == 2 && c0 == 0 && go_on) finish_addr(B, nxt);
+                if (kLoop && c == 2 && go_on) finish_addr(B, nxt);  // before request nc - 2 (nc >= 4)
                 if (kSplit == 2 && c == nc / 2) {
 #pragma unroll
                     for (int tb = 0; tb < NTB; ++tb) {
