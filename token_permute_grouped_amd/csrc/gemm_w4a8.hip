@@ -1021,28 +1021,39 @@ __global__ __launch_bounds__(kThreads, 2) void forward_small_w4a8_kernel(FusedAr
 
 #undef TPG_W4A8_LDS
 
-// h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows: one wave per
-// (row, 128 columns); s = amax / 448 (1 if that is 0), q = e4m3(h / s), decided in fp32.  h is
-// read once, non-temporal (W4A8 layer, expert FFN stage: T = 256 212 -> 205 us MXFP4, T = 64
-// 142 -> 139 us, T = 128 NVFP4 187 -> 184 us).
+// h fp32 [S][I] -> h8 e4m3 [S][I] + hs fp32 [S][I/128] for the live rows.  Item i = (row, 128
+// columns) starts at float 128 i of h (a row holds I / 128 items).  A half-wave takes one item,
+// four columns per lane, and a wave kReqPairs pairs of adjacent items, every load issued before
+// any arithmetic; s = amax / 448 (1 if that is 0), q = e4m3(h / s), decided in fp32.  h is read
+// once, non-temporal.
+constexpr int kReqPairs = 2;
 __global__ __launch_bounds__(256) void requant_fp8_kernel(const float *__restrict__ h, const int32_t *__restrict__ offsets,
                                                           int E, int I, uint8_t *__restrict__ h8,
                                                           float *__restrict__ hs) {
-    const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int nb = I / 128;
-    const int64_t row = item / nb;
-    const int b = (int)(item % nb);
-    if (row >= offsets[E]) return;
-    const f32x2 v = __builtin_nontemporal_load((const f32x2 *)(h + row * I + b * 128 + 2 * lane));
-    float m = fmaxf(fabsf(v.x), fabsf(v.y));
+    const int lane = threadIdx.x & 63, c = 4 * (lane & 31);
+    const int64_t live = (int64_t)offsets[E] * (I / 128);  // items of the live rows
+    const int64_t first = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (2 * kReqPairs) + (lane >> 5);
+    f32x4 v[kReqPairs];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float s = m / 448.0f;
-    if (s == 0.0f) s = 1.0f;
-    const uint32_t q = to_fp8x2<false>(v.x / s, v.y / s, 0u);
-    *(uint16_t *)(h8 + row * I + b * 128 + 2 * lane) = (uint16_t)(q & 0xffffu);
-    if (lane == 0) hs[row * nb + b] = s;
+    for (int u = 0; u < kReqPairs; ++u) {
+        const int64_t it = first + 2 * u;
+        v[u] = it < live ? __builtin_nontemporal_load((const f32x4 *)(h + it * 128 + c)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kReqPairs; ++u) {
+        const int64_t it = first + 2 * u;
+        // the reduction stays within each half-wave (both halves run it, live or not)
+        float m = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+        float s = m / 448.0f;
+        if (s == 0.0f) s = 1.0f;
+        const uint32_t q = to_fp8x2<true>(v[u].z / s, v[u].w / s, to_fp8x2<false>(v[u].x / s, v[u].y / s, 0u));
+        if (it < live) {
+            *(uint32_t *)(h8 + it * 128 + c) = q;
+            if ((lane & 31) == 0) hs[it] = s;
+        }
+    }
 }
 
 // GEMM1 split in two K halves: h = silu(g) * u from the halves' partial sums
@@ -1218,7 +1229,8 @@ hipError_t launch_grouped_ffn_w4a8(const uint8_t *x_perm, const float *x_perm_sc
         hipLaunchKernelGGL(requant_swiglu_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, (int64_t)S * I,
                            offsets, p.E, I, w.w1_gscale, p.swiglu_clamp, h8, hs);
     else
-        hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 3) / 4), dim3(256), 0, s, h32, offsets, p.E, I, h8, hs);
+        hipLaunchKernelGGL(requant_fp8_kernel, dim3((items + 8 * kReqPairs - 1) / (8 * kReqPairs)), dim3(256), 0, s,
+                           h32, offsets, p.E, I, h8, hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     W4Args g2{};
