@@ -504,7 +504,9 @@ static void replay_front_end(const Problem &p, const Routing &r, int threads) {
     check_range("tile list", (long long)r.n_mt[1] * 2 - 1, 1, 2 * max_m_tiles(p));
 }
 
-int main() {
+// argv[1], if given: a file of further problems, one "T H I E k" line each (both weight formats,
+// both layouts)
+int main(int argc, char **argv) {
     g_case = "LDS";
     replay_lds();
     g_case = "tiled layout";
@@ -527,6 +529,18 @@ int main() {
         const int T = 1 + rng.below(2048 / k < 256 ? 2048 / k : 256) / (n < 4 ? 4 : 1);
         probs.push_back({T, 1024 * (1 + rng.below(4)), 1024 * (1 + rng.below(3)), E, k, rng.below(2) == 1,
                          rng.below(2) == 1});
+    }
+    if (argc > 1) {
+        FILE *f = std::fopen(argv[1], "r");
+        if (!f) {
+            std::printf("cannot open %s\n", argv[1]);
+            return 2;
+        }
+        int T, H, I, E, k;
+        while (std::fscanf(f, "%d %d %d %d %d", &T, &H, &I, &E, &k) == 5)
+            for (bool mx : {false, true})
+                for (bool tiled : {false, true}) probs.push_back({T, H, I, E, k, mx, tiled});
+        std::fclose(f);
     }
     for (const Problem &p : probs)
         for (int mode = 0; mode < 4; ++mode) {
